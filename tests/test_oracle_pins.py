@@ -1,0 +1,366 @@
+"""Pins of the FP64 oracle against facts that do not come from the oracle itself:
+closed forms, invariants, brute force on tiny inputs, special cases that reduce
+to a textbook formula or a library routine.  CPU only."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+from scipy import special
+
+import oracle as O
+
+rng = np.random.default_rng(1234)
+
+
+# ---------------------------------------------------------------- decoding
+def test_bf16_decoding_closed_forms():
+    # 0x3F80 = 1.0, 0xC000 = -2.0, 0x3E80 = 0.25, 0x7F7F = largest finite bf16
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x0000, 0x8000, 0x7F7F], np.uint16)
+    v = O.bf16_to_f64(bits)
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 0.25 and v[3] == 0.0
+    assert v[4] == 0.0 and math.copysign(1, v[4]) == -1.0
+    assert v[5] == (2 - 2 ** -7) * 2.0 ** 127
+
+
+def test_int4_unpack_bit_by_bit():
+    packed = rng.integers(0, 256, size=(3, 5), dtype=np.uint8)
+    q = O.int4_unpack(packed)
+    for r in range(3):
+        for i in range(5):
+            byte = int(packed[r, i])
+            for half, shift in ((0, 0), (1, 4)):
+                nib = (byte >> shift) & 0xF
+                val = nib - 16 if nib & 0x8 else nib   # two's complement nibble
+                assert q[r, 2 * i + half] == val
+
+
+def test_int4_one_hot_selects_exactly_one_weight():
+    """A single non-zero nibble at a known (n, k) selects exactly q * s of its group:
+    pins nibble order (low nibble = even k) and the group index k // 128."""
+    N, K = 4, 384
+    for n, kk, qv in ((0, 0, 3), (1, 1, -8), (2, 129, 7), (3, 383, -1)):
+        q = np.zeros((N, K), np.int64)
+        q[n, kk] = qv
+        packed = np.zeros((N, K // 2), np.uint8)
+        for r in range(N):
+            for i in range(K // 2):
+                packed[r, i] = (q[r, 2 * i] & 0xF) | ((q[r, 2 * i + 1] & 0xF) << 4)
+        # power-of-two scales that differ per (row, group): 2^-(r + 3g)
+        s = np.array([[2.0 ** -(r + 3 * g) for g in range(K // 128)] for r in range(N)], np.float32)
+        sbits = (s.view(np.uint32) >> 16).astype(np.uint16)
+        w = O.int4_dequant(packed, sbits)
+        expect = np.zeros((N, K))
+        expect[n, kk] = qv * 2.0 ** -(n + 3 * (kk // 128))
+        assert np.array_equal(w, expect)
+
+
+# ---------------------------------------------------------------- scores
+def test_softmax_rows_sum_to_one_and_match_library():
+    L = rng.normal(size=(50, 64)) * 4
+    P = O.softmax_scores(L)
+    assert np.abs(P.sum(1) - 1).max() <= 1e-12
+    assert np.allclose(P, special.softmax(L, axis=1), rtol=1e-13, atol=0)
+    # closed form: logits (0, ln 3) -> (1/4, 3/4); shift invariance
+    P2 = O.softmax_scores(np.array([[0.0, math.log(3.0)], [100.0, 100.0 + math.log(3.0)]]))
+    assert np.allclose(P2, [[0.25, 0.75], [0.25, 0.75]], rtol=1e-14, atol=0)
+    # large logits do not overflow (max-subtract form)
+    assert np.isfinite(O.softmax_scores(np.array([[1000.0, 999.0]]))).all()
+
+
+def test_sigmoid_matches_library():
+    L = rng.normal(size=(20, 16)) * 3
+    assert np.allclose(O.sigmoid_scores(L), special.expit(L), rtol=1e-14, atol=0)
+    assert O.sigmoid_scores(np.zeros((1, 1)))[0, 0] == 0.5
+
+
+def test_router_logits_bias_and_orientation():
+    # non-square: x [3,5], w_router stored [E=4][d=5]; logits[t,e] = sum_i x[t,i] w[e,i] + b[e]
+    x = rng.normal(size=(3, 5))
+    w = rng.normal(size=(4, 5))
+    b = rng.normal(size=4)
+    L = O.router_logits(x, w, b)
+    for t in range(3):
+        for e in range(4):
+            assert math.isclose(L[t, e], sum(x[t, i] * w[e, i] for i in range(5)) + b[e], rel_tol=1e-12,
+                                abs_tol=1e-12)
+
+
+# ---------------------------------------------------------------- top-k
+def _brute_topk(row, k):
+    order = sorted(range(len(row)), key=lambda e: (-(row[e] + 0.0), e))
+    return order[:k]
+
+
+@pytest.mark.parametrize("E,k", [(4, 1), (8, 2), (16, 4), (16, 16), (5, 3)])
+def test_topk_matches_brute_force_full_sort_with_ties(E, k):
+    # integer-valued keys with few distinct values force many exact ties
+    key = rng.integers(0, 4, size=(64, E)).astype(np.float64)
+    key[0] = 0.0
+    key[1, :] = -0.0  # -0 ties with +0
+    key[1, ::2] = 0.0
+    idx, margin = O.select_topk(key, k)
+    for t in range(key.shape[0]):
+        assert idx[t].tolist() == _brute_topk(key[t].tolist(), k)
+        assert len(set(idx[t].tolist())) == k
+        if k < E:
+            srt = sorted(key[t], reverse=True)
+            assert margin[t] == srt[k - 1] - srt[k]
+        else:
+            assert margin[t] == np.inf
+
+
+def test_zero_router_gives_lowest_indices():
+    """W_r = 0 and no bias: every key ties, so every token selects experts 0..k-1."""
+    x = rng.normal(size=(10, 6))
+    for score in ("softmax", "sigmoid"):
+        res = O.moe_layer(x, np.zeros((8, 6)), _experts_fn(_rand_experts(8, 6, 3)), 8, 3, score=score,
+                          ffn_rows=np.arange(0))
+        assert (res["idx"] == np.arange(3)[None, :]).all()
+
+
+# ---------------------------------------------------------------- gates
+def test_gate_sums_and_order():
+    L = rng.normal(size=(40, 16)) * 2
+    P = O.softmax_scores(L)
+    idx, _ = O.select_topk(P, 4)
+    g = O.gate_weights(P, idx, renorm=False, scale=1.0)
+    assert (g.sum(1) <= 1 + 1e-15).all()
+    assert (np.diff(g, axis=1) <= 0).all()          # non-increasing in slot order
+    gr = O.gate_weights(P, idx, renorm=True, scale=1.0)
+    assert np.abs(gr.sum(1) - 1).max() <= 1e-15
+    S = O.sigmoid_scores(L)
+    gs = O.gate_weights(S, idx, renorm=True, scale=2.5)
+    assert np.abs(gs.sum(1) - 2.5).max() <= 1e-14
+
+
+def test_selection_bias_selects_but_does_not_weight():
+    """Sigmoid scoring with a selection-only bias: the bias decides which experts win,
+    the gate uses the unbiased score.  Hand-worked: logits (2, 0, 0.5), bias (0, 3, 0), k=2
+    -> keys (s(2), s(0)+3, s(0.5)) picks experts 1 then 0; gates 2.5*s_e / (s(0)+s(2))."""
+    x = np.array([[1.0]])
+    w = np.array([[2.0], [0.0], [0.5]])
+    res = O.moe_layer(x, w, _experts_fn(_rand_experts(3, 1, 1)), 3, 2, score="sigmoid", renorm=True,
+                      gate_scale=2.5, select_bias=np.array([0.0, 3.0, 0.0]), ffn_rows=np.arange(0))
+    assert res["idx"][0].tolist() == [1, 0]
+    s0, s2 = 0.5, 1 / (1 + math.exp(-2.0))
+    assert np.allclose(res["gates"][0], [2.5 * s0 / (s0 + s2), 2.5 * s2 / (s0 + s2)], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- permutation
+def test_capacity_rows_exact_integer_ceil():
+    assert O.capacity_rows(8192, 6, 64, 5, 4) == 960        # DeepSeek-V2-Lite at C = 1.25
+    assert O.capacity_rows(8, 2, 4, 5, 4) == 5               # exactly 5.0, must not round up
+    assert O.capacity_rows(10, 1, 4, 1, 1) == 3              # ceil(2.5)
+    assert O.capacity_rows(3, 1, 4, 1, 1) == 1               # ceil(0.75)
+    assert O.capacity_rows(5, 2, 3, 0, 1) == 0
+
+
+def _brute_assign(idx, E, cap):
+    # group pairs by expert with a dict, keep the first `cap` in (t, j) order
+    groups = {}
+    for t, j in itertools.product(range(idx.shape[0]), range(idx.shape[1])):
+        groups.setdefault(int(idx[t, j]), []).append((t, j))
+    kept = {e: (v if cap is None else v[:cap]) for e, v in groups.items()}
+    return groups, kept
+
+
+@pytest.mark.parametrize("T,E,k,cap", [(1, 4, 2, None), (13, 5, 2, None), (40, 8, 3, None),
+                                       (40, 8, 3, 7), (40, 8, 3, 1), (40, 8, 3, 40), (17, 3, 3, 0)])
+def test_assignment_matches_brute_force(T, E, k, cap):
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    a = O.assign_rows(idx, E, cap)
+    groups, kept = _brute_assign(idx, E, cap)
+    assert a["counts"].sum() == T * k
+    for e in range(E):
+        assert a["counts"][e] == len(groups.get(e, []))
+        assert a["kept"][e] == len(kept.get(e, []))
+        rows = list(range(a["offsets"][e], a["offsets"][e + 1]))
+        # rows of expert e map back, in order, to the kept pairs of e
+        assert [int(a["row_token"][r]) for r in rows] == [t for t, _ in kept.get(e, [])]
+        for r, (t, j) in zip(rows, kept.get(e, [])):
+            assert a["slot_row"][t, j] == r
+    # round trip and drop accounting
+    for t in range(T):
+        for j in range(k):
+            if a["drop"][t, j]:
+                assert a["slot_row"][t, j] == -1
+            else:
+                assert a["row_token"][a["slot_row"][t, j]] == t
+    n_drop = int(a["drop"].sum())
+    expect = 0 if cap is None else sum(max(0, len(v) - cap) for v in groups.values())
+    assert n_drop == expect
+    assert int(a["offsets"][E]) == T * k - n_drop
+    if cap is not None and cap >= T:
+        assert n_drop == 0            # an expert receives each token at most once
+    if cap == 1:
+        for e, v in groups.items():   # exactly the first pair in (t, j) order survives
+            t, j = v[0]
+            assert a["drop"][t, j] == 0 and a["offsets"][e + 1] - a["offsets"][e] == 1
+
+
+# ---------------------------------------------------------------- experts / whole layer
+def _rand_experts(E, d, F, scale=0.5):
+    return [(rng.normal(size=(F, d)) * scale, rng.normal(size=(F, d)) * scale, rng.normal(size=(d, F)) * scale)
+            for _ in range(E)]
+
+
+def _experts_fn(lst):
+    return lambda e: lst[e]
+
+
+def _textbook_swiglu(x, Wg_dF, Wu_dF, Wd_Fd):
+    # logical [d, ffn] / [ffn, d] matrices, silu via the library logistic function
+    a = x @ Wg_dF
+    return (a * special.expit(a) * (x @ Wu_dF)) @ Wd_Fd
+
+
+def test_swiglu_scalar_closed_form():
+    # d = ffn = 1: x = 1, Wg = 1, Wu = 2, Wd = 3 -> silu(1) * 2 * 3 = 6 / (1 + e^-1)
+    y = O.swiglu_ffn(np.array([[1.0]]), np.array([[1.0]]), np.array([[2.0]]), np.array([[3.0]]))
+    assert math.isclose(y[0, 0], 6.0 / (1.0 + math.exp(-1.0)), rel_tol=1e-15)
+    # silu is odd-symmetric around its definition: silu(-z) = silu(z) - z
+    z = rng.normal(size=100) * 5
+    assert np.allclose(O.silu(-z), O.silu(z) - z, rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_reduces_to_dense_swiglu():
+    """E = 1, k = 1: the softmax of one logit is 1, so the layer is a dense SwiGLU FFN."""
+    T, d, F = 9, 5, 7
+    x = rng.normal(size=(T, d))
+    Wg, Wu, Wd = rng.normal(size=(d, F)), rng.normal(size=(d, F)), rng.normal(size=(F, d))
+    # stored layout: one K-contiguous row per output channel
+    ex = [(Wg.T.copy(), Wu.T.copy(), Wd.T.copy())]
+    res = O.moe_layer(x, rng.normal(size=(1, d)), _experts_fn(ex), 1, 1,
+                      logit_bias=np.array([0.3]))
+    assert np.allclose(res["gates"], 1.0, rtol=0, atol=1e-15)
+    assert np.allclose(res["out"], _textbook_swiglu(x, Wg, Wu, Wd), rtol=1e-12, atol=1e-12)
+
+
+def test_k_equals_E_is_soft_mixture():
+    """k = E, softmax, no renorm: out = sum_e p_e FFN_e(x) (every gate applied)."""
+    T, d, F, E = 6, 4, 3, 5
+    x = rng.normal(size=(T, d))
+    wr = rng.normal(size=(E, d))
+    ex = _rand_experts(E, d, F)
+    res = O.moe_layer(x, wr, _experts_fn(ex), E, E)
+    L = x @ wr.T
+    P = np.exp(L) / np.exp(L).sum(1, keepdims=True)
+    expect = np.zeros((T, d))
+    for e in range(E):
+        Wg, Wu, Wd = ex[e]
+        expect += P[:, e:e + 1] * _textbook_swiglu(x, Wg.T, Wu.T, Wd.T)
+    assert np.allclose(res["out"], expect, rtol=1e-12, atol=1e-12)
+
+
+def test_everything_dropped_leaves_shared_experts_only():
+    T, d, F, E = 7, 4, 3, 4
+    x = rng.normal(size=(T, d))
+    ex, sh = _rand_experts(E, d, F), _rand_experts(2, d, 6)
+    res = O.moe_layer(x, rng.normal(size=(E, d)), _experts_fn(ex), E, 2, capacity=(0, 1),
+                      shared=_experts_fn(sh), n_shared=2)
+    assert res["drop"].all()
+    expect = sum(_textbook_swiglu(x, a.T, b.T, c.T) for a, b, c in sh)
+    assert np.allclose(res["out"], expect, rtol=1e-12, atol=1e-12)
+    res0 = O.moe_layer(x, rng.normal(size=(E, d)), _experts_fn(ex), E, 2, capacity=(0, 1))
+    assert (res0["out"] == 0).all()
+
+
+def test_capacity_drop_skips_ffn_and_keeps_other_gates():
+    """A dropped pair contributes nothing; kept gates are not renormalised."""
+    T, d, F, E, k = 30, 4, 3, 3, 2
+    x = rng.normal(size=(T, d))
+    wr = rng.normal(size=(E, d))
+    ex = _rand_experts(E, d, F)
+    res = O.moe_layer(x, wr, _experts_fn(ex), E, k, capacity=(1, 2))
+    assert res["drop"].any()
+    for t in range(T):
+        y = np.zeros(d)
+        for j in range(k):
+            if not res["drop"][t, j]:
+                Wg, Wu, Wd = ex[res["idx"][t, j]]
+                y += res["gates"][t, j] * _textbook_swiglu(x[t:t + 1], Wg.T, Wu.T, Wd.T)[0]
+        assert np.allclose(res["out"][t], y, rtol=1e-12, atol=1e-12)
+
+
+def test_linearity_in_gates_and_route_replay_control():
+    T, d, F, E, k = 12, 6, 5, 6, 2
+    x = rng.normal(size=(T, d))
+    wr = rng.normal(size=(E, d))
+    ex, sh = _rand_experts(E, d, F), _rand_experts(1, d, 4)
+    kw = dict(shared=_experts_fn(sh), n_shared=1)
+    base = O.moe_layer(x, wr, _experts_fn(ex), E, k, **kw)
+    # control: replaying the layer's own routes returns the baseline exactly
+    rep = O.moe_layer(x, wr, _experts_fn(ex), E, k, routes=(base["idx"], base["gates"]), **kw)
+    assert np.array_equal(rep["out"], base["out"])
+    shared_part = _textbook_swiglu(x, sh[0][0].T, sh[0][1].T, sh[0][2].T)
+    scaled = O.moe_layer(x, wr, _experts_fn(ex), E, k, routes=(base["idx"], 3.0 * base["gates"]), **kw)
+    assert np.allclose(scaled["out"] - shared_part, 3.0 * (base["out"] - shared_part), rtol=1e-11, atol=1e-11)
+
+
+def test_token_permutation_equivariance():
+    T, d, F, E, k = 15, 5, 4, 6, 3
+    x = rng.normal(size=(T, d))
+    wr = rng.normal(size=(E, d))
+    ex = _rand_experts(E, d, F)
+    perm = rng.permutation(T)
+    a = O.moe_layer(x, wr, _experts_fn(ex), E, k)
+    b = O.moe_layer(x[perm], wr, _experts_fn(ex), E, k)
+    assert np.allclose(b["out"], a["out"][perm], rtol=1e-13, atol=1e-13)
+    assert (b["idx"] == a["idx"][perm]).all()
+
+
+def test_ffn_row_subset_matches_full():
+    T, d, F, E, k = 20, 4, 3, 5, 2
+    x = rng.normal(size=(T, d))
+    wr = rng.normal(size=(E, d))
+    ex = _rand_experts(E, d, F)
+    full = O.moe_layer(x, wr, _experts_fn(ex), E, k)
+    rows = np.array([0, 3, 19])
+    sub = O.moe_layer(x, wr, _experts_fn(ex), E, k, ffn_rows=rows)
+    assert np.allclose(sub["out"][rows], full["out"][rows], rtol=1e-13, atol=1e-14)
+    assert np.isnan(sub["out"][1]).all()
+
+
+def test_experts_touched_formula_statistics():
+    """Unbiased router on random tokens: distinct experts touched by B tokens averages
+    E (1 - (1 - k/E)^B)  (within 4 standard errors over 200 draws).  Orthonormal router
+    rows and isotropic tokens make the logits i.i.d. per (token, expert), which is the
+    uniform independent routing the formula assumes."""
+    E, k, d = 64, 8, 64
+    for B in (1, 4, 16):
+        touched = []
+        for s in range(200):
+            r = np.random.default_rng(10_000 + s)
+            x = r.normal(size=(B, d))
+            wr = np.linalg.qr(r.normal(size=(d, E)))[0].T
+            L = O.router_logits(x, wr)
+            idx, _ = O.select_topk(O.softmax_scores(L), k)
+            touched.append(len(np.unique(idx)))
+        m, se = np.mean(touched), np.std(touched) / math.sqrt(len(touched))
+        expect = O.experts_touched_expected(E, k, B)
+        assert abs(m - expect) <= 4 * se + 1e-9, (B, m, expect, se)
+    assert O.experts_touched_expected(64, 8, 1) == 8
+    assert math.isclose(O.experts_touched_expected(64, 8, 32), 64 * (1 - (7 / 8) ** 32))
+
+
+def test_swaps_per_token():
+    a = np.array([[0, 1, 2, 3], [4, 5, 6, 7]])
+    b = np.array([[3, 2, 1, 0], [4, 5, 9, 8]])
+    assert O.swaps_per_token(a, b).tolist() == [0, 2]
+
+
+def test_logit_bias_steers_selection_and_gates():
+    """The skew bias is part of the logits: a large bias on one expert makes every token
+    select it, and its softmax gate is exp(l + b) / sum exp(l' + b')."""
+    T, d, E, k = 8, 4, 5, 2
+    x = rng.normal(size=(T, d)) * 0.1
+    wr = rng.normal(size=(E, d))
+    bias = np.zeros(E)
+    bias[3] = 20.0
+    res = O.moe_layer(x, wr, _experts_fn(_rand_experts(E, d, 2)), E, k, logit_bias=bias,
+                      ffn_rows=np.arange(0))
+    assert (res["idx"][:, 0] == 3).all()
+    L = x @ wr.T + bias
+    expect = np.exp(L[:, 3]) / np.exp(L).sum(1)
+    assert np.allclose(res["gates"][:, 0], expect, rtol=1e-13)
