@@ -1,0 +1,177 @@
+/*
+ * moe.h -- C ABI of libmoe: the forward pass of a top-k Mixture-of-Experts
+ * SwiGLU FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (after "MoE: dynamism the compiler cannot remove", the natural
+ * implementation: router logits -> top-k -> per-expert FFN -> accumulate, and
+ * its capacity and grouped-GEMM sections):
+ *
+ *   logits  = x W_r^T (+ logit_bias)                       [T, E]  fp32
+ *   scores  = softmax(logits)  or  sigmoid(logits)          fp32
+ *   key     = scores (+ select_bias, sigmoid scoring only)
+ *   idx     = top-k(key), ties -> lower expert index        [T, k]  int32
+ *   gates   = gate_scale * scores[idx] (/ sum_j scores[idx_j] if renorm)
+ *   assignment: (t, j) pairs walked t-major; the r-th pair of expert e is
+ *           dropped when a capacity cap = ceil(C T k / E) is set and r >= cap
+ *   y_row   = (silu(x_t W_gate_e^T) * (x_t W_up_e^T)) W_down_e^T   per kept pair
+ *   out_t   = sum_{kept j} gates[t, j] y_row(t, j) + sum_s FFN_shared_s(x_t)
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device data (x, weights, outputs, ws) are device
+ *    pointers, caller-owned and caller-allocated, row-major, and at least
+ *    16-byte aligned.  `cfg` and `w` (the structs) are host pointers, read
+ *    during the call only.  `stream` is a hipStream_t (NULL = default stream).
+ *  - The library never allocates, frees or synchronises, and never reads
+ *    device data on the host: each call validates its arguments on the host,
+ *    enqueues kernels on `stream` and returns.  Every launch shape depends
+ *    only on the cfg, so moe_forward can be captured in a HIP graph.
+ *  - Errors are returned before any launch (negative moe_status); nothing is
+ *    thrown.  A launch failure returns MOE_ERR_HIP.  moe_last_error() gives a
+ *    thread-local description of the last failure.
+ *  - Drops are data, not errors (drop_mask).
+ *  - Weight layout: every matrix is stored one K-contiguous row per output
+ *    channel: w_gate, w_up [E][ffn][d], w_down [E][d][ffn]; shared experts
+ *    [S][ffn_shared][d] and [S][d][ffn_shared].  INT4 experts: packed bytes
+ *    [E][N][K/2] (byte i holds element 2i in its low nibble and 2i+1 in its
+ *    high nibble, two's complement) plus bf16 scales [E][N][K/128]; the weight
+ *    is q * s for the 128-element group along K.
+ *  - Calls on one stream run in order; two calls that share a workspace must
+ *    not overlap.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad enum value       */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside the shapes the kernels take */
+  MOE_ERR_WORKSPACE = -3,    /* ws NULL or ws_bytes < moe_workspace_bytes     */
+  MOE_ERR_HIP = -4           /* a HIP launch failed                           */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2 } moe_dtype;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+/* Layer shape and routing rule.  Supported: 0 <= T <= 1048576, 1 <= E <= 256,
+ * 1 <= k <= min(E, 8), d, ffn, ffn_shared multiples of 128, 0 <= n_shared <= 8,
+ * act_dtype MOE_F32 or MOE_BF16 (x, w_router, y_rows, y_shared, out),
+ * expert_dtype equal to act_dtype, or MOE_INT4_G128 with act_dtype MOE_BF16. */
+typedef struct moe_cfg {
+  int32_t T;            /* tokens                                              */
+  int32_t d;            /* hidden size                                         */
+  int32_t E;            /* routed experts                                      */
+  int32_t k;            /* experts per token                                   */
+  int32_t ffn;          /* routed expert intermediate size                     */
+  int32_t n_shared;     /* always-on shared experts (weight 1, never dropped)  */
+  int32_t ffn_shared;   /* shared expert intermediate size (ignored if none)   */
+  int32_t act_dtype;    /* moe_dtype                                           */
+  int32_t expert_dtype; /* moe_dtype (shared experts use the same dtype)       */
+  int32_t score;        /* moe_score                                           */
+  int32_t renorm;       /* 1: gates divided by their sum over the k picks      */
+  float gate_scale;     /* multiplies routed gates (1.0; 2.5 for DeepSeek-V3)  */
+  int32_t cap_num;      /* capacity factor C = cap_num / cap_den;              */
+  int32_t cap_den;      /*   0 / 0 = dropless; cap_num = 0 drops every pair    */
+} moe_cfg;
+
+/* Expert weights (device pointers, layout above).  s_* are the INT4 scales
+ * (NULL unless expert_dtype == MOE_INT4_G128); sh_* / shs_* the shared experts
+ * (NULL when n_shared == 0). */
+typedef struct moe_experts {
+  const void *w_gate, *w_up, *w_down;
+  const void *s_gate, *s_up, *s_down;
+  const void *sh_gate, *sh_up, *sh_down;
+  const void *shs_gate, *shs_up, *shs_down;
+} moe_experts;
+
+/* Checks a cfg on the host (no device access).  MOE_OK, or the reason. */
+moe_status moe_validate(const moe_cfg* cfg);
+
+/* Rows R of the expert-major row buffers (row_token, y_rows): T*k dropless,
+ * min(T*k, E*cap) with a capacity.  Negative on an invalid cfg. */
+int64_t moe_rows(const moe_cfg* cfg);
+
+/* Capacity cap = ceil(C*T*k/E) in exact integer arithmetic ("MoE: dynamism
+ * the compiler cannot remove", capacity section), or -1 when dropless;
+ * -2 on an invalid cfg. */
+int64_t moe_capacity(const moe_cfg* cfg);
+
+/* Workspace bytes every entry point needs for this cfg (worst case, static).
+ * 0 on an invalid cfg.  The workspace needs no initialisation. */
+size_t moe_workspace_bytes(const moe_cfg* cfg);
+
+/* Router: logits, scores, top-k and gates ("MoE: dynamism ...", natural
+ * implementation; FP32 gate probabilities from a max-subtract-expsum softmax
+ * as in the launch-bound study's Sub-study 1; sigmoid scoring with a
+ * selection-only per-expert bias as in "MoE Research" section 2).
+ *   x [T][d] act dtype; w_router [E][d] act dtype; logit_bias [E] fp32 or NULL
+ *   (added to the logits); select_bias [E] fp32 or NULL (sigmoid only: added to
+ *   the selection key, never to a gate).
+ *   Out: topk_idx [T][k] int32 in descending key order (ties -> lower index),
+ *   topk_w [T][k] fp32 gates, scores [T][E] fp32 (unbiased) or NULL. */
+moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
+                     const float* logit_bias, const float* select_bias,
+                     int32_t* topk_idx, float* topk_w, float* scores,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Permutation: expert histogram, prefix sum, optional capacity with drops,
+ * fixed-shape assignment ("MoE: dynamism ...", capacity section and batch-1
+ * recipe: fixed-shape scatter into preallocated buffers).
+ *   topk_idx [T][k] int32 (a value outside [0, E) is treated as dropped).
+ *   Out: counts [E] (pairs routed to each expert, before capacity),
+ *   offsets [E+1] (exclusive prefix sum of kept pairs; offsets[E] = kept total),
+ *   row_token [R] (token of each expert-major row; rows >= offsets[E] are left
+ *   unwritten), slot_row [T][k] (row of each pair, -1 if dropped),
+ *   drop_mask [T][k] uint8 (1 = dropped).  Ranks are stable in (t, j) order. */
+moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx,
+                       int32_t* counts, int32_t* offsets, int32_t* row_token,
+                       int32_t* slot_row, uint8_t* drop_mask,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped expert SwiGLU FFN over ragged per-expert row ranges ("MoE:
+ * dynamism ...", grouped GEMM section: one launch over a fixed grid, groups
+ * found from a device-side descriptor).
+ *   x [T][d]; offsets [E+1] and row_token [R] as produced by moe_permute.
+ *   Out: y_rows [R][d] act dtype (row r = FFN_e(x[row_token[r]]) for the expert
+ *   e whose range holds r; rows >= offsets[E] unwritten), y_shared [T][d] =
+ *   sum over shared experts of FFN_s(x_t) (NULL iff n_shared == 0). */
+moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets,
+                          const int32_t* row_token, const moe_experts* w,
+                          void* y_rows, void* y_shared,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine, fixed order over j, fp32 accumulation, one rounding:
+ *   out[t] = sum_{j: slot_row[t,j] in [0, R)} topk_w[t,j] * y_rows[slot_row[t,j]]
+ *            + y_shared[t]  (y_shared NULL iff n_shared == 0).  out [T][d]. */
+moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* slot_row,
+                       const float* topk_w, const void* y_shared, void* out, void* stream);
+
+/* The whole layer in a handful of static-shape launches: route, permute,
+ * gate/up SwiGLU GEMM, down GEMM, combine.  Outputs out [T][d], topk_idx,
+ * topk_w, drop_mask [T][k].  Same results, bit for bit, as moe_route ->
+ * moe_permute -> moe_expert_ffn -> moe_combine on the same inputs. */
+moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router,
+                       const float* logit_bias, const float* select_bias,
+                       const moe_experts* w, void* out, int32_t* topk_idx,
+                       float* topk_w, uint8_t* drop_mask,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel launches moe_forward enqueues for this cfg (0 on an invalid cfg). */
+int32_t moe_forward_launches(const moe_cfg* cfg);
+
+const char* moe_status_str(moe_status s);
+const char* moe_last_error(void);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

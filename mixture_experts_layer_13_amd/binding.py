@@ -1,0 +1,164 @@
+"""ctypes binding of libmoe (include/moe.h): argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, passes their
+device pointers and the current HIP stream to the C ABI and raises MoeError on
+a non-OK status.  No step of the layer runs here; if the library is missing
+the import of this module fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16, MOE_INT4_G128 = 0, 1, 2
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+
+_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128}
+_SCORES = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libmoe status {status}: {message}")
+        self.status = status
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("ffn_shared", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32), ("score", ctypes.c_int32),
+                ("renorm", ctypes.c_int32), ("gate_scale", ctypes.c_float), ("cap_num", ctypes.c_int32),
+                ("cap_den", ctypes.c_int32)]
+
+
+class MoeExperts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                                               "sh_gate", "sh_up", "sh_down", "shs_gate", "shs_up", "shs_down")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "from the repository root (hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    C = ctypes.POINTER(MoeCfg)
+    sig = {
+        "moe_validate": (ctypes.c_int, [C]),
+        "moe_rows": (ctypes.c_int64, [C]),
+        "moe_capacity": (ctypes.c_int64, [C]),
+        "moe_workspace_bytes": (ctypes.c_size_t, [C]),
+        "moe_forward_launches": (ctypes.c_int32, [C]),
+        "moe_route": (ctypes.c_int, [C, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_permute": (ctypes.c_int, [C, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_expert_ffn": (ctypes.c_int, [C, P, P, P, ctypes.POINTER(MoeExperts), P, P, P, ctypes.c_size_t, P]),
+        "moe_combine": (ctypes.c_int, [C, P, P, P, P, P, P]),
+        "moe_forward": (ctypes.c_int, [C, P, P, P, P, ctypes.POINTER(MoeExperts), P, P, P, P, P,
+                                       ctypes.c_size_t, P]),
+        "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_abi_version": (ctypes.c_int32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------- config helpers
+def make_cfg(T: int, d: int, E: int, k: int, ffn: int, n_shared: int = 0, ffn_shared: int = 0,
+             act: str = "bf16", expert: str = "bf16", score: str = "softmax", renorm: bool = False,
+             gate_scale: float = 1.0, capacity: Optional[tuple] = None) -> MoeCfg:
+    cn, cd = capacity if capacity is not None else (0, 0)
+    return MoeCfg(T, d, E, k, ffn, n_shared, ffn_shared, _DTYPES[act], _DTYPES[expert], _SCORES[score],
+                  int(bool(renorm)), float(gate_scale), cn, cd)
+
+
+def cfg_with_T(cfg: MoeCfg, T: int) -> MoeCfg:
+    c = MoeCfg.from_buffer_copy(cfg)
+    c.T = T
+    return c
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoeError(status, lib.moe_last_error().decode())
+
+
+def validate(cfg: MoeCfg) -> int:
+    return lib.moe_validate(ctypes.byref(cfg))
+
+
+def rows(cfg: MoeCfg) -> int:
+    return lib.moe_rows(ctypes.byref(cfg))
+
+
+def capacity(cfg: MoeCfg) -> int:
+    return lib.moe_capacity(ctypes.byref(cfg))
+
+
+def workspace_bytes(cfg: MoeCfg) -> int:
+    return lib.moe_workspace_bytes(ctypes.byref(cfg))
+
+
+def forward_launches(cfg: MoeCfg) -> int:
+    return lib.moe_forward_launches(ctypes.byref(cfg))
+
+
+def alloc_workspace(cfg: MoeCfg, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(cfg), 256), dtype=torch.uint8, device=device)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def experts(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, sh_gate=None, sh_up=None, sh_down=None,
+            shs_gate=None, shs_up=None, shs_down=None) -> MoeExperts:
+    """Pointer struct of the expert weights (the tensors must outlive its use)."""
+    vals = [w_gate, w_up, w_down, s_gate, s_up, s_down, sh_gate, sh_up, sh_down, shs_gate, shs_up, shs_down]
+    return MoeExperts(*[None if v is None else v.data_ptr() for v in vals])
+
+
+# ---------------------------------------------------------------- entry points
+def moe_route(cfg, x, w_router, logit_bias, select_bias, topk_idx, topk_w, scores, ws, stream=None):
+    _check(lib.moe_route(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_bias), _p(select_bias), _p(topk_idx),
+                         _p(topk_w), _p(scores), _p(ws), ws.numel(), _stream(stream)))
+
+
+def moe_permute(cfg, topk_idx, counts, offsets, row_token, slot_row, drop_mask, ws, stream=None):
+    _check(lib.moe_permute(ctypes.byref(cfg), _p(topk_idx), _p(counts), _p(offsets), _p(row_token), _p(slot_row),
+                           _p(drop_mask), _p(ws), ws.numel(), _stream(stream)))
+
+
+def moe_expert_ffn(cfg, x, offsets, row_token, w: MoeExperts, y_rows, y_shared, ws, stream=None):
+    _check(lib.moe_expert_ffn(ctypes.byref(cfg), _p(x), _p(offsets), _p(row_token), ctypes.byref(w), _p(y_rows),
+                              _p(y_shared), _p(ws), ws.numel(), _stream(stream)))
+
+
+def moe_combine(cfg, y_rows, slot_row, topk_w, y_shared, out, stream=None):
+    _check(lib.moe_combine(ctypes.byref(cfg), _p(y_rows), _p(slot_row), _p(topk_w), _p(y_shared), _p(out),
+                           _stream(stream)))
+
+
+def moe_forward(cfg, x, w_router, logit_bias, select_bias, w: MoeExperts, out, topk_idx, topk_w, drop_mask, ws,
+                stream=None):
+    _check(lib.moe_forward(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_bias), _p(select_bias),
+                           ctypes.byref(w), _p(out), _p(topk_idx), _p(topk_w), _p(drop_mask), _p(ws), ws.numel(),
+                           _stream(stream)))

@@ -1,0 +1,413 @@
+// C ABI of libmoe (declared in include/moe.h): host-side validation, the
+// static workspace plan and launch sequencing.  No allocation, no
+// synchronisation, no device reads on the host.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr int kSingleMaxT = 256;   // T up to which routing runs as split router + one route/permute block
+constexpr int kStreamMaxT = 64;    // T up to which the expert GEMMs use the streaming kernels
+constexpr int64_t kMaxT = 1 << 20;
+
+struct Plan {
+  int T, d, E, k, F, S, FS, act, wdt, score, renorm;
+  float gscale;
+  int64_t cap;  // -1: dropless
+  int64_t R;
+  bool single;
+  int KS, kchunk;
+  int n_rt;
+  int mode, bm;
+  int64_t items_max;
+  int sh_items;
+  size_t o_part, o_hist, o_counts, o_off, o_rowtok, o_slot, o_items, o_nitems, o_h, o_hsh, o_y, o_ysh, total;
+};
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+moe_status make_plan(const moe_cfg* c, Plan* p) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->T < 0 || c->T > kMaxT) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, %lld]", c->T, (long long)kMaxT);
+  if (c->E < 1 || c->E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d outside [1, 256]", c->E);
+  if (c->k < 1 || c->k > kMaxK || c->k > c->E) return fail(MOE_ERR_UNSUPPORTED, "k=%d outside [1, min(E, 8)]", c->k);
+  if (c->d < 128 || c->d % 128 || c->d > 65536) return fail(MOE_ERR_UNSUPPORTED, "d=%d is not a multiple of 128 in [128, 65536]", c->d);
+  if (c->ffn < 128 || c->ffn % 128 || c->ffn > 65536)
+    return fail(MOE_ERR_UNSUPPORTED, "ffn=%d is not a multiple of 128 in [128, 65536]", c->ffn);
+  if (c->n_shared < 0 || c->n_shared > 8) return fail(MOE_ERR_UNSUPPORTED, "n_shared=%d outside [0, 8]", c->n_shared);
+  if (c->n_shared > 0 && (c->ffn_shared < 128 || c->ffn_shared % 128 || c->ffn_shared > 65536))
+    return fail(MOE_ERR_UNSUPPORTED, "ffn_shared=%d is not a multiple of 128 in [128, 65536]", c->ffn_shared);
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "act_dtype=%d is not MOE_F32 or MOE_BF16", c->act_dtype);
+  if (c->expert_dtype != MOE_F32 && c->expert_dtype != MOE_BF16 && c->expert_dtype != MOE_INT4_G128)
+    return fail(MOE_ERR_INVALID_ARG, "expert_dtype=%d is not a moe_dtype", c->expert_dtype);
+  if (!(c->expert_dtype == c->act_dtype || (c->expert_dtype == MOE_INT4_G128 && c->act_dtype == MOE_BF16)))
+    return fail(MOE_ERR_UNSUPPORTED, "expert_dtype=%d with act_dtype=%d", c->expert_dtype, c->act_dtype);
+  if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "score=%d is not a moe_score", c->score);
+  if (c->renorm != 0 && c->renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm=%d is not 0 or 1", c->renorm);
+  if (!isfinite(c->gate_scale)) return fail(MOE_ERR_INVALID_ARG, "gate_scale is not finite");
+  const bool dropless = c->cap_num == 0 && c->cap_den == 0;
+  if (!dropless && (c->cap_den <= 0 || c->cap_num < 0))
+    return fail(MOE_ERR_INVALID_ARG, "capacity %d/%d: need 0/0 or num >= 0, den > 0", c->cap_num, c->cap_den);
+
+  Plan& q = *p;
+  q.T = c->T;
+  q.d = c->d;
+  q.E = c->E;
+  q.k = c->k;
+  q.F = c->ffn;
+  q.S = c->n_shared;
+  q.FS = c->n_shared ? c->ffn_shared : 0;
+  q.act = c->act_dtype;
+  q.wdt = c->expert_dtype;
+  q.score = c->score;
+  q.renorm = c->renorm;
+  q.gscale = c->gate_scale;
+  const int64_t pairs = (int64_t)q.T * q.k;
+  if (dropless) {
+    q.cap = -1;
+    q.R = pairs;
+  } else {
+    const int64_t num = (int64_t)c->cap_num * q.T * q.k, den = (int64_t)c->cap_den * q.E;
+    q.cap = (num + den - 1) / den;
+    if (q.cap > pairs) q.cap = pairs;  // a larger cap keeps everything; also keeps it in int range
+    q.R = q.cap * q.E < pairs ? q.cap * q.E : pairs;
+  }
+  q.single = q.T <= kSingleMaxT;
+  // K split of the small-T router so that the single route block reads at most ~64K partial logits
+  if (q.single && q.T > 0) {
+    int64_t ks = 65536 / ((int64_t)q.T * q.E);
+    const int64_t ksmax = q.d / 128;
+    ks = ks < 1 ? 1 : (ks > ksmax ? ksmax : ks);
+    const int64_t steps = q.d / 128;
+    const int64_t per = (steps + ks - 1) / ks;
+    q.kchunk = (int)(per * 128);
+    q.KS = (int)((q.d + q.kchunk - 1) / q.kchunk);
+  } else {
+    q.KS = 0;
+    q.kchunk = q.d;
+  }
+  q.n_rt = (q.T + kRouteTile - 1) / kRouteTile;
+  q.mode = (q.act == MOE_F32 || q.T <= kStreamMaxT) ? 0 : 1;
+  q.bm = q.mode == 0 ? kDecodeRows : kPrefillRows;
+  q.items_max = q.R / q.bm + (q.R < q.E ? q.R : q.E);
+  q.sh_items = q.S > 0 ? (q.T + q.bm - 1) / q.bm : 0;
+
+  const size_t es = q.act == MOE_F32 ? 4 : 2;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  q.o_part = take(q.single ? (size_t)q.KS * q.T * q.E * 4 : 0);
+  q.o_hist = take(q.single ? 0 : (size_t)q.n_rt * q.E * 4);
+  q.o_counts = take((size_t)q.E * 4);
+  q.o_off = take((size_t)(q.E + 1) * 4);
+  q.o_rowtok = take((size_t)q.R * 4);
+  q.o_slot = take((size_t)pairs * 4);
+  q.o_items = take((size_t)q.items_max * 16);
+  q.o_nitems = take(4);
+  q.o_h = take((size_t)q.R * q.F * es);
+  q.o_hsh = take((size_t)q.T * q.S * q.FS * es);
+  q.o_y = take((size_t)q.R * q.d * es);
+  q.o_ysh = take(q.S ? (size_t)q.T * q.d * es : 0);
+  q.total = o;
+  return MOE_OK;
+}
+
+template <typename T> T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool al4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+
+moe_status check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (!al16(ws)) return fail(MOE_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  if (ws_bytes < p.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.total);
+  return MOE_OK;
+}
+
+moe_status hip_ok(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+RouteArgs route_args(const Plan& p, const float* lb, const float* sb, int32_t* idx, float* gates, float* scores) {
+  RouteArgs r;
+  r.T = p.T;
+  r.d = p.d;
+  r.E = p.E;
+  r.k = p.k;
+  r.score = p.score;
+  r.renorm = p.renorm;
+  r.gate_scale = p.gscale;
+  r.logit_bias = lb;
+  r.select_bias = p.score == MOE_SCORE_SIGMOID ? sb : nullptr;
+  r.idx = idx;
+  r.gates = gates;
+  r.scores = scores;
+  return r;
+}
+
+PermArgs perm_args(const Plan& p, void* ws, int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                   uint8_t* drop) {
+  PermArgs a;
+  a.T = p.T;
+  a.k = p.k;
+  a.E = p.E;
+  a.cap = (int)p.cap;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.row_token = row_token;
+  a.slot_row = slot_row;
+  a.drop = drop;
+  a.items = at<int4>(ws, p.o_items);
+  a.n_items = at<int32_t>(ws, p.o_nitems);
+  a.bm = p.bm;
+  return a;
+}
+
+moe_status check_experts(const Plan& p, const moe_experts* w) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "experts struct is NULL");
+  if (!w->w_gate || !w->w_up || !w->w_down) return fail(MOE_ERR_INVALID_ARG, "routed expert weight pointer is NULL");
+  if (!al16(w->w_gate) || !al16(w->w_up) || !al16(w->w_down))
+    return fail(MOE_ERR_INVALID_ARG, "routed expert weights must be 16-byte aligned");
+  if (p.wdt == MOE_INT4_G128 && (!w->s_gate || !w->s_up || !w->s_down))
+    return fail(MOE_ERR_INVALID_ARG, "INT4 experts need s_gate, s_up and s_down");
+  if (p.S > 0) {
+    if (!w->sh_gate || !w->sh_up || !w->sh_down) return fail(MOE_ERR_INVALID_ARG, "shared expert weight pointer is NULL");
+    if (!al16(w->sh_gate) || !al16(w->sh_up) || !al16(w->sh_down))
+      return fail(MOE_ERR_INVALID_ARG, "shared expert weights must be 16-byte aligned");
+    if (p.wdt == MOE_INT4_G128 && (!w->shs_gate || !w->shs_up || !w->shs_down))
+      return fail(MOE_ERR_INVALID_ARG, "INT4 shared experts need shs_gate, shs_up and shs_down");
+  }
+  return MOE_OK;
+}
+
+FfnArgs ffn_args(const Plan& p, void* ws, const void* x, const int32_t* row_token, const moe_experts* w, void* y,
+                 void* ysh) {
+  FfnArgs a;
+  a.T = p.T;
+  a.d = p.d;
+  a.E = p.E;
+  a.F = p.F;
+  a.S = p.S;
+  a.FS = p.FS;
+  a.R = (int)p.R;
+  a.x = x;
+  a.row_token = row_token;
+  a.items = at<int4>(ws, p.o_items);
+  a.n_items = at<int32_t>(ws, p.o_nitems);
+  a.items_max = (int)p.items_max;
+  a.sh_items = p.sh_items;
+  a.bm = p.bm;
+  a.wg = w->w_gate;
+  a.wu = w->w_up;
+  a.wd = w->w_down;
+  a.sg = w->s_gate;
+  a.su = w->s_up;
+  a.sd = w->s_down;
+  a.shg = w->sh_gate;
+  a.shu = w->sh_up;
+  a.shd = w->sh_down;
+  a.shsg = w->shs_gate;
+  a.shsu = w->shs_up;
+  a.shsd = w->shs_down;
+  a.h = at<void>(ws, p.o_h);
+  a.hsh = at<void>(ws, p.o_hsh);
+  a.y = y;
+  a.ysh = ysh;
+  return a;
+}
+
+// route (+ optionally permute into `pa`) for the planned mode
+moe_status enqueue_route(const Plan& p, const void* x, const void* wr, const RouteArgs& ra, const PermArgs* pa,
+                         void* ws, hipStream_t s) {
+  moe_status st;
+  if (p.single) {
+    float* part = at<float>(ws, p.o_part);
+    if ((st = hip_ok(launch_router_partial(p.act, x, wr, p.T, p.d, p.E, p.kchunk, p.KS, part, s), "router")))
+      return st;
+    PermArgs none{};
+    return hip_ok(launch_route_permute_single(part, p.KS, ra, nullptr, pa ? *pa : none, 1, pa ? 1 : 0, s),
+                  "route/permute");
+  }
+  int32_t* hist = at<int32_t>(ws, p.o_hist);
+  if ((st = hip_ok(launch_router_fused(p.act, x, wr, ra, hist, s), "router"))) return st;
+  if (pa) return hip_ok(launch_permute_multi(ra.idx, hist, *pa, s), "permute");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_validate(const moe_cfg* cfg) {
+  Plan p;
+  return make_plan(cfg, &p);
+}
+
+int64_t moe_rows(const moe_cfg* cfg) {
+  Plan p;
+  if (make_plan(cfg, &p) != MOE_OK) return -1;
+  return p.R;
+}
+
+int64_t moe_capacity(const moe_cfg* cfg) {
+  Plan p;
+  if (make_plan(cfg, &p) != MOE_OK) return -2;
+  return p.cap;
+}
+
+size_t moe_workspace_bytes(const moe_cfg* cfg) {
+  Plan p;
+  if (make_plan(cfg, &p) != MOE_OK) return 0;
+  return p.total;
+}
+
+int32_t moe_forward_launches(const moe_cfg* cfg) {
+  Plan p;
+  if (make_plan(cfg, &p) != MOE_OK || p.T == 0) return 0;
+  return 5;
+}
+
+moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, const float* logit_bias,
+                     const float* select_bias, int32_t* topk_idx, float* topk_w, float* scores, void* ws,
+                     size_t ws_bytes, void* stream) {
+  Plan p;
+  moe_status st;
+  if ((st = make_plan(cfg, &p))) return st;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (p.T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "NULL x, w_router, topk_idx or topk_w");
+  if (!al16(x) || !al16(w_router)) return fail(MOE_ERR_INVALID_ARG, "x and w_router must be 16-byte aligned");
+  if (!al4(topk_idx) || !al4(topk_w) || (scores && !al4(scores)) || (logit_bias && !al4(logit_bias)) ||
+      (select_bias && !al4(select_bias)))
+    return fail(MOE_ERR_INVALID_ARG, "index / fp32 arrays must be 4-byte aligned");
+  RouteArgs ra = route_args(p, logit_bias, select_bias, topk_idx, topk_w, scores);
+  return enqueue_route(p, x, w_router, ra, nullptr, ws, (hipStream_t)stream);
+}
+
+moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                       int32_t* row_token, int32_t* slot_row, uint8_t* drop_mask, void* ws, size_t ws_bytes,
+                       void* stream) {
+  Plan p;
+  moe_status st;
+  if ((st = make_plan(cfg, &p))) return st;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (!topk_idx || !counts || !offsets || !row_token || !slot_row || !drop_mask)
+    return fail(MOE_ERR_INVALID_ARG, "NULL permutation argument");
+  if (!al4(topk_idx) || !al4(counts) || !al4(offsets) || !al4(row_token) || !al4(slot_row))
+    return fail(MOE_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  PermArgs pa = perm_args(p, ws, counts, offsets, row_token, slot_row, drop_mask);
+  if (p.single) {
+    RouteArgs ra = route_args(p, nullptr, nullptr, nullptr, nullptr, nullptr);
+    return hip_ok(launch_route_permute_single(nullptr, 0, ra, topk_idx, pa, 0, 1, s), "permute");
+  }
+  int32_t* hist = at<int32_t>(ws, p.o_hist);
+  if ((st = hip_ok(launch_tile_hist(topk_idx, p.T, p.k, p.E, hist, s), "histogram"))) return st;
+  return hip_ok(launch_permute_multi(topk_idx, hist, pa, s), "permute");
+}
+
+moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets, const int32_t* row_token,
+                          const moe_experts* w, void* y_rows, void* y_shared, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Plan p;
+  moe_status st;
+  if ((st = make_plan(cfg, &p))) return st;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if ((st = check_experts(p, w))) return st;
+  if (!x || !offsets || !row_token || !y_rows) return fail(MOE_ERR_INVALID_ARG, "NULL x, offsets, row_token or y_rows");
+  if ((p.S > 0) != (y_shared != nullptr)) return fail(MOE_ERR_INVALID_ARG, "y_shared must be given iff n_shared > 0");
+  if (!al16(x) || !al16(y_rows) || (y_shared && !al16(y_shared)))
+    return fail(MOE_ERR_INVALID_ARG, "x, y_rows and y_shared must be 16-byte aligned");
+  if (p.T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = hip_ok(launch_tile_map(offsets, p.E, (int)p.R, p.bm, at<int4>(ws, p.o_items), at<int32_t>(ws, p.o_nitems), s),
+                   "tile map")))
+    return st;
+  FfnArgs a = ffn_args(p, ws, x, row_token, w, y_rows, y_shared);
+  if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
+  return hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM");
+}
+
+moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* slot_row, const float* topk_w,
+                       const void* y_shared, void* out, void* stream) {
+  Plan p;
+  moe_status st;
+  if ((st = make_plan(cfg, &p))) return st;
+  if (!y_rows || !slot_row || !topk_w || !out) return fail(MOE_ERR_INVALID_ARG, "NULL combine argument");
+  if ((p.S > 0) != (y_shared != nullptr)) return fail(MOE_ERR_INVALID_ARG, "y_shared must be given iff n_shared > 0");
+  if (!al16(y_rows) || !al16(out) || (y_shared && !al16(y_shared)))
+    return fail(MOE_ERR_INVALID_ARG, "y_rows, y_shared and out must be 16-byte aligned");
+  if (p.T == 0) return MOE_OK;
+  return hip_ok(launch_combine(p.act, y_rows, slot_row, topk_w, y_shared, out, p.T, p.d, p.k, (int)p.R,
+                               (hipStream_t)stream),
+                "combine");
+}
+
+moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, const float* logit_bias,
+                       const float* select_bias, const moe_experts* w, void* out, int32_t* topk_idx, float* topk_w,
+                       uint8_t* drop_mask, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  moe_status st;
+  if ((st = make_plan(cfg, &p))) return st;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if ((st = check_experts(p, w))) return st;
+  if (!x || !w_router || !out || !topk_idx || !topk_w || !drop_mask)
+    return fail(MOE_ERR_INVALID_ARG, "NULL x, w_router, out, topk_idx, topk_w or drop_mask");
+  if (!al16(x) || !al16(w_router) || !al16(out)) return fail(MOE_ERR_INVALID_ARG, "x, w_router and out must be 16-byte aligned");
+  if (!al4(topk_idx) || !al4(topk_w) || (logit_bias && !al4(logit_bias)) || (select_bias && !al4(select_bias)))
+    return fail(MOE_ERR_INVALID_ARG, "index / fp32 arrays must be 4-byte aligned");
+  if (p.T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* slot = at<int32_t>(ws, p.o_slot);
+  int32_t* rowtok = at<int32_t>(ws, p.o_rowtok);
+  RouteArgs ra = route_args(p, logit_bias, select_bias, topk_idx, topk_w, nullptr);
+  PermArgs pa = perm_args(p, ws, at<int32_t>(ws, p.o_counts), at<int32_t>(ws, p.o_off), rowtok, slot, drop_mask);
+  if ((st = enqueue_route(p, x, w_router, ra, &pa, ws, s))) return st;
+  void* ysh = p.S ? at<void>(ws, p.o_ysh) : nullptr;
+  FfnArgs a = ffn_args(p, ws, x, rowtok, w, at<void>(ws, p.o_y), ysh);
+  if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
+  if ((st = hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM"))) return st;
+  return hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Internal interface between the C ABI (api.hip) and the kernels
+// (route.hip, ffn.hip).  Not part of the public header.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum { kF32 = 0, kBF16 = 1, kINT4 = 2 };
+enum { kScoreSoftmax = 0, kScoreSigmoid = 1 };
+
+constexpr int kRouteTile = 64;          // tokens per router / permute block (large T)
+constexpr int kSingleMaxPairs = 8192;   // T*k handled by the single-block route+permute
+constexpr int kDecodeRows = 64;         // rows per item in the streaming (small-M) expert kernels
+constexpr int kPrefillRows = 128;       // rows per item in the tiled (large-M) expert kernels
+
+struct RouteArgs {
+  int T, d, E, k;
+  int score;         // kScoreSoftmax | kScoreSigmoid
+  int renorm;
+  float gate_scale;
+  const float* logit_bias;   // [E] or null
+  const float* select_bias;  // [E] or null
+  int32_t* idx;              // [T][k]
+  float* gates;              // [T][k]
+  float* scores;             // [T][E] or null
+};
+
+struct PermArgs {
+  int T, k, E;
+  int cap;                   // < 0: dropless
+  int32_t* counts;           // [E]
+  int32_t* offsets;          // [E+1]
+  int32_t* row_token;        // [R]
+  int32_t* slot_row;         // [T][k]
+  uint8_t* drop;             // [T][k]
+  int4* items;               // tile map {expert, first row, rows, 0} (null: not built)
+  int32_t* n_items;
+  int bm;                    // rows per tile-map item
+};
+
+struct FfnArgs {
+  int T, d, E, F, S, FS;     // tokens, hidden, experts, ffn, shared experts, shared ffn
+  int R;                     // row bound of the routed row buffers
+  const void* x;             // [T][d]
+  const int32_t* row_token;  // [R]
+  const int4* items;         // routed tile map
+  const int32_t* n_items;
+  int items_max;             // static routed item slots of the grid
+  int sh_items;              // static shared items (ceil(T / bm)) when S > 0
+  int bm;
+  const void *wg, *wu, *wd, *sg, *su, *sd;         // routed weights / INT4 scales
+  const void *shg, *shu, *shd, *shsg, *shsu, *shsd;  // shared weights / INT4 scales
+  void* h;                   // [R][F]     act dtype
+  void* hsh;                 // [T][S*FS]  act dtype
+  void* y;                   // [R][d]     act dtype
+  void* ysh;                 // [T][d]     act dtype
+};
+
+hipError_t launch_router_partial(int act, const void* x, const void* wr, int T, int d, int E, int kchunk, int KS,
+                                 float* part, hipStream_t s);
+hipError_t launch_route_permute_single(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
+                                       const PermArgs& pa, int do_route, int do_perm, hipStream_t s);
+hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int32_t* hist,
+                               hipStream_t s);
+hipError_t launch_tile_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, hipStream_t s);
+hipError_t launch_permute_multi(const int32_t* idx, const int32_t* hist, const PermArgs& pa, hipStream_t s);
+hipError_t launch_tile_map(const int32_t* offsets, int E, int R, int bm, int4* items, int32_t* n_items,
+                           hipStream_t s);
+
+// expert FFN: mode 0 = streaming small-M kernels, 1 = LDS-tiled MFMA kernels
+hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s);
+hipError_t launch_combine(int act, const void* y, const int32_t* slot_row, const float* w, const void* ysh,
+                          void* out, int T, int d, int k, int R, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,556 @@
+// Routing and permutation kernels for gfx950.
+//
+// Router ("MoE: dynamism the compiler cannot remove", natural implementation:
+// logits = router(x), then top-k): an MFMA product of the token tile with the
+// router rows, FP32 scoring (max-subtract-expsum softmax, as in the launch-bound
+// study's FusedSoftmax description, or sigmoid plus a selection-only bias, as
+// in "MoE Research" section 2), then a wave-level top-k over the E scores held
+// in registers (E <= 256: at most 4 per lane), ties to the lower expert index.
+//
+// Permutation (same page, capacity section and batch-1 recipe: fixed-shape
+// scatter into preallocated buffers): an atomic-free expert histogram built
+// from wave ballots, an exclusive scan, and a stable token-major ranking that
+// applies the capacity rule and fills the expert-major row map.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// ------------------------------------------------------------------ helpers
+// One 16-byte chunk per lane per step: bf16 -> 8 K values (one MFMA),
+// f32 -> 4 K values (four MFMAs, one K value each).
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16> {
+  static constexpr int EPC = 8;
+  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) { return mma_bf16(a, b, c); }
+};
+template <> struct Chunk<float> {
+  static constexpr int EPC = 4;
+  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c = mma_f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c);
+    return c;
+  }
+};
+
+// Top-k for one token, executed by one full wave.  key/score hold experts
+// e = lane + 64 * j.  Writes idx/gates of token t (and the k selected experts
+// to sel_tok when it is not null).
+__device__ __forceinline__ void topk_token(const float (&score)[4], const float (&keyv)[4], int E, int k,
+                                           int renorm, float gate_scale, int t, int32_t* idx_out,
+                                           float* gate_out, uint16_t* sel_tok) {
+  const int lane = lane_id();
+  uint64_t key[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    // (order key of the float, then inverted index so that ties pick the lower index);
+    // 0 marks an absent or already selected entry and is below every real entry.
+    key[j] = e < E ? ((uint64_t)float_order_key(keyv[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  }
+  float gsum = 0.f;
+  int sel_e = 0;
+  float sel_s = 0.f;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+    const int owner = e & 63, jj = e >> 6;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j == jj && lane == owner) {
+        key[j] = 0ull;
+        s = score[j];
+      }
+    }
+    s = __shfl(s, owner);
+    gsum += s;
+    if (lane == r) {
+      sel_e = e;
+      sel_s = s;
+    }
+  }
+  if (lane < k) {
+    float g = renorm ? sel_s / gsum : sel_s;
+    g *= gate_scale;
+    idx_out[(size_t)t * k + lane] = sel_e;
+    gate_out[(size_t)t * k + lane] = g;
+    if (sel_tok) sel_tok[lane] = (uint16_t)sel_e;
+  }
+}
+
+// Scores and selection keys from fp32 logits (one wave, one token).
+__device__ __forceinline__ void score_token(float (&logit)[4], const RouteArgs& a, float (&score)[4],
+                                            float (&keyv)[4]) {
+  const int lane = lane_id();
+  if (a.score == kScoreSoftmax) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j < a.E) m = fmaxf(m, logit[j]);
+    m = wave_max(m);
+    float ex[4], s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ex[j] = (lane + 64 * j < a.E) ? expf(logit[j] - m) : 0.f;
+      s += ex[j];
+    }
+    s = wave_sum(s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      score[j] = ex[j] / s;
+      keyv[j] = score[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      score[j] = 1.0f / (1.0f + expf(-logit[j]));
+      keyv[j] = score[j] + ((a.select_bias && e < a.E) ? a.select_bias[e] : 0.f);
+    }
+  }
+}
+
+__device__ __forceinline__ void write_scores(const RouteArgs& a, int t, const float (&score)[4]) {
+  if (!a.scores) return;
+  const int lane = lane_id();
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (lane + 64 * j < a.E) a.scores[(size_t)t * a.E + lane + 64 * j] = score[j];
+}
+
+// Exclusive scan of n <= 256 ints in LDS by one wave; returns the total.
+__device__ __forceinline__ int wave_exclusive_scan256(const int* in, int* out, int n) {
+  const int lane = lane_id();
+  int v[4], run = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = 4 * lane + i;
+    v[i] = p < n ? in[p] : 0;
+  }
+  int local = v[0] + v[1] + v[2] + v[3];
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  run = incl - local;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = 4 * lane + i;
+    if (p < n) out[p] = run;
+    run += v[i];
+  }
+  return __shfl(incl, 63);
+}
+
+// Tile map for the grouped expert GEMMs: one item {expert, first row, rows}
+// per bm-row slice of every expert's kept range.  Called by a whole block
+// after kept[] and off[] (LDS) are final; tmp is LDS scratch of >= 257 ints.
+__device__ void write_tile_map(const int* kept, const int* off, int E, int bm, int4* items, int32_t* n_items,
+                               int* tmp) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += blockDim.x) tmp[e] = (kept[e] + bm - 1) / bm;
+  __syncthreads();
+  if (tid < 64) {
+    int total = wave_exclusive_scan256(tmp, tmp + 256, E);
+    if (tid == 0) *n_items = total;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int n = tmp[e], start = tmp[256 + e];
+    for (int i = 0; i < n; ++i)
+      items[start + i] = make_int4(e, off[e] + i * bm, min(bm, kept[e] - i * bm), 0);
+  }
+}
+
+// ------------------------------------------------------------------ router GEMM
+// Partial logits part[z][t][e] = sum over the z-th K chunk of x[t,:] . w_router[e,:].
+// grid (ceil(T/16), ceil(E/64), KS), block 256: wave w owns experts
+// blockIdx.y*64 + 16w .. +16 for a 16-token tile.
+template <typename TIN>
+__global__ __launch_bounds__(256) void router_partial_kernel(const TIN* __restrict__ x,
+                                                             const TIN* __restrict__ wr, int T, int d, int E,
+                                                             int kchunk, float* __restrict__ part) {
+  constexpr int EPC = Chunk<TIN>::EPC;
+  constexpr int KSTEP = 4 * EPC;
+  const int lane = lane_id(), w = threadIdx.x / 64;
+  const int e0 = blockIdx.y * 64 + w * 16;
+  if (e0 >= E) return;
+  const int t0 = blockIdx.x * 16;
+  const int k0 = blockIdx.z * kchunk, k1 = min(d, k0 + kchunk);
+  const int ta = min(t0 + (lane & 15), T - 1);
+  const int eb = min(e0 + (lane & 15), E - 1);
+  const int g = lane >> 4;
+  const TIN* pa = x + (size_t)ta * d + g * EPC;
+  const TIN* pb = wr + (size_t)eb * d + g * EPC;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int kk = k0;
+  for (; kk + 4 * KSTEP <= k1; kk += 4 * KSTEP) {
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = ld16(pa + kk + u * KSTEP);
+      b[u] = ld16(pb + kk + u * KSTEP);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = Chunk<TIN>::mma(a[u], b[u], acc);
+  }
+  for (; kk < k1; kk += KSTEP) acc = Chunk<TIN>::mma(ld16(pa + kk), ld16(pb + kk), acc);
+  const int e = e0 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * g + i;
+    if (t < T && e < E) part[((size_t)blockIdx.z * T + t) * E + e] = acc[i];
+  }
+}
+
+// ------------------------------------------------------------------ ranking core
+// Ranks one pass of up to blockDim.x pairs (one per thread, token-major order).
+// wcnt: LDS [nwaves][256]; base: LDS [256] running per-expert count (updated).
+// Returns this pair's rank within its expert (undefined when !valid).
+__device__ __forceinline__ int rank_pass(int e, bool valid, int* wcnt, int* base, int E) {
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / 64, nw = blockDim.x / 64;
+  __syncthreads();  // the previous pass's readers of wcnt are done
+  for (int i = tid; i < nw * 256; i += blockDim.x) wcnt[i] = 0;
+  __syncthreads();
+  const uint64_t active = __ballot(valid);
+  const uint64_t peers = match_peers(valid ? (uint32_t)e : 0u, active, 8);
+  if (valid && lane == __ffsll((unsigned long long)peers) - 1) wcnt[w * 256 + e] = __popcll(peers);
+  __syncthreads();
+  for (int x = tid; x < E; x += blockDim.x) {
+    int acc = base[x];
+    for (int ww = 0; ww < nw; ++ww) {
+      const int c = wcnt[ww * 256 + x];
+      wcnt[ww * 256 + x] = acc;
+      acc += c;
+    }
+    base[x] = acc;
+  }
+  __syncthreads();
+  return valid ? wcnt[w * 256 + e] + __popcll(peers & lanemask_lt()) : 0;
+}
+
+// Applies a rank: writes slot_row / drop / row_token for pair i = t*k + j.
+__device__ __forceinline__ void place_pair(const PermArgs& p, int i, int e, bool valid, int rank, const int* off) {
+  const bool kept = valid && (p.cap < 0 || rank < p.cap);
+  if (kept) {
+    const int row = off[e] + rank;
+    p.slot_row[i] = row;
+    p.drop[i] = 0;
+    p.row_token[row] = i / p.k;
+  } else {
+    p.slot_row[i] = -1;
+    p.drop[i] = 1;
+  }
+}
+
+// ------------------------------------------------------------------ single-block route + permute
+// For small T (T*k <= kSingleMaxPairs): one block of 1024 threads sums the partial
+// logits, scores and selects every token (a wave per token), then counts, scans
+// and ranks all pairs.  Either half can be switched off (route-only, permute-only).
+__global__ __launch_bounds__(1024) void route_permute_single_kernel(const float* __restrict__ part, int KS,
+                                                                    RouteArgs ra, const int32_t* idx_in,
+                                                                    PermArgs pa, int do_route, int do_perm) {
+  __shared__ uint16_t sel[kSingleMaxPairs];
+  __shared__ int wcnt[16 * 256];
+  __shared__ int base[256], kept[256], off[257], tmp[512];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / 64;
+  const int T = ra.T, E = ra.E, k = ra.k, n = T * k;
+  if (do_route) {
+    for (int t = w; t < T; t += 16) {
+      float logit[4], score[4], keyv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        float s = 0.f;
+        if (e < E) {
+          for (int z = 0; z < KS; ++z) s += part[((size_t)z * T + t) * E + e];
+          if (ra.logit_bias) s += ra.logit_bias[e];
+        }
+        logit[j] = s;
+      }
+      score_token(logit, ra, score, keyv);
+      write_scores(ra, t, score);
+      topk_token(score, keyv, E, k, ra.renorm, ra.gate_scale, t, ra.idx, ra.gates, sel + t * k);
+    }
+  } else if (do_perm) {
+    for (int i = tid; i < n; i += blockDim.x) {
+      const int e = idx_in[i];
+      sel[i] = (e >= 0 && e < E) ? (uint16_t)e : (uint16_t)0xFFFF;
+    }
+  }
+  if (!do_perm) return;
+  __syncthreads();
+  // phase A: per-expert counts
+  for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;
+  __syncthreads();
+  for (int p0 = 0; p0 < n; p0 += blockDim.x) {
+    const int i = p0 + tid;
+    const int e = i < n ? (int)sel[i] : 0xFFFF;
+    rank_pass(e, e < E, wcnt, base, E);
+  }
+  for (int x = tid; x < E; x += blockDim.x) {
+    pa.counts[x] = base[x];
+    kept[x] = pa.cap < 0 ? base[x] : min(base[x], pa.cap);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int tot = wave_exclusive_scan256(kept, off, E);
+    if (tid == 0) off[E] = tot;
+  }
+  __syncthreads();
+  for (int x = tid; x <= E; x += blockDim.x) pa.offsets[x] = off[x];
+  if (pa.items) write_tile_map(kept, off, E, pa.bm, pa.items, pa.n_items, tmp);
+  // phase B: ranks and placement
+  for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;
+  __syncthreads();
+  for (int p0 = 0; p0 < n; p0 += blockDim.x) {
+    const int i = p0 + tid;
+    const int e = i < n ? (int)sel[i] : 0xFFFF;
+    const bool valid = e < E;
+    const int r = rank_pass(e, valid, wcnt, base, E);
+    if (i < n) place_pair(pa, i, e, valid, r, off);
+  }
+}
+
+// ------------------------------------------------------------------ fused router (large T)
+// One block per 64-token tile computes all E logits with MFMA, scores and
+// selects each token (a wave per token) and writes the tile's expert histogram.
+template <typename TIN>
+__global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict__ x, const TIN* __restrict__ wr,
+                                                           RouteArgs ra, int32_t* __restrict__ hist) {
+  constexpr int EPC = Chunk<TIN>::EPC;
+  constexpr int KSTEP = 4 * EPC;
+  constexpr int LD = 256 + 4;
+  __shared__ float slog[kRouteTile * LD];
+  __shared__ uint16_t sel[kRouteTile * kMaxK];
+  __shared__ int wcnt[4 * 256];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / 64, g = lane >> 4;
+  const int T = ra.T, E = ra.E, d = ra.d, k = ra.k;
+  const int t0 = blockIdx.x * kRouteTile;
+  const int nblk = (E + 15) / 16;
+  // wave w owns expert blocks w, w+4, w+8, w+12
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const TIN* pa[4];
+  const TIN* pb[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) pa[m] = x + (size_t)min(t0 + 16 * m + (lane & 15), T - 1) * d + g * EPC;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) pb[b] = wr + (size_t)min(16 * (w + 4 * b) + (lane & 15), E - 1) * d + g * EPC;
+  for (int kk = 0; kk < d; kk += KSTEP) {
+    u32x4 av[4], bv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) av[m] = ld16(pa[m] + kk);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (w + 4 * b < nblk) bv[b] = ld16(pb[b] + kk);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (w + 4 * b < nblk)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m][b] = Chunk<TIN>::mma(av[m], bv[b], acc[m][b]);
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (w + 4 * b >= nblk) continue;
+    const int e = 16 * (w + 4 * b) + (lane & 15);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) slog[(16 * m + 4 * g + i) * LD + e] = acc[m][b][i];
+  }
+  __syncthreads();
+  const int nt = min(kRouteTile, T - t0);
+  for (int tt = w; tt < nt; tt += 4) {
+    float logit[4], score[4], keyv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      float s = 0.f;
+      if (e < E) {
+        s = slog[tt * LD + e];
+        if (ra.logit_bias) s += ra.logit_bias[e];
+      }
+      logit[j] = s;
+    }
+    score_token(logit, ra, score, keyv);
+    write_scores(ra, t0 + tt, score);
+    topk_token(score, keyv, E, k, ra.renorm, ra.gate_scale, t0 + tt, ra.idx, ra.gates, sel + tt * k);
+  }
+  __syncthreads();
+  // tile histogram over the tile's pairs (at most 64 * 8 = 512: two passes of 256)
+  int* base = reinterpret_cast<int*>(slog);  // reuse: 256 ints
+  for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;
+  __syncthreads();
+  const int np = nt * k;
+  for (int p0 = 0; p0 < np; p0 += blockDim.x) {
+    const int i = p0 + tid;
+    const int e = i < np ? (int)sel[i] : 0xFFFF;
+    rank_pass(e, e < E, wcnt, base, E);
+  }
+  for (int x = tid; x < E; x += blockDim.x) hist[(size_t)blockIdx.x * E + x] = base[x];
+}
+
+// Tile histogram of given indices (for the standalone permute on large T).
+__global__ __launch_bounds__(512) void tile_hist_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                        int32_t* __restrict__ hist) {
+  __shared__ int wcnt[8 * 256];
+  __shared__ int base[256];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRouteTile, nt = min(kRouteTile, T - t0), np = nt * k;
+  for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;
+  __syncthreads();
+  for (int p0 = 0; p0 < np; p0 += blockDim.x) {
+    const int i = p0 + tid;
+    int e = 0xFFFF;
+    if (i < np) {
+      const int v = idx[(size_t)t0 * k + i];
+      e = (v >= 0 && v < E) ? v : 0xFFFF;
+    }
+    rank_pass(e, e < E, wcnt, base, E);
+  }
+  for (int x = tid; x < E; x += blockDim.x) hist[(size_t)blockIdx.x * E + x] = base[x];
+}
+
+// ------------------------------------------------------------------ multi-block permute (large T)
+// One block per 64-token tile: expert bases from the tile histograms of the
+// tiles before it, totals from all of them, then the tile's pairs are ranked
+// and placed.  Block 0 also writes counts, offsets and the tile map.
+__global__ __launch_bounds__(512) void permute_multi_kernel(const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ hist, int n_tiles,
+                                                            PermArgs pa) {
+  __shared__ int wcnt[8 * 256];
+  __shared__ int red_b[512], red_t[512];
+  __shared__ int base[256], tot[256], kept[256], off[257], tmp[512];
+  const int tid = threadIdx.x;
+  const int E = pa.E, k = pa.k, T = pa.T, tile = blockIdx.x;
+  // partial sums over tiles: thread -> (expert, part)
+  const int P = max(1, (int)blockDim.x / E);
+  {
+    int sb = 0, st = 0;
+    const int e = tid % E, part = tid / E;
+    if (part < P) {
+      for (int r = part; r < n_tiles; r += P) {
+        const int v = hist[(size_t)r * E + e];
+        st += v;
+        if (r < tile) sb += v;
+      }
+    }
+    red_b[tid] = sb;
+    red_t[tid] = st;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    int sb = 0, st = 0;
+    for (int part = 0; part < P; ++part) {
+      sb += red_b[part * E + e];
+      st += red_t[part * E + e];
+    }
+    base[e] = sb;
+    tot[e] = st;
+    kept[e] = pa.cap < 0 ? st : min(st, pa.cap);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int s = wave_exclusive_scan256(kept, off, E);
+    if (tid == 0) off[E] = s;
+  }
+  __syncthreads();
+  if (tile == 0) {
+    for (int x = tid; x < E; x += blockDim.x) pa.counts[x] = tot[x];
+    for (int x = tid; x <= E; x += blockDim.x) pa.offsets[x] = off[x];
+    if (pa.items) write_tile_map(kept, off, E, pa.bm, pa.items, pa.n_items, tmp);
+  }
+  const int t0 = tile * kRouteTile, nt = min(kRouteTile, T - t0), np = nt * k;
+  for (int p0 = 0; p0 < np; p0 += blockDim.x) {
+    const int i = p0 + tid;
+    int e = 0xFFFF;
+    if (i < np) {
+      const int v = idx[(size_t)t0 * k + i];
+      e = (v >= 0 && v < E) ? v : 0xFFFF;
+    }
+    const bool valid = e < E;
+    const int r = rank_pass(e, valid, wcnt, base, E);
+    if (i < np) place_pair(pa, t0 * k + i, e, valid, r, off);
+  }
+}
+
+// ------------------------------------------------------------------ tile map from offsets
+// For moe_expert_ffn called with caller-provided offsets: clamps them into
+// [0, R] (non-decreasing) and writes the tile map.
+__global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict__ offsets, int E, int R, int bm,
+                                                       int4* items, int32_t* n_items) {
+  __shared__ int off[257], kept[256], tmp[512];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int prev = 0;
+    for (int e = 0; e <= E; ++e) {
+      int v = e == 0 ? 0 : offsets[e];
+      v = min(max(v, prev), R);
+      off[e] = v;
+      prev = v;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) kept[e] = off[e + 1] - off[e];
+  __syncthreads();
+  write_tile_map(kept, off, E, bm, items, n_items, tmp);
+}
+
+// ------------------------------------------------------------------ host launchers
+hipError_t launch_router_partial(int act, const void* x, const void* wr, int T, int d, int E, int kchunk, int KS,
+                                 float* part, hipStream_t s) {
+  dim3 grid((T + 15) / 16, (E + 63) / 64, KS);
+  if (act == kF32)
+    hipLaunchKernelGGL(router_partial_kernel<float>, grid, dim3(256), 0, s, (const float*)x, (const float*)wr, T, d,
+                       E, kchunk, part);
+  else
+    hipLaunchKernelGGL(router_partial_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, T, d, E,
+                       kchunk, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute_single(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
+                                       const PermArgs& pa, int do_route, int do_perm, hipStream_t s) {
+  hipLaunchKernelGGL(route_permute_single_kernel, dim3(1), dim3(1024), 0, s, part, KS, ra, idx_in, pa, do_route,
+                     do_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int32_t* hist,
+                               hipStream_t s) {
+  dim3 grid((ra.T + kRouteTile - 1) / kRouteTile);
+  if (act == kF32)
+    hipLaunchKernelGGL(router_fused_kernel<float>, grid, dim3(256), 0, s, (const float*)x, (const float*)wr, ra, hist);
+  else
+    hipLaunchKernelGGL(router_fused_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, hipStream_t s) {
+  hipLaunchKernelGGL(tile_hist_kernel, dim3((T + kRouteTile - 1) / kRouteTile), dim3(512), 0, s, idx, T, k, E, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_multi(const int32_t* idx, const int32_t* hist, const PermArgs& pa, hipStream_t s) {
+  const int n_tiles = (pa.T + kRouteTile - 1) / kRouteTile;
+  hipLaunchKernelGGL(permute_multi_kernel, dim3(n_tiles), dim3(512), 0, s, idx, hist, n_tiles, pa);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_map(const int32_t* offsets, int E, int R, int bm, int4* items, int32_t* n_items,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(256), 0, s, offsets, E, R, bm, items, n_items);
+  return hipGetLastError();
+}
+
+}  // namespace moe
