@@ -1,0 +1,282 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+Default workload: the OLMoE-1B-7B-shaped layer (d=2048, E=64, k=8, SwiGLU
+ffn=1024, bf16, softmax top-k without renorm, router skew bias std 0.5) at
+T=4096 tokens, seeded synthetic inputs resident in HBM.  A step is one
+moe_forward: router + top-k, permutation, gate/up GEMM, down GEMM, combine.
+
+Prints one JSON line.  `roofline` is for the dominant kernel (the grouped
+gate/up SwiGLU GEMM, MFMA-bound), timed with HIP events recorded by the
+library around that launch on its own stream during the timed steps.
+`cpu_baseline` is the FP64 oracle on a bounded token sample of the same
+workload.  `decode` adds the same layer at decode sizes (hipGraph replays,
+weights rotated over several copies so the Infinity Cache does not serve
+them), reported against HBM bandwidth.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s at 1 MI355X; decode HBM GB/s and prefill MFMA % of peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--T", type=int, default=4096)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles created through the HIP runtime (for the library's timing hook)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev[i] = h
+
+    def ms(self, a, b) -> float:
+        f = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(ctypes.c_void_p(self.ev[b])) == 0
+        assert self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(self.ev[a]),
+                                            ctypes.c_void_p(self.ev[b])) == 0
+        return f.value
+
+    def slice(self, i, n):
+        return ctypes.cast(ctypes.byref(self.ev, i * ctypes.sizeof(ctypes.c_void_p)), ctypes.POINTER(ctypes.c_void_p))
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(h))
+
+
+def moe_layer(sp, lay):
+    from mixture_experts_layer_13_amd import binding as B
+    from mixture_experts_layer_13_amd.layer import MoeLayer
+    cfg = B.make_cfg(1, sp.d, sp.E, sp.k, sp.ffn, sp.n_shared, sp.ffn_shared, act=sp.act, expert=sp.expert,
+                     score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale, capacity=sp.capacity)
+    return MoeLayer(cfg, lay.w_router, lay.w_gate, lay.w_up, lay.w_down, logit_bias=lay.logit_bias,
+                    select_bias=lay.select_bias, s_gate=lay.s_gate, s_up=lay.s_up, s_down=lay.s_down,
+                    sh_gate=lay.sh_gate, sh_up=lay.sh_up, sh_down=lay.sh_down)
+
+
+def expert_bytes(sp):
+    n = 3 * sp.d * sp.ffn
+    return n // 2 + (3 * sp.d * sp.ffn // 128) * 2 if sp.expert == "int4" else n * (4 if sp.expert == "f32" else 2)
+
+
+def alg_work(sp, T, idx, drop):
+    """Algorithmic bytes and flops of one forward: touched expert weights, shared
+    experts, router weight, x and out; flops 6 d F per kept pair + 6 d Fs S T + 2 T d E."""
+    import torch
+    kept = (drop == 0)
+    touched = int(torch.unique(idx[kept]).numel()) if kept.any() else 0
+    n_kept = int(kept.sum().item())
+    es = 4 if sp.act == "f32" else 2
+    byts = (touched * expert_bytes(sp) + sp.n_shared * 3 * sp.d * sp.ffn_shared * es + sp.E * sp.d * es
+            + 2 * T * sp.d * es)
+    gateup = 4.0 * sp.d * sp.ffn * n_kept + 4.0 * sp.d * sp.ffn_shared * sp.n_shared * T
+    flops = 1.5 * gateup + 2.0 * T * sp.d * sp.E
+    return dict(bytes=byts, flops=flops, gateup_flops=gateup, touched=touched, kept=n_kept)
+
+
+def traffic_record(kernel_src):
+    """HBM bytes of the dominant kernel from the committed rocprofv3 counter summary,
+    valid only while the kernel source is the one the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", "gateup_tiled_olmoe_T4096_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(sp, lay, x, n_tokens):
+    import oracle as O
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_harness import ExpertSource, to_f64
+    xs = x[:n_tokens]
+    xf, wr, lb = to_f64(xs), to_f64(lay.w_router), to_f64(lay.logit_bias)
+
+    class HostWeights:  # expert weights copied to host memory before timing (inputs resident)
+        w_gate = [t.cpu() for t in lay.w_gate]
+        w_up = [t.cpu() for t in lay.w_up]
+        w_down = [t.cpu() for t in lay.w_down]
+
+    host = ExpertSource(sp, HostWeights)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    O.moe_layer(xf, wr, host, sp.E, sp.k, score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale,
+                logit_bias=lb, capacity=sp.capacity)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_tokens} of the {x.shape[0]} tokens (full FP64 layer on the sample: routing, "
+                      f"all selected expert FFNs from bf16 bit patterns, combine); {dt:.1f} s"}
+
+
+def decode_sweep(sp, lay, Ts=(1, 8, 32, 64), replays=200, copies=4):
+    """Decode-sized forwards as hipGraph replays over `copies` weight copies (cold in
+    the 256 MB Infinity Cache), reported as achieved HBM bandwidth."""
+    import torch
+
+    import moe_synth as S
+    layers = [moe_layer(sp, lay)]
+    keep = []
+    for c in range(1, copies):
+        cp = S.Layer(sp, lay.w_router.clone(), lay.logit_bias, lay.select_bias, lay.w_gate.clone(),
+                     lay.w_up.clone(), lay.w_down.clone())
+        keep.append(cp)
+        layers.append(moe_layer(sp, cp))
+    res = {}
+    s = torch.cuda.Stream()
+    for T in Ts:
+        x = S.make_tokens(sp, T, device="cuda")
+        graphs, outs = [], []
+        for ml in layers:
+            o = (torch.empty((T, sp.d), dtype=torch.bfloat16, device="cuda"),
+                 torch.empty((T, sp.k), dtype=torch.int32, device="cuda"),
+                 torch.empty((T, sp.k), dtype=torch.float32, device="cuda"),
+                 torch.empty((T, sp.k), dtype=torch.uint8, device="cuda"))
+            ml.workspace(ml.cfg_for(T))
+            with torch.cuda.stream(s):
+                ml.forward(x, *o)  # eager warm-up on the capture stream
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                ml.forward(x, *o)
+            graphs.append(g)
+            outs.append(o)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(replays):
+            graphs[i % len(graphs)].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / replays
+        w = alg_work(sp, T, outs[0][1], outs[0][3])
+        gbs = w["bytes"] / (us * 1e-6) / 1e9
+        res[f"T{T}"] = {"us_per_layer": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
+                        "alg_bytes": w["bytes"], "touched_experts": w["touched"], "hbm_GBps": round(gbs, 1),
+                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del graphs
+    return {"layer": "olmoe_1b7b", "method": f"hipGraph replay, {copies} weight copies round-robin, "
+                                              f"{replays} replays", "points": res}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures the layer on one GPU only (asked for {max(args.gpus, world)}): the path has no "
+              "multi-GPU mode (expert-parallel sharding is a design note, not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import moe_synth as S
+    from mixture_experts_layer_13_amd import binding as B
+
+    torch.cuda.set_device(0)
+    sp = S.SPECS["olmoe"]
+    T = args.T
+    lay = S.make_layer(sp, device="cuda")
+    x = S.make_tokens(sp, T, device="cuda")
+    ml = moe_layer(sp, lay)
+    cfg = ml.cfg_for(T)
+    nl = B.forward_launches(cfg)
+    outs = (torch.empty((T, sp.d), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((T, sp.k), dtype=torch.int32, device="cuda"),
+            torch.empty((T, sp.k), dtype=torch.float32, device="cuda"),
+            torch.empty((T, sp.k), dtype=torch.uint8, device="cuda"))
+    for _ in range(args.warmup):
+        ml.forward(x, *outs)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = HipEvents(K * (nl + 1))
+    t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record()
+    for i in range(K):
+        B.lib.moe_set_timing_events(ev.slice(i * (nl + 1), nl + 1), nl + 1)
+        ml.forward(x, *outs)
+    t_all1.record()
+    B.lib.moe_set_timing_events(None, 0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_all0.elapsed_time(t_all1) / K
+    names = ["router", "permute", "gateup", "down", "combine"]
+    per = {n: 0.0 for n in names}
+    for i in range(K):
+        b = i * (nl + 1)
+        for j, n in enumerate(names):
+            per[n] += ev.ms(b + j, b + j + 1) / K
+    ev.close()
+
+    w = alg_work(sp, T, outs[1], outs[3])
+    t_gu = per["gateup"] * 1e-3
+    achieved = w["gateup_flops"] / t_gu / 1e12
+    traffic = traffic_record(os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", "ffn.hip"))
+    line = {
+        "metric": METRIC,
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"olmoe_1b7b_layer_T{T}", "T": T, "d": sp.d, "E": sp.E, "k": sp.k,
+                   "ffn": sp.ffn, "launches_per_layer": nl},
+        "roofline": {"bound": "mfma", "kernel": "ffn_tiled_kernel<bf16,gate/up>", "achieved": round(achieved, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "avg_launch_us": round(per["gateup"] * 1e3, 2),
+                     "alg_flops_per_launch": w["gateup_flops"]},
+        "layer": {"per_launch_us": {n: round(v * 1e3, 2) for n, v in per.items()},
+                  "alg_flops": w["flops"], "alg_bytes": w["bytes"],
+                  "mfma_frac": round(w["flops"] / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                  "wall_s_timed": round(wall, 3)},
+    }
+    if not args.no_decode:
+        line["decode"] = decode_sweep(sp, lay)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_tokens=256)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

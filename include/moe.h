@@ -167,6 +167,15 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router,
 /* Kernel launches moe_forward enqueues for this cfg (0 on an invalid cfg). */
 int32_t moe_forward_launches(const moe_cfg* cfg);
 
+/* Measurement hook for per-kernel timing with HIP events.  When `events` is
+ * not NULL, later moe_forward calls on this host thread record events[i] (a
+ * caller-created hipEvent_t) on their stream just before their i-th launch
+ * and events[n] after the last one, n = moe_forward_launches(cfg); the caller
+ * reads them with hipEventElapsedTime after synchronising.  n_events must be
+ * at least n + 1 or the hook is ignored.  NULL turns it off.  Meant for eager
+ * timing runs, not for graph capture.  Always MOE_OK. */
+moe_status moe_set_timing_events(void* const* events, int32_t n_events);
+
 const char* moe_status_str(moe_status s);
 const char* moe_last_error(void);
 int32_t moe_abi_version(void);

@@ -62,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [C, P, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [C, P, P, P, P, ctypes.POINTER(MoeExperts), P, P, P, P, P,
                                        ctypes.c_size_t, P]),
+        "moe_set_timing_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int32, []),

@@ -15,6 +15,13 @@ using namespace moe;
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local void* const* g_events = nullptr;
+thread_local int g_nevents = 0;
+
+// records the i-th timing event of moe_forward when the hook is armed
+void mark(int i, int n_launches, hipStream_t s) {
+  if (g_events && g_nevents > n_launches) (void)hipEventRecord((hipEvent_t)g_events[i], s);
+}
 
 moe_status fail(moe_status s, const char* fmt, ...) {
   va_list ap;
@@ -35,7 +42,7 @@ struct Plan {
   int64_t R;
   bool single;
   int KS, kchunk;
-  int n_rt;
+  int rt, n_rt;
   int mode, bm;
   int64_t items_max;
   int sh_items;
@@ -106,9 +113,11 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     q.KS = 0;
     q.kchunk = q.d;
   }
-  q.n_rt = (q.T + kRouteTile - 1) / kRouteTile;
+  q.rt = (q.E > 128 && q.act == MOE_BF16) ? 32 : 16;
+  q.n_rt = (q.T + q.rt - 1) / q.rt;
   q.mode = (q.act == MOE_F32 || q.T <= kStreamMaxT) ? 0 : 1;
-  q.bm = q.mode == 0 ? kDecodeRows : kPrefillRows;
+  // streaming kernels take items of 16, 32 or 64 rows (an expert gets each token at most once)
+  q.bm = q.mode == 1 ? kPrefillRows : (q.T <= 16 ? 16 : (q.T <= 32 ? 32 : kDecodeRows));
   q.items_max = q.R / q.bm + (q.R < q.E ? q.R : q.E);
   q.sh_items = q.S > 0 ? (q.T + q.bm - 1) / q.bm : 0;
 
@@ -185,6 +194,7 @@ PermArgs perm_args(const Plan& p, void* ws, int32_t* counts, int32_t* offsets, i
   a.items = at<int4>(ws, p.o_items);
   a.n_items = at<int32_t>(ws, p.o_nitems);
   a.bm = p.bm;
+  a.rt = p.rt;
   return a;
 }
 
@@ -241,22 +251,17 @@ FfnArgs ffn_args(const Plan& p, void* ws, const void* x, const int32_t* row_toke
   return a;
 }
 
-// route (+ optionally permute into `pa`) for the planned mode
-moe_status enqueue_route(const Plan& p, const void* x, const void* wr, const RouteArgs& ra, const PermArgs* pa,
-                         void* ws, hipStream_t s) {
+// router (logits, scores, top-k, gates) for the planned mode
+moe_status enqueue_route(const Plan& p, const void* x, const void* wr, const RouteArgs& ra, void* ws, hipStream_t s) {
   moe_status st;
   if (p.single) {
     float* part = at<float>(ws, p.o_part);
     if ((st = hip_ok(launch_router_partial(p.act, x, wr, p.T, p.d, p.E, p.kchunk, p.KS, part, s), "router")))
       return st;
     PermArgs none{};
-    return hip_ok(launch_route_permute_single(part, p.KS, ra, nullptr, pa ? *pa : none, 1, pa ? 1 : 0, s),
-                  "route/permute");
+    return hip_ok(launch_route_permute_single(part, p.KS, ra, nullptr, none, 1, 0, s), "route");
   }
-  int32_t* hist = at<int32_t>(ws, p.o_hist);
-  if ((st = hip_ok(launch_router_fused(p.act, x, wr, ra, hist, s), "router"))) return st;
-  if (pa) return hip_ok(launch_permute_multi(ra.idx, hist, *pa, s), "permute");
-  return MOE_OK;
+  return hip_ok(launch_router_fused(p.act, x, wr, ra, p.rt, at<int32_t>(ws, p.o_hist), s), "router");
 }
 
 }  // namespace
@@ -306,7 +311,7 @@ moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, co
       (select_bias && !al4(select_bias)))
     return fail(MOE_ERR_INVALID_ARG, "index / fp32 arrays must be 4-byte aligned");
   RouteArgs ra = route_args(p, logit_bias, select_bias, topk_idx, topk_w, scores);
-  return enqueue_route(p, x, w_router, ra, nullptr, ws, (hipStream_t)stream);
+  return enqueue_route(p, x, w_router, ra, ws, (hipStream_t)stream);
 }
 
 moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
@@ -327,7 +332,7 @@ moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* cou
     return hip_ok(launch_route_permute_single(nullptr, 0, ra, topk_idx, pa, 0, 1, s), "permute");
   }
   int32_t* hist = at<int32_t>(ws, p.o_hist);
-  if ((st = hip_ok(launch_tile_hist(topk_idx, p.T, p.k, p.E, hist, s), "histogram"))) return st;
+  if ((st = hip_ok(launch_tile_hist(topk_idx, p.T, p.k, p.E, p.rt, hist, s), "histogram"))) return st;
   return hip_ok(launch_permute_multi(topk_idx, hist, pa, s), "permute");
 }
 
@@ -387,12 +392,36 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   int32_t* rowtok = at<int32_t>(ws, p.o_rowtok);
   RouteArgs ra = route_args(p, logit_bias, select_bias, topk_idx, topk_w, nullptr);
   PermArgs pa = perm_args(p, ws, at<int32_t>(ws, p.o_counts), at<int32_t>(ws, p.o_off), rowtok, slot, drop_mask);
-  if ((st = enqueue_route(p, x, w_router, ra, &pa, ws, s))) return st;
+  const int nl = 5;
+  mark(0, nl, s);
+  if (p.single) {
+    float* part = at<float>(ws, p.o_part);
+    if ((st = hip_ok(launch_router_partial(p.act, x, w_router, p.T, p.d, p.E, p.kchunk, p.KS, part, s), "router")))
+      return st;
+    mark(1, nl, s);
+    if ((st = hip_ok(launch_route_permute_single(part, p.KS, ra, nullptr, pa, 1, 1, s), "route/permute"))) return st;
+  } else {
+    int32_t* hist = at<int32_t>(ws, p.o_hist);
+    if ((st = hip_ok(launch_router_fused(p.act, x, w_router, ra, p.rt, hist, s), "router"))) return st;
+    mark(1, nl, s);
+    if ((st = hip_ok(launch_permute_multi(ra.idx, hist, pa, s), "permute"))) return st;
+  }
+  mark(2, nl, s);
   void* ysh = p.S ? at<void>(ws, p.o_ysh) : nullptr;
   FfnArgs a = ffn_args(p, ws, x, rowtok, w, at<void>(ws, p.o_y), ysh);
   if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
+  mark(3, nl, s);
   if ((st = hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM"))) return st;
-  return hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
+  mark(4, nl, s);
+  st = hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
+  mark(5, nl, s);
+  return st;
+}
+
+moe_status moe_set_timing_events(void* const* events, int32_t n_events) {
+  g_events = events;
+  g_nevents = events ? n_events : 0;
+  return MOE_OK;
 }
 
 const char* moe_status_str(moe_status s) {

@@ -52,25 +52,57 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------- wave ops
+// Whole-wave reductions (all 64 lanes active) in low-latency form: four DPP
+// steps combine each lane with a partner inside its row of 16 (swap neighbours,
+// swap pairs, mirror halves of 8, mirror the row of 16), leaving every row
+// uniform; the four row values are then read into scalars and combined in a
+// fixed order, so every lane gets the same, deterministic result.
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+constexpr int kDppSwap1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppSwap2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f32(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int CTRL> __device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(x >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)x);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppSwap1>(v));
+  v = fmaxf(v, dpp_f32<kDppSwap2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f32<kDppSwap1>(v);
+  v += dpp_f32<kDppSwap2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o);
-    v = w > v ? w : v;
-  }
-  return v;
+  v = max_u64(v, dpp_u64<kDppSwap1>(v));
+  v = max_u64(v, dpp_u64<kDppSwap2>(v));
+  v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+  v = max_u64(v, dpp_u64<kDppMirror>(v));
+  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)), max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
 // Monotone map float -> uint32 (total order; -0 is canonicalised to +0 first).

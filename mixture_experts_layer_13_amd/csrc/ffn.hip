@@ -48,6 +48,19 @@ __device__ __forceinline__ u32x4 int4x8_to_bf16(uint32_t w) {
   return r;
 }
 
+// Same, times the group scale, rounded once to bf16 (operand of the tiled kernels).
+__device__ __forceinline__ u32x4 int4x8_to_bf16_scaled(uint32_t w, float sc) {
+  const uint32_t x = w ^ 0x88888888u;
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float lo = (__uint_as_float(0x4B000000u | ((x >> (8 * p)) & 0xFu)) - 8388616.0f) * sc;
+    const float hi = (__uint_as_float(0x4B000000u | ((x >> (8 * p + 4)) & 0xFu)) - 8388616.0f) * sc;
+    r[p] = pack_bf16x2(lo, hi);
+  }
+  return r;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // ------------------------------------------------------------------ streaming (small-M) kernels
@@ -127,20 +140,27 @@ template <> __device__ __forceinline__ f32x4 dstep<INT4>(const u32x4 (&av)[4], u
 }
 
 // GATEUP: h[row][n] = silu(A Wg^T) * (A Wu^T); else y[row][n] = A Wd^T.
-// grid: items_max * (N / 16) routed blocks, then sh_items * (Ns / 16) shared blocks.
-template <typename TW, bool GATEUP>
+// A block owns one item (<= 16 * MT rows of one expert).  Gate/up (K = d,
+// large): the four waves split K into quarters for the same 16 channels and
+// add their partial sums in LDS in wave order.  Down (K = ffn): each wave owns
+// 16 channels over the whole K, so a block covers 64.  Steps are unrolled U
+// deep so each lane keeps U weight loads per matrix in flight.
+// grid: items_max * (N / channels per block) routed blocks, then the shared blocks.
+template <typename TW, bool GATEUP, int MT>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   using D = Dec<TW>;
   using TA = typename D::TA;
   constexpr int NM = GATEUP ? 2 : 1;
-  constexpr int MT = kDecodeRows / 16;
-  constexpr int U = D::U, AL = D::AL, KSTEP = D::KSTEP;
-  __shared__ f32x4 red[3][NM][MT][64];
+  constexpr int KSPLIT = GATEUP ? 4 : 1;         // waves sharing one channel block
+  constexpr int CPB = 16 * (4 / KSPLIT);          // channels per block
+  constexpr int U = (std::is_same<TW, INT4>::value || MT == 4) ? 4 : 8;
+  constexpr int AL = D::AL, KSTEP = D::KSTEP;
+  __shared__ f32x4 red[KSPLIT > 1 ? 3 : 1][NM][MT][64];
   const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
 
   const int Nr = GATEUP ? a.F : a.d;
   const int Ns = GATEUP ? a.S * a.FS : a.d;
-  const int nbr = Nr / 16, nbs = Ns / 16;
+  const int nbr = Nr / CPB, nbs = Ns / CPB;
   const int routed_blocks = a.items_max * nbr;
   int bid = blockIdx.x, e = 0, row0, mrows, nb;
   const bool shared = bid >= routed_blocks;
@@ -160,7 +180,19 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
     mrows = min(a.bm, a.T - row0);
   }
   const int nmt = (mrows + 15) / 16;
-  const int n = nb * 16 + c;
+  const int kpart = KSPLIT > 1 ? w : 0;
+  const int n = nb * CPB + (KSPLIT > 1 ? 0 : 16 * w) + c;
+
+  const int K = GATEUP ? a.d : (shared ? a.FS : a.F);  // K of one segment
+  const int nseg = (!GATEUP && shared) ? a.S : 1;
+  // weight rows first: their loads do not wait for the activation row lookup
+  BRow<TW> b0 = GATEUP ? BRow<TW>(shared ? a.shg : expert_mat<TW>(a.wg, e, a.F, a.d), n, K, g,
+                                  shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d))
+                       : BRow<TW>(shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, K), n, K, g,
+                                  shared ? a.shsd : expert_scales(a.sd, e, a.d, K));
+  BRow<TW> b1 = GATEUP ? BRow<TW>(shared ? a.shu : expert_mat<TW>(a.wu, e, a.F, a.d), n, K, g,
+                                  shared ? a.shsu : expert_scales(a.su, e, a.F, a.d))
+                       : b0;
 
   // activation rows (clamped into the item so every load is in bounds)
   const TA* arow[MT];
@@ -183,19 +215,14 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[m][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int K = GATEUP ? a.d : (shared ? a.FS : a.F);  // K of one segment
-  const int nseg = (!GATEUP && shared) ? a.S : 1;
   for (int seg = 0; seg < nseg; ++seg) {
-    BRow<TW> b0 = GATEUP ? BRow<TW>(shared ? a.shg : expert_mat<TW>(a.wg, e, a.F, a.d), n, K, g,
-                                    shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d))
-                         : BRow<TW>(shared ? expert_mat<TW>(a.shd, seg, a.d, K) : expert_mat<TW>(a.wd, e, a.d, K), n,
-                                    K, g, shared ? expert_scales(a.shsd, seg, a.d, K) : expert_scales(a.sd, e, a.d, K));
-    BRow<TW> b1 = GATEUP ? BRow<TW>(shared ? a.shu : expert_mat<TW>(a.wu, e, a.F, a.d), n, K, g,
-                                    shared ? a.shsu : expert_scales(a.su, e, a.F, a.d))
-                         : b0;
+    if (seg > 0) {  // next slab of the shared down projection: [S][d][FS]
+      b0 = BRow<TW>(expert_mat<TW>(a.shd, seg, a.d, K), n, K, g, expert_scales(a.shsd, seg, a.d, K));
+      b1 = b0;
+    }
     const int aoff = seg * K;
     const int nsteps = K / KSTEP;
-    const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
+    const int s0 = kpart * nsteps / KSPLIT, s1 = (kpart + 1) * nsteps / KSPLIT;
     for (int st = s0; st < s1; st += U) {
       u32x4 bq[NM][U];
       float sc[NM][U];
@@ -210,6 +237,12 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
             bq[NM - 1][u] = b1.load(kb);
             sc[NM - 1][u] = b1.scale(kb);
           }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (st + u < s1) {
+          const int kb = (st + u) * KSTEP;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             if (mt < nmt)
@@ -231,21 +264,23 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
     }
   }
 
-  // reduce the four K slices (fixed order) and write
-  if (w > 0) {
+  if (KSPLIT > 1) {
+    // add the K slices (fixed order) in wave 0
+    if (w > 0) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          if (mt < nmt) red[w - 1][m][mt][lane] = acc[m][mt];
+    }
+    __syncthreads();
+    if (w != 0) return;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        if (mt < nmt) red[w - 1][m][mt][lane] = acc[m][mt];
+        if (mt < nmt) acc[m][mt] = ((acc[m][mt] + red[0][m][mt][lane]) + red[1][m][mt][lane]) + red[2][m][mt][lane];
   }
-  __syncthreads();
-  if (w != 0) return;
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      if (mt < nmt) acc[m][mt] = ((acc[m][mt] + red[0][m][mt][lane]) + red[1][m][mt][lane]) + red[2][m][mt][lane];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt >= nmt) break;
@@ -266,47 +301,66 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
 }
 
 // ------------------------------------------------------------------ tiled (large-M) kernels
-// Block tile 128 rows x 128 weight rows x 64 K, 4 waves as 2 x 2, each wave
-// 64 rows x 64 weight rows as 4 x 4 MFMA 16x16x32 tiles.  Gate/up: weight rows
-// 0..63 are gate rows n0..n0+63, rows 64..127 the up rows of the same
-// channels, and each wave holds the gate and up tiles of the same 32 channels
-// so the SwiGLU epilogue stays in registers.
-constexpr int PBM = 128, PBN = 128, PBK = 64, PLD = PBK + 8;
-
-template <typename TW> struct PLoad;
-template <> struct PLoad<bf16> {
-  u32x4 v[4];
+// Block: 128 rows of one item x 256 weight rows, four waves.  The gathered
+// activation tile goes through double-buffered LDS (every wave needs all 128
+// rows); each wave owns 64 weight rows (four 16-row MFMA fragments) that no
+// other wave reads, so they travel from global memory straight into MFMA
+// operand registers, prefetched one K step ahead.  Per K step a wave issues
+// 8 x 4 MFMA 16x16x32 per 32-wide K slice against 8 LDS fragment reads, half
+// the LDS traffic per MFMA of a 64 x 64 wave tile.
+// Gate/up: wave w's fragments are gate rows n0+32w .. +32 and the up rows of
+// the same channels, so the SwiGLU epilogue stays in registers.
+// Lane K order inside a step: bf16 (64-wide steps) k = kb + 32 s + 8 g + i;
+// INT4 (128-wide steps, one scale group) k = kb + 32 g + 8 s + i, so a lane's
+// 16-byte weight load covers 32 nibbles of one group.
+template <typename TW> struct Til;
+template <> struct Til<bf16> {
+  static constexpr int KSTEP = 64, SUB = 2, BL = 2;   // BL: 16-byte weight loads per fragment per step
 };
-template <> struct PLoad<INT4> {
-  u32x4 v;
-  float s;
+template <> struct Til<INT4> {
+  static constexpr int KSTEP = 128, SUB = 4, BL = 1;
 };
+constexpr int TBM = 128;
 
 template <typename TW, bool GATEUP>
-__global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
-  __shared__ bf16 As[2][PBM * PLD];
-  __shared__ bf16 Bs[2][PBN * PLD];
+__global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void ffn_tiled_kernel(FfnArgs a) {
+  using TT = Til<TW>;
+  constexpr int KSTEP = TT::KSTEP, SUB = TT::SUB, BL = TT::BL;
+  constexpr bool I4 = std::is_same<TW, INT4>::value;
+  constexpr int LDA = KSTEP + 8;          // padded LDS row (bf16 elements)
+  constexpr int CPR = KSTEP / 8;          // 16-byte chunks per A row per step
+  constexpr int CPT = TBM * CPR / 256;    // A chunks per thread per step
+  constexpr int RPT = 256 / CPR;          // row stride between a thread's chunks
+  constexpr int NT = GATEUP ? 128 : 256;  // output channels per block (F, S*FS multiples of 128)
+  __shared__ bf16 As[2][TBM * LDA];
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6, g = lane >> 4, c = lane & 15;
-  const int wm = w >> 1, wn = w & 1;
-  constexpr int NT = GATEUP ? 64 : 128;  // output channels per block
   const int Nr = GATEUP ? a.F : a.d;
   const int Ns = GATEUP ? a.S * a.FS : a.d;
-  const int nbr = Nr / NT, nbs = Ns / NT;
-  const int routed_blocks = a.items_max * nbr;
-  int bid = blockIdx.x, e = 0, row0, mrows, nb;
-  const bool shared = bid >= routed_blocks;
+  const int nbr = (Nr + NT - 1) / NT, nbs = (Ns + NT - 1) / NT;
+  // Tile list: routed items (expert-major, so one expert's tiles are adjacent)
+  // times N blocks, then the shared-expert tiles.  Blocks are dispatched
+  // round-robin over the 8 XCDs, so XCD x = blockIdx % 8 takes the x-th of 8
+  // contiguous, equal chunks of the list: the tiles of an expert then run
+  // together on one XCD and share their weight and activation K slabs in its L2.
+  const int routed_tiles = *a.n_items * nbr;
+  const int total = routed_tiles + (a.S > 0 ? a.sh_items * nbs : 0);
+  const int xcd = blockIdx.x & 7;
+  const int lo = (int)((int64_t)total * xcd / 8), hi = (int)((int64_t)total * (xcd + 1) / 8);
+  const int tile = lo + (int)(blockIdx.x >> 3);
+  if (tile >= hi) return;
+  int e = 0, row0, mrows, nb;
+  const bool shared = tile >= routed_tiles;
   if (!shared) {
-    const int slot = bid / nbr;
-    nb = bid - slot * nbr;
-    if (slot >= *a.n_items) return;
+    const int slot = tile / nbr;
+    nb = tile - slot * nbr;
     const int4 it = a.items[slot];
     e = it.x;
     row0 = it.y;
     mrows = it.z;
   } else {
-    bid -= routed_blocks;
-    const int slot = bid / nbs;
-    nb = bid - slot * nbs;
+    const int sb = tile - routed_tiles;
+    const int slot = sb / nbs;
+    nb = sb - slot * nbs;
     row0 = slot * a.bm;
     mrows = min(a.bm, a.T - row0);
   }
@@ -314,146 +368,157 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
   const int Kfull = GATEUP ? a.d : (shared ? a.S * a.FS : a.F);
   const int Kseg = GATEUP ? a.d : (shared ? a.FS : a.F);
 
-  // A sources: rows (tid >> 3) + 32 i, 16-byte chunk (tid & 7)
-  const int ch = tid & 7;
-  const bf16* asrc[4];
+  // activation chunk sources: rows (tid / CPR) + RPT q, 16-byte chunk tid % CPR
+  const int ch = tid % CPR;
+  const bf16* asrc[CPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = min((tid >> 3) + 32 * i, mrows - 1);
+  for (int q = 0; q < CPT; ++q) {
+    const int r = min(tid / CPR + RPT * q, mrows - 1);
     if (GATEUP) {
       int tok = shared ? row0 + r : a.row_token[row0 + r];
       tok = min(max(tok, 0), a.T - 1);
-      asrc[i] = (const bf16*)a.x + (size_t)tok * a.d + ch * 8;
+      asrc[q] = (const bf16*)a.x + (size_t)tok * a.d + ch * 8;
     } else {
-      asrc[i] = (const bf16*)(shared ? a.hsh : a.h) + (size_t)(row0 + r) * Kfull + ch * 8;
+      asrc[q] = (const bf16*)(shared ? a.hsh : a.h) + (size_t)(row0 + r) * Kfull + ch * 8;
     }
   }
-  // B source row for weight-tile row rb, K offset k0 (returns element / byte pointer)
-  auto brow_ptr = [&](int rb, int k0, const void** sptr) -> const void* {
-    const void* mat;
+  // weight fragment f of this wave: per-lane pointer to its row at K = 0 (slab 0);
+  // each K step adds a block-uniform offset (K position, and the slab of the
+  // shared down projection, whose K runs over S slabs [S][d][FS])
+  const char* bptr[4];
+  const uint16_t* sptr[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    int row;
+    const void* m;
     const void* sc;
-    int n;
-    int kk = k0;
     if (GATEUP) {
-      const bool up = rb >= 64;
-      n = n0 + (rb & 63);
-      mat = shared ? (up ? a.shu : a.shg) : expert_mat<TW>(up ? a.wu : a.wg, e, a.F, a.d);
+      const bool up = f >= 2;
+      row = n0 + 32 * w + 16 * (f & 1) + c;
+      m = shared ? (up ? a.shu : a.shg) : expert_mat<TW>(up ? a.wu : a.wg, e, a.F, a.d);
       sc = shared ? (up ? a.shsu : a.shsg) : expert_scales(up ? a.su : a.sg, e, a.F, a.d);
     } else {
-      n = n0 + rb;
-      const int slab = shared ? k0 / Kseg : 0;
-      kk = k0 - slab * Kseg;
-      mat = shared ? expert_mat<TW>(a.shd, slab, a.d, Kseg) : expert_mat<TW>(a.wd, e, a.d, Kseg);
-      sc = shared ? expert_scales(a.shsd, slab, a.d, Kseg) : expert_scales(a.sd, e, a.d, Kseg);
+      row = min(n0 + 64 * w + 16 * f + c, a.d - 1);  // a last block may be half past d
+      m = shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, Kseg);
+      sc = shared ? a.shsd : expert_scales(a.sd, e, a.d, Kseg);
     }
-    if constexpr (std::is_same<TW, INT4>::value) {
-      *sptr = (const uint16_t*)sc + (size_t)n * (Kseg / kInt4Group) + kk / kInt4Group;
-      return (const uint8_t*)mat + (size_t)n * (Kseg / 2) + kk / 2;
+    if constexpr (I4) {
+      bptr[f] = (const char*)m + (size_t)row * (Kseg / 2) + 16 * g;
+      sptr[f] = (const uint16_t*)sc + (size_t)row * (Kseg / kInt4Group);
     } else {
-      *sptr = nullptr;
-      return (const bf16*)mat + (size_t)n * Kseg + kk;
+      bptr[f] = (const char*)m + ((size_t)row * Kseg + 8 * g) * sizeof(bf16);
+      sptr[f] = nullptr;
+    }
+  }
+  // byte offset of K step kt inside a weight row (plus the slab stride), and scale index
+  auto woff = [&](int kt, int* soff) -> size_t {
+    const int k0 = kt * KSTEP;
+    const int slab = (!GATEUP && shared) ? k0 / Kseg : 0;
+    const int kk = k0 - slab * Kseg;
+    const size_t slab_elems = (size_t)slab * a.d * Kseg;
+    if constexpr (I4) {
+      *soff = (int)(slab_elems / kInt4Group) + kk / kInt4Group;
+      return (slab_elems + kk) / 2;
+    } else {
+      *soff = 0;
+      return (slab_elems + kk) * sizeof(bf16);
     }
   };
 
-  PLoad<TW> pl;
-  u32x4 ar[4];
-  auto gload = [&](int kt) {
-    const int k0 = kt * PBK;
+  f32x4 acc[8][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ar[i] = ld16(asrc[i] + k0);
-    if constexpr (std::is_same<TW, INT4>::value) {
-      const void* sp;
-      const uint8_t* p = (const uint8_t*)brow_ptr(tid >> 1, k0, &sp);
-      pl.v = ld16(p + 16 * (tid & 1));
-      pl.s = bf16_bits_to_f32(*(const uint16_t*)sp);
-    } else {
+  for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const void* sp;
-        const bf16* p = (const bf16*)brow_ptr((tid >> 3) + 32 * i, k0, &sp);
-        pl.v[i] = ld16(p + ch * 8);
+    for (int f = 0; f < 4; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 ar[CPT];
+  u32x4 bcur[4][BL], bnext[4][BL];
+  float scur[4], snext[4];
+  const int nkt = Kfull / KSTEP;
+
+  auto load_a = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) ar[q] = ld16(asrc[q] + kt * KSTEP);
+  };
+  auto store_a = [&](bf16* dst) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q)
+      *reinterpret_cast<u32x4*>(&dst[(tid / CPR + RPT * q) * LDA + ch * 8]) = ar[q];
+  };
+  auto load_b = [&](u32x4 (&bq)[4][BL], float (&bs)[4], int kt) {
+    int so;
+    const size_t o = woff(kt, &so);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if constexpr (I4) {
+        bq[f][0] = ld16(bptr[f] + o);
+        bs[f] = bf16_bits_to_f32(sptr[f][so]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < BL; ++s) bq[f][s] = ld16(bptr[f] + o + 64 * s);
+        bs[f] = 1.f;
       }
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&As[buf][((tid >> 3) + 32 * i) * PLD + ch * 8]) = ar[i];
-    if constexpr (std::is_same<TW, INT4>::value) {
-      const int rb = tid >> 1, half = tid & 1;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 d8 = int4x8_to_bf16(pl.v[q]);
-        // apply the group scale and round once to bf16
-        u32x4 o;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float lo = bf16_bits_to_f32(d8[p] & 0xFFFFu) * pl.s;
-          const float hi = bf16_bits_to_f32(d8[p] >> 16) * pl.s;
-          o[p] = pack_bf16x2(lo, hi);
-        }
-        *reinterpret_cast<u32x4*>(&Bs[buf][rb * PLD + 32 * half + 8 * q]) = o;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(&Bs[buf][((tid >> 3) + 32 * i) * PLD + ch * 8]) = pl.v[i];
-    }
-  };
 
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int brow[4];
-#pragma unroll
-  for (int nf = 0; nf < 4; ++nf)
-    brow[nf] = GATEUP ? (nf < 2 ? 32 * wn + 16 * nf : 64 + 32 * wn + 16 * (nf - 2)) : 64 * wn + 16 * nf;
-
-  const int nkt = Kfull / PBK;
-  gload(0);
-  lstore(0);
+  load_a(0);
+  load_b(bcur, scur, 0);
+  store_a(As[0]);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      u32x4 af[4], bfr[4];
-#pragma unroll
-      for (int mf = 0; mf < 4; ++mf)
-        af[mf] = *reinterpret_cast<const u32x4*>(&As[buf][(64 * wm + 16 * mf + c) * PLD + sub * 32 + 8 * g]);
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf)
-        bfr[nf] = *reinterpret_cast<const u32x4*>(&Bs[buf][(brow[nf] + c) * PLD + sub * 32 + 8 * g]);
-#pragma unroll
-      for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mma_bf16(af[mf], bfr[nf], acc[mf][nf]);
+    const bf16* A = As[kt & 1];
+    const bool more = kt + 1 < nkt;
+    if (more) {
+      load_a(kt + 1);
+      load_b(bnext, snext, kt + 1);
     }
-    if (kt + 1 < nkt) lstore(buf ^ 1);
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      u32x4 bf[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if constexpr (I4) bf[f] = int4x8_to_bf16_scaled(bcur[f][0][s], scur[f]);
+        else bf[f] = bcur[f][s];
+      }
+      const int col = I4 ? (32 * g + 8 * s) : (32 * s + 8 * g);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(&A[(16 * m + c) * LDA + col]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[m][f] = mma_bf16(af, bf[f], acc[m][f]);
+      }
+    }
+    if (more) store_a(As[(kt + 1) & 1]);
     __syncthreads();
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+#pragma unroll
+      for (int s = 0; s < BL; ++s) bcur[f][s] = bnext[f][s];
+      scur[f] = snext[f];
+    }
   }
 
 #pragma unroll
-  for (int mf = 0; mf < 4; ++mf) {
+  for (int m = 0; m < 8; ++m) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 64 * wm + 16 * mf + 4 * g + i;
+      const int r = 16 * m + 4 * g + i;
       if (r >= mrows) continue;
       if (GATEUP) {
         bf16* hout = (bf16*)(shared ? a.hsh : a.h);
         const int ld = shared ? Ns : Nr;
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf) {
-          const float hv = silu(acc[mf][nf][i]) * acc[mf][nf + 2][i];
-          hout[(size_t)(row0 + r) * ld + n0 + 32 * wn + 16 * nf + c] = (bf16)hv;
+        for (int f = 0; f < 2; ++f) {
+          const float hv = silu(acc[m][f][i]) * acc[m][f + 2][i];
+          hout[(size_t)(row0 + r) * ld + n0 + 32 * w + 16 * f + c] = (bf16)hv;
         }
       } else {
         bf16* yout = (bf16*)(shared ? a.ysh : a.y);
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) yout[(size_t)(row0 + r) * a.d + n0 + 64 * wn + 16 * nf + c] = (bf16)acc[mf][nf][i];
+        for (int f = 0; f < 4; ++f) {
+          const int col = n0 + 64 * w + 16 * f + c;
+          if (col < a.d) yout[(size_t)(row0 + r) * a.d + col] = (bf16)acc[m][f][i];
+        }
       }
     }
   }
@@ -510,19 +575,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const TA* __restrict__ y, 
 static int ffn_grid(const FfnArgs& a, int nt_routed, int nt_shared) {
   return a.items_max * nt_routed + (a.S > 0 ? a.sh_items * nt_shared : 0);
 }
+// tiled kernels: one block per tile slot, rounded up to whole rounds of the 8 XCDs
+static int ffn_grid_xcd(const FfnArgs& a, int nt_routed, int nt_shared) {
+  return (ffn_grid(a, nt_routed, nt_shared) + 7) / 8 * 8;
+}
+
+template <bool GATEUP, int MT>
+static void launch_stream(int wdt, const FfnArgs& a, int grid, hipStream_t s) {
+  if (wdt == kF32)
+    hipLaunchKernelGGL((ffn_stream_kernel<float, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+  else if (wdt == kBF16)
+    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_stream_kernel<INT4, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+}
+
+template <bool GATEUP>
+static void launch_stream_mt(int wdt, const FfnArgs& a, int grid, hipStream_t s) {
+  if (a.bm <= 16)
+    launch_stream<GATEUP, 1>(wdt, a, grid, s);
+  else if (a.bm <= 32)
+    launch_stream<GATEUP, 2>(wdt, a, grid, s);
+  else
+    launch_stream<GATEUP, 4>(wdt, a, grid, s);
+}
 
 hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s) {
   if (mode == 0) {
     const int grid = ffn_grid(a, a.F / 16, a.S * a.FS / 16);
     if (grid == 0) return hipSuccess;
-    if (wdt == kF32)
-      hipLaunchKernelGGL((ffn_stream_kernel<float, true>), dim3(grid), dim3(256), 0, s, a);
-    else if (wdt == kBF16)
-      hipLaunchKernelGGL((ffn_stream_kernel<bf16, true>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((ffn_stream_kernel<INT4, true>), dim3(grid), dim3(256), 0, s, a);
+    launch_stream_mt<true>(wdt, a, grid, s);
   } else {
-    const int grid = ffn_grid(a, a.F / 64, a.S * a.FS / 64);
+    const int grid = ffn_grid_xcd(a, a.F / 128, a.S * a.FS / 128);
     if (grid == 0) return hipSuccess;
     if (wdt == kBF16)
       hipLaunchKernelGGL((ffn_tiled_kernel<bf16, true>), dim3(grid), dim3(256), 0, s, a);
@@ -535,16 +619,11 @@ hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipSt
 
 hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s) {
   if (mode == 0) {
-    const int grid = ffn_grid(a, a.d / 16, a.d / 16);
+    const int grid = ffn_grid(a, a.d / 64, a.d / 64);
     if (grid == 0) return hipSuccess;
-    if (wdt == kF32)
-      hipLaunchKernelGGL((ffn_stream_kernel<float, false>), dim3(grid), dim3(256), 0, s, a);
-    else if (wdt == kBF16)
-      hipLaunchKernelGGL((ffn_stream_kernel<bf16, false>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((ffn_stream_kernel<INT4, false>), dim3(grid), dim3(256), 0, s, a);
+    launch_stream_mt<false>(wdt, a, grid, s);
   } else {
-    const int grid = ffn_grid(a, a.d / 128, a.d / 128);
+    const int grid = ffn_grid_xcd(a, (a.d + 255) / 256, (a.d + 255) / 256);
     if (grid == 0) return hipSuccess;
     if (wdt == kBF16)
       hipLaunchKernelGGL((ffn_tiled_kernel<bf16, false>), dim3(grid), dim3(256), 0, s, a);

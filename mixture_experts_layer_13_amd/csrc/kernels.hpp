@@ -9,7 +9,6 @@ namespace moe {
 enum { kF32 = 0, kBF16 = 1, kINT4 = 2 };
 enum { kScoreSoftmax = 0, kScoreSigmoid = 1 };
 
-constexpr int kRouteTile = 64;          // tokens per router / permute block (large T)
 constexpr int kSingleMaxPairs = 8192;   // T*k handled by the single-block route+permute
 constexpr int kDecodeRows = 64;         // rows per item in the streaming (small-M) expert kernels
 constexpr int kPrefillRows = 128;       // rows per item in the tiled (large-M) expert kernels
@@ -37,6 +36,7 @@ struct PermArgs {
   int4* items;               // tile map {expert, first row, rows, 0} (null: not built)
   int32_t* n_items;
   int bm;                    // rows per tile-map item
+  int rt;                    // tokens per router tile / tile-histogram row (large T)
 };
 
 struct FfnArgs {
@@ -61,9 +61,9 @@ hipError_t launch_router_partial(int act, const void* x, const void* wr, int T, 
                                  float* part, hipStream_t s);
 hipError_t launch_route_permute_single(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
                                        const PermArgs& pa, int do_route, int do_perm, hipStream_t s);
-hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int32_t* hist,
+hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int rt, int32_t* hist,
                                hipStream_t s);
-hipError_t launch_tile_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, hipStream_t s);
+hipError_t launch_tile_hist(const int32_t* idx, int T, int k, int E, int rt, int32_t* hist, hipStream_t s);
 hipError_t launch_permute_multi(const int32_t* idx, const int32_t* hist, const PermArgs& pa, hipStream_t s);
 hipError_t launch_tile_map(const int32_t* offsets, int E, int R, int bm, int4* items, int32_t* n_items,
                            hipStream_t s);

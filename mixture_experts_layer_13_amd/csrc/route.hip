@@ -66,7 +66,7 @@ __device__ __forceinline__ void topk_token(const float (&score)[4], const float 
         s = score[j];
       }
     }
-    s = __shfl(s, owner);
+    s = readlane_f32(s, owner);
     gsum += s;
     if (lane == r) {
       sel_e = e;
@@ -319,57 +319,80 @@ __global__ __launch_bounds__(1024) void route_permute_single_kernel(const float*
 }
 
 // ------------------------------------------------------------------ fused router (large T)
-// One block per 64-token tile computes all E logits with MFMA, scores and
-// selects each token (a wave per token) and writes the tile's expert histogram.
-template <typename TIN>
+// One block per tile of 16 * MT tokens computes all E logits with MFMA: the
+// four waves split K into quarters and their partial sums are added in LDS in
+// fixed wave order.  Then each token is scored and selected (a wave per token)
+// and the block writes the tile's expert histogram.  NB = experts / 16 held
+// per wave (compile-time bound, E <= 16 * NB).
+template <typename TIN, int MT, int NB>
 __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict__ x, const TIN* __restrict__ wr,
                                                            RouteArgs ra, int32_t* __restrict__ hist) {
   constexpr int EPC = Chunk<TIN>::EPC;
   constexpr int KSTEP = 4 * EPC;
-  constexpr int LD = 256 + 4;
-  __shared__ float slog[kRouteTile * LD];
-  __shared__ uint16_t sel[kRouteTile * kMaxK];
+  constexpr int TM = 16 * MT;
+  constexpr int LD = 16 * NB + 4;
+  constexpr int U = 2;
+  __shared__ float slog[TM * LD];
+  __shared__ uint16_t sel[TM * kMaxK];
   __shared__ int wcnt[4 * 256];
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / 64, g = lane >> 4;
+  __shared__ int base[256];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / 64, g = lane >> 4, c = lane & 15;
   const int T = ra.T, E = ra.E, d = ra.d, k = ra.k;
-  const int t0 = blockIdx.x * kRouteTile;
+  const int t0 = blockIdx.x * TM;
   const int nblk = (E + 15) / 16;
-  // wave w owns expert blocks w, w+4, w+8, w+12
-  f32x4 acc[4][4];
+  f32x4 acc[MT][NB];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const TIN* pa[4];
-  const TIN* pb[4];
+    for (int b = 0; b < NB; ++b) acc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const TIN* pa[MT];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) pa[m] = x + (size_t)min(t0 + 16 * m + (lane & 15), T - 1) * d + g * EPC;
+  for (int m = 0; m < MT; ++m) pa[m] = x + (size_t)min(t0 + 16 * m + c, T - 1) * d + g * EPC;
+  const TIN* pb = wr + (size_t)min(c, E - 1) * d + g * EPC;   // expert block b adds 16 * b rows
+  const int nsteps = d / KSTEP;
+  const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
+  for (int st = s0; st < s1; st += U) {
+    u32x4 av[U][MT], bv[U][NB];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) pb[b] = wr + (size_t)min(16 * (w + 4 * b) + (lane & 15), E - 1) * d + g * EPC;
-  for (int kk = 0; kk < d; kk += KSTEP) {
-    u32x4 av[4], bv[4];
+    for (int u = 0; u < U; ++u) {
+      if (st + u < s1) {
+        const int kk = (st + u) * KSTEP;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) av[m] = ld16(pa[m] + kk);
+        for (int m = 0; m < MT; ++m) av[u][m] = ld16(pa[m] + kk);
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (w + 4 * b < nblk) bv[b] = ld16(pb[b] + kk);
+        for (int b = 0; b < NB; ++b) {
+          const int row = min(16 * b + c, E - 1) - min(c, E - 1);
+          if (b < nblk) bv[u][b] = ld16(pb + (size_t)row * d + kk);
+        }
+      }
+    }
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (w + 4 * b < nblk)
+    for (int u = 0; u < U; ++u)
+      if (st + u < s1)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m][b] = Chunk<TIN>::mma(av[m], bv[b], acc[m][b]);
+        for (int b = 0; b < NB; ++b)
+          if (b < nblk)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m][b] = Chunk<TIN>::mma(av[u][m], bv[u][b], acc[m][b]);
   }
+  // sum the four K quarters in wave order
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    if (w + 4 * b >= nblk) continue;
-    const int e = 16 * (w + 4 * b) + (lane & 15);
+      for (int b = 0; b < NB; ++b) {
+        if (b >= nblk) continue;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) slog[(16 * m + 4 * g + i) * LD + e] = acc[m][b][i];
+          for (int i = 0; i < 4; ++i) {
+            float* p = &slog[(16 * m + 4 * g + i) * LD + 16 * b + c];
+            *p = ww == 0 ? acc[m][b][i] : *p + acc[m][b][i];
+          }
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  const int nt = min(kRouteTile, T - t0);
+  const int nt = min(TM, T - t0);
   for (int tt = w; tt < nt; tt += 4) {
     float logit[4], score[4], keyv[4];
 #pragma unroll
@@ -386,27 +409,26 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict
     write_scores(ra, t0 + tt, score);
     topk_token(score, keyv, E, k, ra.renorm, ra.gate_scale, t0 + tt, ra.idx, ra.gates, sel + tt * k);
   }
+  // tile histogram over the tile's pairs (sel[] is complete only after this barrier)
   __syncthreads();
-  // tile histogram over the tile's pairs (at most 64 * 8 = 512: two passes of 256)
-  int* base = reinterpret_cast<int*>(slog);  // reuse: 256 ints
-  for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;
-  __syncthreads();
+  for (int xx = tid; xx < 256; xx += blockDim.x) base[xx] = 0;
   const int np = nt * k;
   for (int p0 = 0; p0 < np; p0 += blockDim.x) {
     const int i = p0 + tid;
     const int e = i < np ? (int)sel[i] : 0xFFFF;
     rank_pass(e, e < E, wcnt, base, E);
   }
-  for (int x = tid; x < E; x += blockDim.x) hist[(size_t)blockIdx.x * E + x] = base[x];
+  __syncthreads();
+  for (int xx = tid; xx < E; xx += blockDim.x) hist[(size_t)blockIdx.x * E + xx] = base[xx];
 }
 
 // Tile histogram of given indices (for the standalone permute on large T).
-__global__ __launch_bounds__(512) void tile_hist_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
+__global__ __launch_bounds__(512) void tile_hist_kernel(const int32_t* __restrict__ idx, int T, int k, int E, int rt,
                                                         int32_t* __restrict__ hist) {
   __shared__ int wcnt[8 * 256];
   __shared__ int base[256];
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kRouteTile, nt = min(kRouteTile, T - t0), np = nt * k;
+  const int t0 = blockIdx.x * rt, nt = min(rt, T - t0), np = nt * k;
   for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;
   __syncthreads();
   for (int p0 = 0; p0 < np; p0 += blockDim.x) {
@@ -418,6 +440,7 @@ __global__ __launch_bounds__(512) void tile_hist_kernel(const int32_t* __restric
     }
     rank_pass(e, e < E, wcnt, base, E);
   }
+  __syncthreads();
   for (int x = tid; x < E; x += blockDim.x) hist[(size_t)blockIdx.x * E + x] = base[x];
 }
 
@@ -470,7 +493,7 @@ __global__ __launch_bounds__(512) void permute_multi_kernel(const int32_t* __res
     for (int x = tid; x <= E; x += blockDim.x) pa.offsets[x] = off[x];
     if (pa.items) write_tile_map(kept, off, E, pa.bm, pa.items, pa.n_items, tmp);
   }
-  const int t0 = tile * kRouteTile, nt = min(kRouteTile, T - t0), np = nt * k;
+  const int t0 = tile * pa.rt, nt = min(pa.rt, T - t0), np = nt * k;
   for (int p0 = 0; p0 < np; p0 += blockDim.x) {
     const int i = p0 + tid;
     int e = 0xFFFF;
@@ -526,23 +549,36 @@ hipError_t launch_route_permute_single(const float* part, int KS, const RouteArg
   return hipGetLastError();
 }
 
-hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int32_t* hist,
+hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int rt, int32_t* hist,
                                hipStream_t s) {
-  dim3 grid((ra.T + kRouteTile - 1) / kRouteTile);
-  if (act == kF32)
-    hipLaunchKernelGGL(router_fused_kernel<float>, grid, dim3(256), 0, s, (const float*)x, (const float*)wr, ra, hist);
-  else
-    hipLaunchKernelGGL(router_fused_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra, hist);
+  dim3 grid((ra.T + rt - 1) / rt);
+  const int nb = (ra.E + 15) / 16;
+  if (act == kF32) {
+    hipLaunchKernelGGL((router_fused_kernel<float, 1, 16>), grid, dim3(256), 0, s, (const float*)x, (const float*)wr,
+                       ra, hist);
+  } else if (rt == 32) {
+    hipLaunchKernelGGL((router_fused_kernel<bf16, 2, 16>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
+                       hist);
+  } else if (nb <= 4) {
+    hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 4>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
+                       hist);
+  } else if (nb <= 8) {
+    hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 8>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
+                       hist);
+  } else {
+    hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 16>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
+                       hist);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_tile_hist(const int32_t* idx, int T, int k, int E, int32_t* hist, hipStream_t s) {
-  hipLaunchKernelGGL(tile_hist_kernel, dim3((T + kRouteTile - 1) / kRouteTile), dim3(512), 0, s, idx, T, k, E, hist);
+hipError_t launch_tile_hist(const int32_t* idx, int T, int k, int E, int rt, int32_t* hist, hipStream_t s) {
+  hipLaunchKernelGGL(tile_hist_kernel, dim3((T + rt - 1) / rt), dim3(512), 0, s, idx, T, k, E, rt, hist);
   return hipGetLastError();
 }
 
 hipError_t launch_permute_multi(const int32_t* idx, const int32_t* hist, const PermArgs& pa, hipStream_t s) {
-  const int n_tiles = (pa.T + kRouteTile - 1) / kRouteTile;
+  const int n_tiles = (pa.T + pa.rt - 1) / pa.rt;
   hipLaunchKernelGGL(permute_multi_kernel, dim3(n_tiles), dim3(512), 0, s, idx, hist, n_tiles, pa);
   return hipGetLastError();
 }

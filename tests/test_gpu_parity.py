@@ -135,3 +135,32 @@ def test_forward_is_deterministic():
         for u, v in zip(a, b):
             assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
                                v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
+
+
+def test_graph_replay_matches_eager():
+    """moe_forward captured in a HIP graph replays to the eager result, bit for bit,
+    on every replay, with eager work on the buffers in between."""
+    sp, lay, ml = get_layer("olmoe")
+    for T in (8, 300, 4096):
+        x = S.make_tokens(sp, T, device="cuda")
+        ref = [t.clone() for t in ml.forward(x)]
+        outs = [torch.empty_like(t) for t in ref]
+        ml.workspace(ml.cfg_for(T))
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            ml.forward(x, *outs)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            ml.forward(x, *outs)
+        for rep in range(3):
+            for t in outs:
+                t.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for u, v in zip(ref, outs):
+                assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                                   v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), (T, rep)
+        del g
