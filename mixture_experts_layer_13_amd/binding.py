@@ -14,7 +14,8 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe.so")
+# MOE_LIBRARY may point at another build of the same library (e.g. an instrumented one)
+LIB_PATH = os.environ.get("MOE_LIBRARY", os.path.join(HERE, "libmoe.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_INT4_G128 = 0, 1, 2

@@ -105,6 +105,65 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)), max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
+// The same reductions for N independent values at once (N tokens per wave):
+// the N dependency chains interleave, hiding each other's latency.
+template <int N> __device__ __forceinline__ void wave_max_n(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<kDppSwap1>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<kDppSwap2>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<kDppHalfMirror>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<kDppMirror>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = fmaxf(fmaxf(readlane_f32(v[i], 0), readlane_f32(v[i], 16)),
+                 fmaxf(readlane_f32(v[i], 32), readlane_f32(v[i], 48)));
+}
+template <int N> __device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<kDppSwap1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<kDppSwap2>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<kDppHalfMirror>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<kDppMirror>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = (readlane_f32(v[i], 0) + readlane_f32(v[i], 16)) + (readlane_f32(v[i], 32) + readlane_f32(v[i], 48));
+}
+template <int N> __device__ __forceinline__ void wave_max_u64_n(uint64_t (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = max_u64(v[i], dpp_u64<kDppSwap1>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = max_u64(v[i], dpp_u64<kDppSwap2>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = max_u64(v[i], dpp_u64<kDppHalfMirror>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = max_u64(v[i], dpp_u64<kDppMirror>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = max_u64(max_u64(readlane_u64(v[i], 0), readlane_u64(v[i], 16)),
+                   max_u64(readlane_u64(v[i], 32), readlane_u64(v[i], 48)));
+}
+
+template <int N> __device__ __forceinline__ void wave_max_u32_n(uint32_t (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = max(v[i], dpp_u32<kDppSwap1>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = max(v[i], dpp_u32<kDppSwap2>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = max(v[i], dpp_u32<kDppHalfMirror>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = max(v[i], dpp_u32<kDppMirror>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = max(max((uint32_t)__builtin_amdgcn_readlane((int)v[i], 0), (uint32_t)__builtin_amdgcn_readlane((int)v[i], 16)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)v[i], 32), (uint32_t)__builtin_amdgcn_readlane((int)v[i], 48)));
+}
+
 // Monotone map float -> uint32 (total order; -0 is canonicalised to +0 first).
 __device__ __forceinline__ uint32_t float_order_key(float f) {
   uint32_t b = __float_as_uint(f + 0.0f);

@@ -223,6 +223,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
     const int aoff = seg * K;
     const int nsteps = K / KSTEP;
     const int s0 = kpart * nsteps / KSPLIT, s1 = (kpart + 1) * nsteps / KSPLIT;
+#pragma unroll 1  // U-deep unroll inside already; a further unroll only costs occupancy
     for (int st = s0; st < s1; st += U) {
       u32x4 bq[NM][U];
       float sc[NM][U];

@@ -33,93 +33,181 @@ template <> struct Chunk<float> {
   }
 };
 
-// Top-k for one token, executed by one full wave.  key/score hold experts
-// e = lane + 64 * j.  Writes idx/gates of token t (and the k selected experts
-// to sel_tok when it is not null).
-__device__ __forceinline__ void topk_token(const float (&score)[4], const float (&keyv)[4], int E, int k,
-                                           int renorm, float gate_scale, int t, int32_t* idx_out,
-                                           float* gate_out, uint16_t* sel_tok) {
+// Routes NT tokens at once with one full wave (their reductions interleave).
+// logit[i][j] holds expert e = lane + 64 j (j < EPL, E <= 64 EPL) of token
+// t0 + i.  Scores: softmax (max-subtract-expsum, fp32) or sigmoid; selection
+// key: the score, plus the selection-only bias for sigmoid scoring.  Top-k:
+// k rounds; each takes the wave-wide maximum of the fp32 keys in a monotone
+// 32-bit encoding, then, among the entries holding that maximum, the lowest
+// expert index (ballots over the lanes' best entries), so equal keys select
+// the lower index and slots come out in descending key order.  Gates: the
+// selected unbiased scores (renormalised over the k picks when asked), times
+// gate_scale.  Tokens i >= nvalid are computed but not written.
+template <int NT, int EPL>
+__device__ __forceinline__ void route_tokens(float (&logit)[NT][EPL], const RouteArgs& a, int t0, int nvalid,
+                                             uint16_t* sel) {
   const int lane = lane_id();
-  uint64_t key[4];
+  const int E = a.E, k = a.k;
+  float score[NT][EPL];
+  uint32_t key[NT][EPL];
+  if (a.score == kScoreSoftmax) {
+    float m[NT], sum[NT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    // (order key of the float, then inverted index so that ties pick the lower index);
-    // 0 marks an absent or already selected entry and is below every real entry.
-    key[j] = e < E ? ((uint64_t)float_order_key(keyv[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
-  }
-  float gsum = 0.f;
-  int sel_e = 0;
-  float sel_s = 0.f;
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = key[0];
+    for (int i = 0; i < NT; ++i) {
+      m[i] = -INFINITY;
 #pragma unroll
-    for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    const int owner = e & 63, jj = e >> 6;
-    float s = 0.f;
+      for (int j = 0; j < EPL; ++j)
+        if (lane + 64 * j < E) m[i] = fmaxf(m[i], logit[i][j]);
+    }
+    wave_max_n<NT>(m);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j == jj && lane == owner) {
-        key[j] = 0ull;
-        s = score[j];
+    for (int i = 0; i < NT; ++i) {
+      sum[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        score[i][j] = (lane + 64 * j < E) ? expf(logit[i][j] - m[i]) : 0.f;
+        sum[i] += score[i][j];
       }
     }
-    s = readlane_f32(s, owner);
-    gsum += s;
-    if (lane == r) {
-      sel_e = e;
-      sel_s = s;
+    wave_sum_n<NT>(sum);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        score[i][j] = score[i][j] / sum[i];
+        key[i][j] = float_order_key(score[i][j]);
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      const float b = (a.select_bias && e < E) ? a.select_bias[e] : 0.f;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        score[i][j] = 1.0f / (1.0f + expf(-logit[i][j]));
+        key[i][j] = float_order_key(score[i][j] + b);
+      }
+    }
+  }
+  if (a.scores) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      if (i < nvalid)
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (lane + 64 * j < E) a.scores[(size_t)(t0 + i) * E + lane + 64 * j] = score[i][j];
+  }
+  // 0 marks an absent or already selected entry: every finite or infinite key encodes above 0
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (lane + 64 * j >= E)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) key[i][j] = 0u;
+  float gsum[NT], sel_s[NT];
+  int sel_e[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    gsum[i] = 0.f;
+    sel_s[i] = 0.f;
+    sel_e[i] = 0;
+  }
+  for (int r = 0; r < k; ++r) {
+    uint32_t best[NT], lbest[NT];
+    int lj[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {  // the lane's best entry (lowest j among equals)
+      lbest[i] = key[i][0];
+      lj[i] = 0;
+#pragma unroll
+      for (int j = 1; j < EPL; ++j)
+        if (key[i][j] > lbest[i]) {
+          lbest[i] = key[i][j];
+          lj[i] = j;
+        }
+      best[i] = lbest[i];
+    }
+    wave_max_u32_n<NT>(best);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      // lowest expert index holding the maximum: smallest j first, then the lowest lane
+      int e = 0;
+#pragma unroll
+      for (int j = EPL - 1; j >= 0; --j) {
+        const uint64_t b = __ballot(lbest[i] == best[i] && lj[i] == j);
+        if (b) e = __ffsll((unsigned long long)b) - 1 + 64 * j;
+      }
+      const int owner = e & 63, jj = e >> 6;
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        if (j == jj && lane == owner) {
+          key[i][j] = 0u;
+          s = score[i][j];
+        }
+      }
+      s = readlane_f32(s, owner);
+      gsum[i] += s;
+      if (lane == r) {
+        sel_e[i] = e;
+        sel_s[i] = s;
+      }
     }
   }
   if (lane < k) {
-    float g = renorm ? sel_s / gsum : sel_s;
-    g *= gate_scale;
-    idx_out[(size_t)t * k + lane] = sel_e;
-    gate_out[(size_t)t * k + lane] = g;
-    if (sel_tok) sel_tok[lane] = (uint16_t)sel_e;
-  }
-}
-
-// Scores and selection keys from fp32 logits (one wave, one token).
-__device__ __forceinline__ void score_token(float (&logit)[4], const RouteArgs& a, float (&score)[4],
-                                            float (&keyv)[4]) {
-  const int lane = lane_id();
-  if (a.score == kScoreSoftmax) {
-    float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j < a.E) m = fmaxf(m, logit[j]);
-    m = wave_max(m);
-    float ex[4], s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ex[j] = (lane + 64 * j < a.E) ? expf(logit[j] - m) : 0.f;
-      s += ex[j];
-    }
-    s = wave_sum(s);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      score[j] = ex[j] / s;
-      keyv[j] = score[j];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      score[j] = 1.0f / (1.0f + expf(-logit[j]));
-      keyv[j] = score[j] + ((a.select_bias && e < a.E) ? a.select_bias[e] : 0.f);
+    for (int i = 0; i < NT; ++i) {
+      if (i >= nvalid) break;
+      float gt = a.renorm ? sel_s[i] / gsum[i] : sel_s[i];
+      gt *= a.gate_scale;
+      a.idx[(size_t)(t0 + i) * k + lane] = sel_e[i];
+      a.gates[(size_t)(t0 + i) * k + lane] = gt;
+      if (sel) sel[i * k + lane] = (uint16_t)sel_e[i];
     }
   }
 }
 
-__device__ __forceinline__ void write_scores(const RouteArgs& a, int t, const float (&score)[4]) {
-  if (!a.scores) return;
+// Loads the logits of NT tokens (rows of `src`, row stride ld) for route_tokens.
+template <int NT, int EPL>
+__device__ __forceinline__ void load_logits(float (&logit)[NT][EPL], const float* src, int ld, int E,
+                                            const float* bias) {
   const int lane = lane_id();
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (lane + 64 * j < a.E) a.scores[(size_t)t * a.E + lane + 64 * j] = score[j];
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    const float b = (e < E && bias) ? bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) logit[i][j] = e < E ? src[i * ld + e] + b : 0.f;
+  }
+}
+
+// Routes tokens [0, nt) whose logits sit in LDS rows (wave w takes groups of 4).
+template <int EPL>
+__device__ void route_rows(const float* slog, int ld, int nt, int t0, const RouteArgs& ra, const float* bias,
+                           uint16_t* sel, int w, int nw) {
+  const int k = ra.k;
+  for (int t4 = 4 * w; t4 < nt; t4 += 4 * nw) {
+    if (nt - t4 >= 4) {
+      float logit[4][EPL];
+      load_logits<4, EPL>(logit, slog + t4 * ld, ld, ra.E, bias);
+      route_tokens<4, EPL>(logit, ra, t0 + t4, 4, sel + t4 * k);
+    } else {
+      for (int i = t4; i < nt; ++i) {
+        float logit[1][EPL];
+        load_logits<1, EPL>(logit, slog + i * ld, ld, ra.E, bias);
+        route_tokens<1, EPL>(logit, ra, t0 + i, 1, sel + i * k);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void route_rows_any(const float* slog, int ld, int nt, int t0, const RouteArgs& ra,
+                                               const float* bias, uint16_t* sel, int w, int nw) {
+  if (ra.E <= 64)
+    route_rows<1>(slog, ld, nt, t0, ra, bias, sel, w, nw);
+  else if (ra.E <= 128)
+    route_rows<2>(slog, ld, nt, t0, ra, bias, sel, w, nw);
+  else
+    route_rows<4>(slog, ld, nt, t0, ra, bias, sel, w, nw);
 }
 
 // Exclusive scan of n <= 256 ints in LDS by one wave; returns the total.
@@ -256,27 +344,47 @@ __device__ __forceinline__ void place_pair(const PermArgs& p, int i, int e, bool
 __global__ __launch_bounds__(1024) void route_permute_single_kernel(const float* __restrict__ part, int KS,
                                                                     RouteArgs ra, const int32_t* idx_in,
                                                                     PermArgs pa, int do_route, int do_perm) {
+  constexpr int kLog = 16384;  // logits staged in LDS per token group
+  __shared__ float slog[kLog];
   __shared__ uint16_t sel[kSingleMaxPairs];
   __shared__ int wcnt[16 * 256];
   __shared__ int base[256], kept[256], off[257], tmp[512];
   const int tid = threadIdx.x, lane = lane_id(), w = tid / 64;
   const int T = ra.T, E = ra.E, k = ra.k, n = T * k;
   if (do_route) {
-    for (int t = w; t < T; t += 16) {
-      float logit[4], score[4], keyv[4];
+    const int G = kLog / E;  // tokens per group (E <= 256 -> G >= 64)
+    for (int tg = 0; tg < T; tg += G) {
+      const int nt = min(G, T - tg);
+      // logits (before the skew bias) = sum of the K-chunk partials in chunk
+      // order; each thread issues the loads of up to 4 elements x 8 chunks at once
+      const size_t zs = (size_t)T * E;
+      for (int i0 = tid; i0 < nt * E; i0 += 4 * blockDim.x) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int z0 = 0; z0 < KS; z0 += 8) {
+          float v[4][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        float s = 0.f;
-        if (e < E) {
-          for (int z = 0; z < KS; ++z) s += part[((size_t)z * T + t) * E + e];
-          if (ra.logit_bias) s += ra.logit_bias[e];
+          for (int q = 0; q < 4; ++q) {
+            const int i = i0 + q * blockDim.x;
+            const int t = tg + i / E, e = i - (i / E) * E;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              v[q][u] = (i < nt * E && z0 + u < KS) ? part[(size_t)(z0 + u) * zs + (size_t)t * E + e] : 0.f;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (z0 + u < KS) acc[q] += v[q][u];
         }
-        logit[j] = s;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = i0 + q * blockDim.x;
+          if (i < nt * E) slog[i] = acc[q];
+        }
       }
-      score_token(logit, ra, score, keyv);
-      write_scores(ra, t, score);
-      topk_token(score, keyv, E, k, ra.renorm, ra.gate_scale, t, ra.idx, ra.gates, sel + t * k);
+      __syncthreads();
+      route_rows_any(slog, E, nt, tg, ra, ra.logit_bias, sel + tg * k, w, 16);
+      __syncthreads();
     }
   } else if (do_perm) {
     for (int i = tid; i < n; i += blockDim.x) {
@@ -286,6 +394,7 @@ __global__ __launch_bounds__(1024) void route_permute_single_kernel(const float*
   }
   if (!do_perm) return;
   __syncthreads();
+  (void)lane;
   // phase A: per-expert counts
   for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;
   __syncthreads();
@@ -393,22 +502,7 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict
     __syncthreads();
   }
   const int nt = min(TM, T - t0);
-  for (int tt = w; tt < nt; tt += 4) {
-    float logit[4], score[4], keyv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      float s = 0.f;
-      if (e < E) {
-        s = slog[tt * LD + e];
-        if (ra.logit_bias) s += ra.logit_bias[e];
-      }
-      logit[j] = s;
-    }
-    score_token(logit, ra, score, keyv);
-    write_scores(ra, t0 + tt, score);
-    topk_token(score, keyv, E, k, ra.renorm, ra.gate_scale, t0 + tt, ra.idx, ra.gates, sel + tt * k);
-  }
+  route_rows<(16 * NB + 63) / 64>(slog, LD, nt, t0, ra, ra.logit_bias, sel, w, 4);
   // tile histogram over the tile's pairs (sel[] is complete only after this barrier)
   __syncthreads();
   for (int xx = tid; xx < 256; xx += blockDim.x) base[xx] = 0;
