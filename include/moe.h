@@ -28,6 +28,8 @@
  *  - Errors are returned before any launch (negative moe_status); nothing is
  *    thrown.  A launch failure returns MOE_ERR_HIP.  moe_last_error() gives a
  *    thread-local description of the last failure.
+ *  - T == 0 (for a valid cfg) returns MOE_OK at once: nothing is launched and
+ *    no buffer is touched.
  *  - Drops are data, not errors (drop_mask).
  *  - Weight layout: every matrix is stored one K-contiguous row per output
  *    channel: w_gate, w_up [E][ffn][d], w_down [E][d][ffn]; shared experts

@@ -303,8 +303,8 @@ moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, co
   Plan p;
   moe_status st;
   if ((st = make_plan(cfg, &p))) return st;
-  if ((st = check_ws(p, ws, ws_bytes))) return st;
   if (p.T == 0) return MOE_OK;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
   if (!x || !w_router || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "NULL x, w_router, topk_idx or topk_w");
   if (!al16(x) || !al16(w_router)) return fail(MOE_ERR_INVALID_ARG, "x and w_router must be 16-byte aligned");
   if (!al4(topk_idx) || !al4(topk_w) || (scores && !al4(scores)) || (logit_bias && !al4(logit_bias)) ||
@@ -320,6 +320,7 @@ moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* cou
   Plan p;
   moe_status st;
   if ((st = make_plan(cfg, &p))) return st;
+  if (p.T == 0) return MOE_OK;
   if ((st = check_ws(p, ws, ws_bytes))) return st;
   if (!topk_idx || !counts || !offsets || !row_token || !slot_row || !drop_mask)
     return fail(MOE_ERR_INVALID_ARG, "NULL permutation argument");
@@ -342,13 +343,13 @@ moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offs
   Plan p;
   moe_status st;
   if ((st = make_plan(cfg, &p))) return st;
+  if (p.T == 0) return MOE_OK;
   if ((st = check_ws(p, ws, ws_bytes))) return st;
   if ((st = check_experts(p, w))) return st;
   if (!x || !offsets || !row_token || !y_rows) return fail(MOE_ERR_INVALID_ARG, "NULL x, offsets, row_token or y_rows");
   if ((p.S > 0) != (y_shared != nullptr)) return fail(MOE_ERR_INVALID_ARG, "y_shared must be given iff n_shared > 0");
   if (!al16(x) || !al16(y_rows) || (y_shared && !al16(y_shared)))
     return fail(MOE_ERR_INVALID_ARG, "x, y_rows and y_shared must be 16-byte aligned");
-  if (p.T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   if ((st = hip_ok(launch_tile_map(offsets, p.E, (int)p.R, p.bm, at<int4>(ws, p.o_items), at<int32_t>(ws, p.o_nitems), s),
                    "tile map")))
@@ -363,11 +364,11 @@ moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* sl
   Plan p;
   moe_status st;
   if ((st = make_plan(cfg, &p))) return st;
+  if (p.T == 0) return MOE_OK;
   if (!y_rows || !slot_row || !topk_w || !out) return fail(MOE_ERR_INVALID_ARG, "NULL combine argument");
   if ((p.S > 0) != (y_shared != nullptr)) return fail(MOE_ERR_INVALID_ARG, "y_shared must be given iff n_shared > 0");
   if (!al16(y_rows) || !al16(out) || (y_shared && !al16(y_shared)))
     return fail(MOE_ERR_INVALID_ARG, "y_rows, y_shared and out must be 16-byte aligned");
-  if (p.T == 0) return MOE_OK;
   return hip_ok(launch_combine(p.act, y_rows, slot_row, topk_w, y_shared, out, p.T, p.d, p.k, (int)p.R,
                                (hipStream_t)stream),
                 "combine");
@@ -379,6 +380,7 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   Plan p;
   moe_status st;
   if ((st = make_plan(cfg, &p))) return st;
+  if (p.T == 0) return MOE_OK;
   if ((st = check_ws(p, ws, ws_bytes))) return st;
   if ((st = check_experts(p, w))) return st;
   if (!x || !w_router || !out || !topk_idx || !topk_w || !drop_mask)
@@ -386,7 +388,6 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   if (!al16(x) || !al16(w_router) || !al16(out)) return fail(MOE_ERR_INVALID_ARG, "x, w_router and out must be 16-byte aligned");
   if (!al4(topk_idx) || !al4(topk_w) || (logit_bias && !al4(logit_bias)) || (select_bias && !al4(select_bias)))
     return fail(MOE_ERR_INVALID_ARG, "index / fp32 arrays must be 4-byte aligned");
-  if (p.T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   int32_t* slot = at<int32_t>(ws, p.o_slot);
   int32_t* rowtok = at<int32_t>(ws, p.o_rowtok);

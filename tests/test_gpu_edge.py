@@ -1,0 +1,215 @@
+"""GPU edge cases and degenerate layers: empty and ragged token counts across
+every mode boundary, the dense and soft-mixture limits, exact ties, a capacity
+that drops everything, extreme routing skew, invalid indices handed to the
+permutation, caller-built row maps, gate sums, and the INT4 routing-drift
+report.  Every comparison is against the FP64 oracle or a closed form."""
+import numpy as np
+import pytest
+import torch
+from scipy import special
+
+import moe_synth as S
+import oracle as O
+from gpu_harness import compare_routes, layer_of, oracle_run, row_rel_err, to_f64, tol_of
+
+pytestmark = pytest.mark.gpu
+
+# a mid-size layer keeps the oracle fast while crossing every tile boundary
+MID = S.SPECS["olmoe"].replace(name="mid", cfg_id=11, d=1024, E=32, k=4, ffn=512)
+
+
+def run_and_check(sp, lay, ml, x, nsamp=None, tol=None):
+    T = x.shape[0]
+    out, idx, gates, drop = ml.forward(x)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if nsamp is None or T <= nsamp else \
+        np.sort(np.random.default_rng(1).choice(T, nsamp, replace=False))
+    ref = oracle_run(sp, lay, x, ffn_rows=rows)
+    gi = idx.cpu().numpy()
+    rep = compare_routes(gi, ref, sp.k)
+    assert rep.set_mismatch_strict == 0 and rep.order_mismatch == 0
+    ok = rows[rep.matched[rows]]
+    rel = row_rel_err(out.float().cpu().numpy().astype(np.float64)[ok], ref["out"][ok])
+    assert rel.max(initial=0) <= (tol or tol_of(sp)), rel.max()
+    return out, idx, gates, drop, ref
+
+
+@pytest.fixture(scope="module")
+def mid():
+    lay = S.make_layer(MID, device="cuda")
+    return MID, lay, layer_of(MID, lay)
+
+
+def test_zero_tokens_is_a_noop(mid):
+    sp, lay, ml = mid
+    x = torch.empty((0, sp.d), dtype=torch.bfloat16, device="cuda")
+    out, idx, gates, drop = ml.forward(x)
+    torch.cuda.synchronize()
+    assert out.shape == (0, sp.d) and idx.shape == (0, sp.k)
+
+
+@pytest.mark.parametrize("T", [1, 3, 17, 33, 63, 64, 65, 100, 255, 256, 257, 300, 1000])
+def test_ragged_token_counts(mid, T):
+    """Crosses the small/large routing boundary (256), the streaming/tiled GEMM
+    boundary (64), the 16/32/64-row streaming items and partial 128-row tiles."""
+    sp, lay, ml = mid
+    x = S.make_tokens(sp, T, device="cuda", seed=T)
+    run_and_check(sp, lay, ml, x, nsamp=300)
+
+
+def test_dense_limit_matches_textbook_swiglu():
+    """E = 1, k = 1: the gate is softmax of one logit = 1, so the layer is a dense
+    SwiGLU FFN.  Checked against the formula written out with scipy's expit."""
+    sp = MID.replace(name="dense", cfg_id=12, E=1, k=1)
+    lay = S.make_layer(sp, device="cuda")
+    ml = layer_of(sp, lay)
+    for T in (5, 300):
+        x = S.make_tokens(sp, T, device="cuda")
+        out, idx, gates, _ = ml.forward(x)
+        torch.cuda.synchronize()
+        assert (idx.cpu() == 0).all() and torch.equal(gates.cpu(), torch.ones_like(gates.cpu()))
+        xf = to_f64(x)
+        wg, wu, wd = to_f64(lay.w_gate[0]), to_f64(lay.w_up[0]), to_f64(lay.w_down[0])
+        a = xf @ wg.T
+        ref = (a * special.expit(a) * (xf @ wu.T)) @ wd.T
+        assert row_rel_err(to_f64(out), ref).max() <= 2e-2
+
+
+def test_k_equals_E_soft_mixture():
+    sp = MID.replace(name="soft", cfg_id=13, E=8, k=8)
+    lay = S.make_layer(sp, device="cuda")
+    ml = layer_of(sp, lay)
+    for T in (40, 400):
+        x = S.make_tokens(sp, T, device="cuda")
+        out, idx, gates, _, ref = run_and_check(sp, lay, ml, x)
+        # every token uses every expert; gates are the full softmax, summing to 1
+        assert (np.sort(idx.cpu().numpy(), 1) == np.arange(8)).all()
+        assert np.abs(gates.cpu().numpy().sum(1) - 1).max() <= 1e-5
+
+
+def test_zero_router_gives_lowest_indices_on_gpu():
+    """All logits equal (W_r = 0, no bias): exact ties everywhere, so every token
+    selects experts 0..k-1 with softmax gates 1/E (sigmoid: 2.5/k after renorm)."""
+    for sp, T in ((MID.replace(name="ties", cfg_id=14, logit_bias_std=0.0), 300),
+                  (S.SPECS["dsv3"].replace(name="ties3", cfg_id=15, d=512, E=64, ffn=256, select_bias_std=0.0), 40)):
+        lay = S.make_layer(sp, device="cuda")
+        lay.w_router.zero_()
+        ml = layer_of(sp, lay)
+        x = S.make_tokens(sp, T, device="cuda")
+        _, idx, gates, _ = ml.forward(x)
+        torch.cuda.synchronize()
+        assert (idx.cpu().numpy() == np.arange(sp.k)[None, :]).all()
+        expect = 1.0 / sp.E if sp.score == "softmax" else sp.gate_scale / sp.k
+        assert np.abs(gates.cpu().numpy() - expect).max() <= 1e-6
+
+
+def test_capacity_zero_leaves_shared_experts():
+    """C = 0 drops every routed pair; the output is the shared experts' FFN."""
+    sp = S.SPECS["dsv2_lite"].replace(name="capzero", cfg_id=16, d=512, E=16, ffn=256, ffn_shared=256,
+                                      capacity=(0, 1))
+    lay = S.make_layer(sp, device="cuda")
+    ml = layer_of(sp, lay)
+    x = S.make_tokens(sp, 200, device="cuda")
+    out, idx, gates, drop, ref = run_and_check(sp, lay, ml, x)
+    assert drop.cpu().numpy().all()
+    assert ref["drop"].all()
+
+
+def test_extreme_skew_single_hot_set():
+    """Every token identical: every token picks the same k experts, so k experts
+    each get all T rows (many tiles per expert) and the rest get none."""
+    sp = MID
+    lay = S.make_layer(sp, device="cuda")
+    ml = layer_of(sp, lay)
+    x1 = S.make_tokens(sp, 1, device="cuda")
+    for T in (64, 700):
+        x = x1.repeat(T, 1).contiguous()
+        out, idx, *_ = run_and_check(sp, lay, ml, x, nsamp=20)
+        assert (idx.cpu() == idx[0].cpu()).all()
+        assert (out.float() == out[0:1].float()).all()
+
+
+@pytest.mark.parametrize("T", [40, 600])
+def test_permute_treats_invalid_indices_as_dropped(mid, T):
+    sp, lay, ml = mid
+    r = np.random.default_rng(T)
+    idx = np.stack([r.choice(sp.E, sp.k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[3, 1] = -1
+    idx[5, 0] = sp.E
+    idx[7, 2] = 1 << 20
+    counts, offsets, row_token, slot_row, drop = ml.permute(torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    valid = (idx >= 0) & (idx < sp.E)
+    assert np.array_equal(drop.cpu().numpy(), (~valid).astype(np.uint8))
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(idx[valid], minlength=sp.E))
+    sr, rt, off = slot_row.cpu().numpy(), row_token.cpu().numpy(), offsets.cpu().numpy()
+    assert (sr[~valid] == -1).all() and off[-1] == valid.sum()
+    for t in range(T):
+        for j in range(sp.k):
+            if valid[t, j]:
+                e = idx[t, j]
+                assert off[e] <= sr[t, j] < off[e + 1] and rt[sr[t, j]] == t
+    # rows of an expert are ascending in t (stable token-major ranking)
+    for e in range(sp.E):
+        seg = rt[off[e]:off[e + 1]]
+        assert (np.diff(seg) > 0).all()
+
+
+def test_expert_ffn_on_caller_row_map(mid):
+    """moe_expert_ffn on a row map built on the host (not by moe_permute): each
+    row equals the oracle's FFN of its token through its expert."""
+    sp, lay, ml = mid
+    T = 90
+    x = S.make_tokens(sp, T, device="cuda")
+    r = np.random.default_rng(5)
+    idx = np.stack([r.choice(sp.E, sp.k, replace=False) for _ in range(T)]).astype(np.int32)
+    a = O.assign_rows(idx, sp.E)
+    offsets = torch.tensor(a["offsets"], dtype=torch.int32, device="cuda")
+    row_token = torch.tensor(a["row_token"], dtype=torch.int32, device="cuda")
+    y_rows, _ = ml.expert_ffn(x, offsets, row_token)
+    torch.cuda.synchronize()
+    xf = to_f64(x)
+    y = to_f64(y_rows)
+    for e in (0, 7, 31):
+        rows = np.arange(a["offsets"][e], a["offsets"][e + 1])
+        if rows.size == 0:
+            continue
+        wg, wu, wd = to_f64(lay.w_gate[e]), to_f64(lay.w_up[e]), to_f64(lay.w_down[e])
+        ref = O.swiglu_ffn(xf[a["row_token"][rows]], wg, wu, wd)
+        assert row_rel_err(y[rows], ref).max() <= 2e-2
+
+
+def test_gate_sums_on_gpu():
+    for name, T, target in (("dsv3", 16, 2.5), ("qwen3_int4", 32, 1.0)):
+        sp = S.SPECS[name]
+        if name == "dsv3":
+            sp = sp.replace(name="dsv3s", cfg_id=17, d=1024, ffn=256, E=256)
+        lay = S.make_layer(sp, device="cuda")
+        ml = layer_of(sp, lay)
+        x = S.make_tokens(sp, T, device="cuda")
+        _, _, gates, _ = ml.forward(x)
+        torch.cuda.synchronize()
+        assert np.abs(gates.cpu().numpy().sum(1) - target).max() <= 1e-5 * target
+
+
+def test_int4_routing_drift_report():
+    """INT4 experts with a bf16 router: routing is the bf16-weight layer's routing,
+    so drift (mean swaps out of k) is 0 up to near-ties.  Also reports the INT4
+    vs bf16-twin output difference as quality context (not a pass/fail bar)."""
+    sp = S.SPECS["qwen3_int4"]
+    lay = S.make_layer(sp, device="cuda")
+    ml = layer_of(sp, lay)
+    twin_sp = sp.replace(expert="bf16")
+    wg, wu, wd = S.make_bf16_twin(sp, device="cuda")
+    twin = S.Layer(twin_sp, lay.w_router, lay.logit_bias, lay.select_bias, wg, wu, wd)
+    mt = layer_of(twin_sp, twin)
+    for T in (32, 4096):
+        x = S.make_tokens(sp, T, device="cuda")
+        o4, i4, _, _ = ml.forward(x)
+        ob, ib, _, _ = mt.forward(x)
+        torch.cuda.synchronize()
+        swaps = O.swaps_per_token(i4.cpu().numpy(), ib.cpu().numpy())
+        rel = float((o4.float() - ob.float()).pow(2).mean().sqrt() / ob.float().pow(2).mean().sqrt())
+        print(f"\nqwen3 INT4 T={T}: routing drift {swaps.mean():.4f} swaps/token (of {sp.k}); "
+              f"INT4 vs bf16-twin output rel RMS {rel:.3f}")
+        assert swaps.mean() == 0.0
