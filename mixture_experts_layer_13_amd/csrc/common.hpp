@@ -37,6 +37,12 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// 16-byte load at a block-uniform base plus a per-lane unsigned 32-bit byte
+// offset (lets the compiler use the scalar-base addressing form)
+__device__ __forceinline__ u32x4 ld16_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + byte_off);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).

@@ -314,21 +314,27 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
 // Lane K order inside a step: bf16 (64-wide steps) k = kb + 32 s + 8 g + i;
 // INT4 (128-wide steps, one scale group) k = kb + 32 g + 8 s + i, so a lane's
 // 16-byte weight load covers 32 nibbles of one group.
-template <typename TW> struct Til;
-template <> struct Til<bf16> {
+// K step per weight type and projection (measured: the gate/up kernel, with
+// two weight matrices, runs best with 64-wide steps; the down kernel with
+// 32-wide steps, whose smaller register footprint avoids spills).
+template <typename TW, bool GATEUP> struct Til;
+template <> struct Til<bf16, true> {
   static constexpr int KSTEP = 64, SUB = 2, BL = 2;   // BL: 16-byte weight loads per fragment per step
 };
-template <> struct Til<INT4> {
+template <> struct Til<bf16, false> {
+  static constexpr int KSTEP = 32, SUB = 1, BL = 1;
+};
+template <bool G> struct Til<INT4, G> {
   static constexpr int KSTEP = 128, SUB = 4, BL = 1;
 };
 constexpr int TBM = 128;
 
 template <typename TW, bool GATEUP>
 __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void ffn_tiled_kernel(FfnArgs a) {
-  using TT = Til<TW>;
+  using TT = Til<TW, GATEUP>;
   constexpr int KSTEP = TT::KSTEP, SUB = TT::SUB, BL = TT::BL;
   constexpr bool I4 = std::is_same<TW, INT4>::value;
-  constexpr int LDA = KSTEP + 8;          // padded LDS row (bf16 elements)
+  constexpr int LDA = KSTEP + 16;         // padded LDS row (bf16 elements)
   constexpr int CPR = KSTEP / 8;          // 16-byte chunks per A row per step
   constexpr int CPT = TBM * CPR / 256;    // A chunks per thread per step
   constexpr int RPT = 256 / CPR;          // row stride between a thread's chunks
@@ -369,59 +375,60 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
   const int Kfull = GATEUP ? a.d : (shared ? a.S * a.FS : a.F);
   const int Kseg = GATEUP ? a.d : (shared ? a.FS : a.F);
 
-  // activation chunk sources: rows (tid / CPR) + RPT q, 16-byte chunk tid % CPR
+  // activation chunk sources: rows (tid / CPR) + RPT q, 16-byte chunk tid % CPR;
+  // 32-bit element offsets from one block-uniform base keep registers low
   const int ch = tid % CPR;
-  const bf16* asrc[CPT];
+  const bf16* abase = GATEUP ? (const bf16*)a.x : (const bf16*)(shared ? a.hsh : a.h);
+  uint32_t aoff[CPT];  // byte offsets
 #pragma unroll
   for (int q = 0; q < CPT; ++q) {
     const int r = min(tid / CPR + RPT * q, mrows - 1);
     if (GATEUP) {
       int tok = shared ? row0 + r : a.row_token[row0 + r];
       tok = min(max(tok, 0), a.T - 1);
-      asrc[q] = (const bf16*)a.x + (size_t)tok * a.d + ch * 8;
+      aoff[q] = ((uint32_t)tok * a.d + ch * 8) * 2u;
     } else {
-      asrc[q] = (const bf16*)(shared ? a.hsh : a.h) + (size_t)(row0 + r) * Kfull + ch * 8;
+      aoff[q] = ((uint32_t)(row0 + r) * Kfull + ch * 8) * 2u;
     }
   }
-  // weight fragment f of this wave: per-lane pointer to its row at K = 0 (slab 0);
-  // each K step adds a block-uniform offset (K position, and the slab of the
-  // shared down projection, whose K runs over S slabs [S][d][FS])
-  const char* bptr[4];
-  const uint16_t* sptr[4];
+  // weight fragment f of this wave: byte offset of its row (plus the lane's K
+  // group) inside one of two block-uniform matrices (gate / up, or down; the
+  // shared down projection adds a block-uniform slab offset per K step)
+  const char* bmat[2];
+  const uint16_t* smat[2];
+  uint32_t boff[4], soff[4];
+  if (GATEUP) {
+    bmat[0] = (const char*)(shared ? a.shg : expert_mat<TW>(a.wg, e, a.F, a.d));
+    bmat[1] = (const char*)(shared ? a.shu : expert_mat<TW>(a.wu, e, a.F, a.d));
+    smat[0] = (const uint16_t*)(shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d));
+    smat[1] = (const uint16_t*)(shared ? a.shsu : expert_scales(a.su, e, a.F, a.d));
+  } else {
+    bmat[0] = bmat[1] = (const char*)(shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, Kseg));
+    smat[0] = smat[1] = (const uint16_t*)(shared ? a.shsd : expert_scales(a.sd, e, a.d, Kseg));
+  }
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
-    int row;
-    const void* m;
-    const void* sc;
-    if (GATEUP) {
-      const bool up = f >= 2;
-      row = n0 + 32 * w + 16 * (f & 1) + c;
-      m = shared ? (up ? a.shu : a.shg) : expert_mat<TW>(up ? a.wu : a.wg, e, a.F, a.d);
-      sc = shared ? (up ? a.shsu : a.shsg) : expert_scales(up ? a.su : a.sg, e, a.F, a.d);
-    } else {
-      row = min(n0 + 64 * w + 16 * f + c, a.d - 1);  // a last block may be half past d
-      m = shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, Kseg);
-      sc = shared ? a.shsd : expert_scales(a.sd, e, a.d, Kseg);
-    }
+    const int row = GATEUP ? n0 + 32 * w + 16 * (f & 1) + c
+                           : min(n0 + 64 * w + 16 * f + c, a.d - 1);  // a last block may be half past d
     if constexpr (I4) {
-      bptr[f] = (const char*)m + (size_t)row * (Kseg / 2) + 16 * g;
-      sptr[f] = (const uint16_t*)sc + (size_t)row * (Kseg / kInt4Group);
+      boff[f] = (uint32_t)row * (Kseg / 2) + 16 * g;
+      soff[f] = (uint32_t)row * (Kseg / kInt4Group) * 2u;
     } else {
-      bptr[f] = (const char*)m + ((size_t)row * Kseg + 8 * g) * sizeof(bf16);
-      sptr[f] = nullptr;
+      boff[f] = ((uint32_t)row * Kseg + 8 * g) * 2u;
+      soff[f] = 0;
     }
   }
   // byte offset of K step kt inside a weight row (plus the slab stride), and scale index
-  auto woff = [&](int kt, int* soff) -> size_t {
+  auto woff = [&](int kt, int* so) -> size_t {
     const int k0 = kt * KSTEP;
     const int slab = (!GATEUP && shared) ? k0 / Kseg : 0;
     const int kk = k0 - slab * Kseg;
     const size_t slab_elems = (size_t)slab * a.d * Kseg;
     if constexpr (I4) {
-      *soff = (int)(slab_elems / kInt4Group) + kk / kInt4Group;
+      *so = (int)(slab_elems / kInt4Group) + kk / kInt4Group;
       return (slab_elems + kk) / 2;
     } else {
-      *soff = 0;
+      *so = 0;
       return (slab_elems + kk) * sizeof(bf16);
     }
   };
@@ -439,7 +446,7 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
 
   auto load_a = [&](int kt) {
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) ar[q] = ld16(asrc[q] + kt * KSTEP);
+    for (int q = 0; q < CPT; ++q) ar[q] = ld16_at(abase + kt * KSTEP, aoff[q]);
   };
   auto store_a = [&](bf16* dst) {
 #pragma unroll
@@ -451,53 +458,74 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
     const size_t o = woff(kt, &so);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
+      const char* m = bmat[GATEUP ? (f >> 1) : 0] + o;
       if constexpr (I4) {
-        bq[f][0] = ld16(bptr[f] + o);
-        bs[f] = bf16_bits_to_f32(sptr[f][so]);
+        bq[f][0] = ld16_at(m, boff[f]);
+        const char* sm = (const char*)(smat[GATEUP ? (f >> 1) : 0] + so);
+        bs[f] = bf16_bits_to_f32(*(const uint16_t*)(sm + soff[f]));
       } else {
 #pragma unroll
-        for (int s = 0; s < BL; ++s) bq[f][s] = ld16(bptr[f] + o + 64 * s);
+        for (int s = 0; s < BL; ++s) bq[f][s] = ld16_at(m + 64 * s, boff[f]);
         bs[f] = 1.f;
       }
     }
   };
 
-  load_a(0);
-  load_b(bcur, scur, 0);
-  store_a(As[0]);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const bf16* A = As[kt & 1];
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      load_a(kt + 1);
-      load_b(bnext, snext, kt + 1);
-    }
+  // one K step: SUB slices of 32; the activation fragment of the next m is
+  // read from LDS before the four MFMAs of the current one are issued
+  auto compute = [&](const bf16* A, const u32x4 (&bq)[4][BL], const float (&bs)[4]) {
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
       u32x4 bf[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        if constexpr (I4) bf[f] = int4x8_to_bf16_scaled(bcur[f][0][s], scur[f]);
-        else bf[f] = bcur[f][s];
+        if constexpr (I4) bf[f] = int4x8_to_bf16_scaled(bq[f][0][s], bs[f]);
+        else bf[f] = bq[f][s];
       }
       const int col = I4 ? (32 * g + 8 * s) : (32 * s + 8 * g);
+      u32x4 af = *reinterpret_cast<const u32x4*>(&A[c * LDA + col]);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(&A[(16 * m + c) * LDA + col]);
+        u32x4 an = af;
+        if (m + 1 < 8) an = *reinterpret_cast<const u32x4*>(&A[(16 * (m + 1) + c) * LDA + col]);
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[m][f] = mma_bf16(af, bf[f], acc[m][f]);
+        af = an;
       }
     }
-    if (more) store_a(As[(kt + 1) & 1]);
+  };
+
+  // two-step ping-pong without branches: step kt computes from (As[kt & 1],
+  // register set kt & 1) while step kt + 1 loads into the other pair; past the
+  // last step the prefetch repeats step nkt - 1 (harmless, never used)
+  u32x4 b1q[4][BL];
+  float s1q[4];
+  load_a(0);
+  load_b(bcur, scur, 0);
+  store_a(As[0]);
+  __syncthreads();
+  int kt = 0;
+  // the scheduling barriers keep the next step's loads ahead of this step's
+  // MFMAs (left alone, the scheduler sinks them next to their first use)
+  for (; kt + 2 <= nkt; kt += 2) {
+    load_a(min(kt + 1, nkt - 1));
+    load_b(b1q, s1q, min(kt + 1, nkt - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As[0], bcur, scur);
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(As[1]);
     __syncthreads();
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-#pragma unroll
-      for (int s = 0; s < BL; ++s) bcur[f][s] = bnext[f][s];
-      scur[f] = snext[f];
-    }
+    load_a(min(kt + 2, nkt - 1));
+    load_b(bcur, scur, min(kt + 2, nkt - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As[1], b1q, s1q);
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(As[0]);
+    __syncthreads();
   }
+  if (kt < nkt) compute(As[0], bcur, scur);
+  (void)bnext;
+  (void)snext;
 
 #pragma unroll
   for (int m = 0; m < 8; ++m) {

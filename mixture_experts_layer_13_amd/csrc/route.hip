@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict
   constexpr int KSTEP = 4 * EPC;
   constexpr int TM = 16 * MT;
   constexpr int LD = 16 * NB + 4;
-  constexpr int U = 2;
+  constexpr int U = 2;  // steps whose loads are issued together (deeper costs occupancy)
   __shared__ float slog[TM * LD];
   __shared__ uint16_t sel[TM * kMaxK];
   __shared__ int wcnt[4 * 256];
@@ -556,10 +556,19 @@ __global__ __launch_bounds__(512) void permute_multi_kernel(const int32_t* __res
     int sb = 0, st = 0;
     const int e = tid % E, part = tid / E;
     if (part < P) {
-      for (int r = part; r < n_tiles; r += P) {
-        const int v = hist[(size_t)r * E + e];
-        st += v;
-        if (r < tile) sb += v;
+      // 8 tile rows per batch: the loads are issued together
+      for (int r0 = part; r0 < n_tiles; r0 += 8 * P) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r = r0 + u * P;
+          v[u] = r < n_tiles ? hist[(size_t)r * E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          st += v[u];
+          if (r0 + u * P < tile) sb += v[u];
+        }
       }
     }
     red_b[tid] = sb;
