@@ -39,7 +39,22 @@ def parse():
     ap.add_argument("--T", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="run only the decode sweep and print it")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy three times (calibrates the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": a.numel() * 4, "copies": 3}))
 
 
 class HipEvents:
@@ -206,9 +221,15 @@ def main():
     from mixture_experts_layer_13_amd import binding as B
 
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe()
+        return
     sp = S.SPECS["olmoe"]
     T = args.T
     lay = S.make_layer(sp, device="cuda")
+    if args.decode_only:
+        print(json.dumps(decode_sweep(sp, lay)), flush=True)
+        return
     x = S.make_tokens(sp, T, device="cuda")
     ml = moe_layer(sp, lay)
     cfg = ml.cfg_for(T)
