@@ -51,10 +51,26 @@ def copy_probe():
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(3):
         b.copy_(a)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes": a.numel() * 4, "copies": 3}))
+    ms = e0.elapsed_time(e1) / 3
+    # reference points for HBM: read+write bandwidth of a plain copy, read bandwidth of a reduction
+    big = torch.ones(4 << 28, dtype=torch.float32, device="cuda")  # 4 GiB
+    big.sum()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        big.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_r = e0.elapsed_time(e1) / 3
+    print(json.dumps({"copy_probe_bytes": a.numel() * 4, "copies": 3, "ms_per_copy": round(ms, 3),
+                      "read_plus_write_GBps": round(2 * a.numel() * 4 / (ms * 1e-3) / 1e9, 1),
+                      "reduction_read_GBps": round(big.numel() * 4 / (ms_r * 1e-3) / 1e9, 1)}))
 
 
 class HipEvents:
