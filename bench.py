@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--T", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
+                    help="expert weight layout (tiled: repacked once before timing)")
     ap.add_argument("--decode-only", action="store_true", help="run only the decode sweep and print it")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device-to-device copy three times (calibrates the HBM byte counters)")
@@ -102,14 +104,20 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(h))
 
 
-def moe_layer(sp, lay):
+def moe_layer(sp, lay, layout):
+    """A MoeLayer over the generated weights; with layout "tiled" the expert
+    matrices are repacked once (moe_pack_weights), before any timing."""
     from mixture_experts_layer_13_amd import binding as B
     from mixture_experts_layer_13_amd.layer import MoeLayer
     cfg = B.make_cfg(1, sp.d, sp.E, sp.k, sp.ffn, sp.n_shared, sp.ffn_shared, act=sp.act, expert=sp.expert,
-                     score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale, capacity=sp.capacity)
-    return MoeLayer(cfg, lay.w_router, lay.w_gate, lay.w_up, lay.w_down, logit_bias=lay.logit_bias,
-                    select_bias=lay.select_bias, s_gate=lay.s_gate, s_up=lay.s_up, s_down=lay.s_down,
-                    sh_gate=lay.sh_gate, sh_up=lay.sh_up, sh_down=lay.sh_down)
+                     score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale, capacity=sp.capacity,
+                     layout=layout)
+    mats = [lay.w_gate, lay.w_up, lay.w_down, lay.sh_gate, lay.sh_up, lay.sh_down]
+    if layout == "tiled":
+        mats = [None if m is None else B.pack_tiled(m, sp.expert) for m in mats]
+    wg, wu, wd, shg, shu, shd = mats
+    return MoeLayer(cfg, lay.w_router, wg, wu, wd, logit_bias=lay.logit_bias, select_bias=lay.select_bias,
+                    s_gate=lay.s_gate, s_up=lay.s_up, s_down=lay.s_down, sh_gate=shg, sh_up=shu, sh_down=shd)
 
 
 def expert_bytes(sp):
@@ -172,19 +180,19 @@ def cpu_baseline(sp, lay, x, n_tokens):
                       f"all selected expert FFNs from bf16 bit patterns, combine); {dt:.1f} s"}
 
 
-def decode_sweep(sp, lay, Ts=(1, 8, 32, 64), replays=200, copies=4):
+def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4):
     """Decode-sized forwards as hipGraph replays over `copies` weight copies (cold in
     the 256 MB Infinity Cache), reported as achieved HBM bandwidth."""
     import torch
 
     import moe_synth as S
-    layers = [moe_layer(sp, lay)]
+    layers = [moe_layer(sp, lay, layout)]
     keep = []
     for c in range(1, copies):
         cp = S.Layer(sp, lay.w_router.clone(), lay.logit_bias, lay.select_bias, lay.w_gate.clone(),
                      lay.w_up.clone(), lay.w_down.clone())
         keep.append(cp)
-        layers.append(moe_layer(sp, cp))
+        layers.append(moe_layer(sp, cp, layout))
     res = {}
     s = torch.cuda.Stream()
     for T in Ts:
@@ -244,10 +252,10 @@ def main():
     T = args.T
     lay = S.make_layer(sp, device="cuda")
     if args.decode_only:
-        print(json.dumps(decode_sweep(sp, lay)), flush=True)
+        print(json.dumps(decode_sweep(sp, lay, args.layout)), flush=True)
         return
     x = S.make_tokens(sp, T, device="cuda")
-    ml = moe_layer(sp, lay)
+    ml = moe_layer(sp, lay, args.layout)
     cfg = ml.cfg_for(T)
     nl = B.forward_launches(cfg)
     outs = (torch.empty((T, sp.d), dtype=torch.bfloat16, device="cuda"),
@@ -298,7 +306,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"olmoe_1b7b_layer_T{T}", "T": T, "d": sp.d, "E": sp.E, "k": sp.k,
-                   "ffn": sp.ffn, "launches_per_layer": nl},
+                   "ffn": sp.ffn, "launches_per_layer": nl, "weight_layout": args.layout},
         "roofline": {"bound": "mfma", "kernel": "ffn_tiled_kernel<bf16,gate/up>", "achieved": round(achieved, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic, "avg_launch_us": round(per["gateup"] * 1e3, 2),
@@ -309,7 +317,7 @@ def main():
                   "wall_s_timed": round(wall, 3)},
     }
     if not args.no_decode:
-        line["decode"] = decode_sweep(sp, lay)
+        line["decode"] = decode_sweep(sp, lay, args.layout)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_tokens=256)
     print(json.dumps(line), flush=True)

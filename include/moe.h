@@ -31,12 +31,14 @@
  *  - T == 0 (for a valid cfg) returns MOE_OK at once: nothing is launched and
  *    no buffer is touched.
  *  - Drops are data, not errors (drop_mask).
- *  - Weight layout: every matrix is stored one K-contiguous row per output
- *    channel: w_gate, w_up [E][ffn][d], w_down [E][d][ffn]; shared experts
- *    [S][ffn_shared][d] and [S][d][ffn_shared].  INT4 experts: packed bytes
- *    [E][N][K/2] (byte i holds element 2i in its low nibble and 2i+1 in its
- *    high nibble, two's complement) plus bf16 scales [E][N][K/128]; the weight
- *    is q * s for the 128-element group along K.
+ *  - Weight layout (MOE_LAYOUT_ROWS): every matrix is stored one K-contiguous
+ *    row per output channel: w_gate, w_up [E][ffn][d], w_down [E][d][ffn];
+ *    shared experts [S][ffn_shared][d] and [S][d][ffn_shared].  INT4 experts:
+ *    packed bytes [E][N][K/2] (byte i holds element 2i in its low nibble and
+ *    2i+1 in its high nibble, two's complement) plus bf16 scales
+ *    [E][N][K/128]; the weight is q * s for the 128-element group along K.
+ *    MOE_LAYOUT_TILED holds the same bytes permuted by moe_pack_weights (the
+ *    INT4 scales and the router weight keep the row layout).
  *  - Calls on one stream run in order; two calls that share a workspace must
  *    not overlap.
  */
@@ -50,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -62,11 +64,13 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2 } moe_dtype;
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
 
 /* Layer shape and routing rule.  Supported: 0 <= T <= 1048576, 1 <= E <= 256,
  * 1 <= k <= min(E, 8), d, ffn, ffn_shared multiples of 128, 0 <= n_shared <= 8,
  * act_dtype MOE_F32 or MOE_BF16 (x, w_router, y_rows, y_shared, out),
- * expert_dtype equal to act_dtype, or MOE_INT4_G128 with act_dtype MOE_BF16. */
+ * expert_dtype equal to act_dtype, or MOE_INT4_G128 with act_dtype MOE_BF16,
+ * and every expert matrix (ffn x d, ffn_shared x d) under 2 GiB. */
 typedef struct moe_cfg {
   int32_t T;            /* tokens                                              */
   int32_t d;            /* hidden size                                         */
@@ -82,6 +86,7 @@ typedef struct moe_cfg {
   float gate_scale;     /* multiplies routed gates (1.0; 2.5 for DeepSeek-V3)  */
   int32_t cap_num;      /* capacity factor C = cap_num / cap_den;              */
   int32_t cap_den;      /*   0 / 0 = dropless; cap_num = 0 drops every pair    */
+  int32_t weight_layout; /* moe_layout of the routed and shared expert weights  */
 } moe_cfg;
 
 /* Expert weights (device pointers, layout above).  s_* are the INT4 scales
@@ -165,6 +170,21 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router,
                        const moe_experts* w, void* out, int32_t* topk_idx,
                        float* topk_w, uint8_t* drop_mask,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* Repacks weight rows from MOE_LAYOUT_ROWS into MOE_LAYOUT_TILED (out of
+ * place; a pure byte permutation, so results do not change, bit for bit).
+ * Not from the pages: an MI355X data-layout choice.  A 16-byte load per lane
+ * of the matrix cores' operand layout reads 16 rows x 64 bytes, four rows per
+ * group of four lanes; the tiled layout stores each 16-row x 64-byte fragment
+ * as one contiguous KB in that lane order, so one wave-wide load reads 1 KB of
+ * consecutive addresses.  Byte b of row n (R = bytes per row) moves to
+ *   ((n/16)*(R/64) + b/64)*1024 + ((b%64)/16)*256 + (n%16)*16 + b%16.
+ *   src, dst: device, 16-byte aligned, not overlapping, rows*R bytes each;
+ *   rows: a multiple of 16 (a stack [E][N][K] is E*N rows); K elements per row
+ *   of `dtype` (MOE_INT4_G128: K/2 packed bytes, K a multiple of 128), R a
+ *   multiple of 64.  Pack w_gate, w_up, w_down and the shared matrices once at
+ *   load time; scales are not packed.  Async on `stream`. */
+moe_status moe_pack_weights(int32_t dtype, const void* src, void* dst, int64_t rows, int32_t K, void* stream);
 
 /* Kernel launches moe_forward enqueues for this cfg (0 on an invalid cfg). */
 int32_t moe_forward_launches(const moe_cfg* cfg);

@@ -20,9 +20,11 @@ LIB_PATH = os.environ.get("MOE_LIBRARY", os.path.join(HERE, "libmoe.so"))
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_INT4_G128 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 
 _DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128}
 _SCORES = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
+_LAYOUTS = {"rows": MOE_LAYOUT_ROWS, "tiled": MOE_LAYOUT_TILED}
 
 
 class MoeError(RuntimeError):
@@ -36,7 +38,7 @@ class MoeCfg(ctypes.Structure):
                 ("ffn", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("ffn_shared", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("gate_scale", ctypes.c_float), ("cap_num", ctypes.c_int32),
-                ("cap_den", ctypes.c_int32)]
+                ("cap_den", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 class MoeExperts(ctypes.Structure):
@@ -63,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [C, P, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [C, P, P, P, P, ctypes.POINTER(MoeExperts), P, P, P, P, P,
                                        ctypes.c_size_t, P]),
+        "moe_pack_weights": (ctypes.c_int, [ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int32, P]),
         "moe_set_timing_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
@@ -80,10 +83,10 @@ lib = _load()
 # ---------------------------------------------------------------- config helpers
 def make_cfg(T: int, d: int, E: int, k: int, ffn: int, n_shared: int = 0, ffn_shared: int = 0,
              act: str = "bf16", expert: str = "bf16", score: str = "softmax", renorm: bool = False,
-             gate_scale: float = 1.0, capacity: Optional[tuple] = None) -> MoeCfg:
+             gate_scale: float = 1.0, capacity: Optional[tuple] = None, layout: str = "rows") -> MoeCfg:
     cn, cd = capacity if capacity is not None else (0, 0)
     return MoeCfg(T, d, E, k, ffn, n_shared, ffn_shared, _DTYPES[act], _DTYPES[expert], _SCORES[score],
-                  int(bool(renorm)), float(gate_scale), cn, cd)
+                  int(bool(renorm)), float(gate_scale), cn, cd, _LAYOUTS[layout])
 
 
 def cfg_with_T(cfg: MoeCfg, T: int) -> MoeCfg:
@@ -136,6 +139,22 @@ def experts(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, sh_gate=N
     """Pointer struct of the expert weights (the tensors must outlive its use)."""
     vals = [w_gate, w_up, w_down, s_gate, s_up, s_down, sh_gate, sh_up, sh_down, shs_gate, shs_up, shs_down]
     return MoeExperts(*[None if v is None else v.data_ptr() for v in vals])
+
+
+def moe_pack_weights(dtype: int, src: torch.Tensor, dst: torch.Tensor, rows: int, K: int, stream=None):
+    _check(lib.moe_pack_weights(dtype, _p(src), _p(dst), rows, K, _stream(stream)))
+
+
+def pack_tiled(w: torch.Tensor, expert: str = "bf16", K: Optional[int] = None, stream=None) -> torch.Tensor:
+    """A new tensor holding the weight rows of `w` (shape [..., N, Kstored]) in
+    the tiled layout.  K is the element count per row (INT4: twice the bytes)."""
+    dt = _DTYPES[expert]
+    Ks = w.shape[-1]
+    K = K if K is not None else (2 * Ks if dt == MOE_INT4_G128 else Ks)
+    rows = w.numel() // Ks
+    out = torch.empty_like(w)
+    moe_pack_weights(dt, w, out, rows, K, stream)
+    return out
 
 
 # ---------------------------------------------------------------- entry points

@@ -36,7 +36,7 @@ constexpr int kStreamMaxT = 64;    // T up to which the expert GEMMs use the str
 constexpr int64_t kMaxT = 1 << 20;
 
 struct Plan {
-  int T, d, E, k, F, S, FS, act, wdt, score, renorm;
+  int T, d, E, k, F, S, FS, act, wdt, score, renorm, tiled;
   float gscale;
   int64_t cap;  // -1: dropless
   int64_t R;
@@ -72,6 +72,15 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     return fail(MOE_ERR_INVALID_ARG, "score=%d is not a moe_score", c->score);
   if (c->renorm != 0 && c->renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm=%d is not 0 or 1", c->renorm);
   if (!isfinite(c->gate_scale)) return fail(MOE_ERR_INVALID_ARG, "gate_scale is not finite");
+  if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_TILED)
+    return fail(MOE_ERR_INVALID_ARG, "weight_layout=%d is not a moe_layout", c->weight_layout);
+  {
+    // every expert matrix must stay below 2 GiB (32-bit byte offsets inside one matrix)
+    const int64_t nmax = c->ffn > (c->n_shared ? c->ffn_shared : 0) ? c->ffn : c->ffn_shared;
+    const int64_t bytes = nmax * c->d * (c->expert_dtype == MOE_F32 ? 4 : 2);
+    if (bytes >= ((int64_t)1 << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "an expert matrix of %lld bytes exceeds 2 GiB", (long long)bytes);
+  }
   const bool dropless = c->cap_num == 0 && c->cap_den == 0;
   if (!dropless && (c->cap_den <= 0 || c->cap_num < 0))
     return fail(MOE_ERR_INVALID_ARG, "capacity %d/%d: need 0/0 or num >= 0, den > 0", c->cap_num, c->cap_den);
@@ -89,6 +98,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   q.score = c->score;
   q.renorm = c->renorm;
   q.gscale = c->gate_scale;
+  q.tiled = c->weight_layout == MOE_LAYOUT_TILED;
   const int64_t pairs = (int64_t)q.T * q.k;
   if (dropless) {
     q.cap = -1;
@@ -234,6 +244,7 @@ FfnArgs ffn_args(const Plan& p, void* ws, const void* x, const int32_t* row_toke
   a.items_max = (int)p.items_max;
   a.sh_items = p.sh_items;
   a.bm = p.bm;
+  a.wtiled = p.tiled;
   a.wg = w->w_gate;
   a.wu = w->w_up;
   a.wd = w->w_down;
@@ -419,6 +430,21 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   st = hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
   mark(5, nl, s);
   return st;
+}
+
+moe_status moe_pack_weights(int32_t dtype, const void* src, void* dst, int64_t rows, int32_t K, void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_INT4_G128)
+    return fail(MOE_ERR_INVALID_ARG, "dtype=%d is not a moe_dtype", dtype);
+  if (rows < 0 || rows % 16) return fail(MOE_ERR_INVALID_ARG, "rows=%lld is not a non-negative multiple of 16", (long long)rows);
+  const int64_t rb = dtype == MOE_INT4_G128 ? (int64_t)K / 2 : (int64_t)K * (dtype == MOE_F32 ? 4 : 2);
+  if (K <= 0 || (dtype == MOE_INT4_G128 && K % kInt4Group) || rb % 64)
+    return fail(MOE_ERR_INVALID_ARG, "K=%d: a row must be a positive multiple of 64 bytes (INT4: K multiple of 128)", K);
+  if (rows == 0) return MOE_OK;
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "NULL src or dst");
+  if (!al16(src) || !al16(dst)) return fail(MOE_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+  const uintptr_t a0 = (uintptr_t)src, b0 = (uintptr_t)dst, n = (uintptr_t)(rows * rb);
+  if (a0 < b0 + n && b0 < a0 + n) return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+  return hip_ok(launch_pack_tiled(src, dst, rows, rb, (hipStream_t)stream), "pack");
 }
 
 moe_status moe_set_timing_events(void* const* events, int32_t n_events) {

@@ -80,29 +80,44 @@ template <> struct Dec<INT4> {
   static constexpr int KSTEP = 128, AL = 4, U = 2;
 };
 
-// One weight row of a [N][K] matrix as seen by one lane (lane group g = lane/16).
-// Lane K order inside a step: bf16 k = kb + 8g + i; f32 k = kb + 4g + i;
-// INT4 k = kb + 32g + 8s + i (s = dword of the 16-byte load).
-template <typename TW> struct BRow;
-template <> struct BRow<float> {
-  const float* p;
-  __device__ BRow(const void* m, int n, int K, int g, const void*) : p((const float*)m + (size_t)n * K + 4 * g) {}
-  __device__ u32x4 load(int kb) const { return ld16(p + kb); }
-  __device__ float scale(int) const { return 1.f; }
+// Weight bytes of one output channel n (row n of an [N][K] matrix, Kb bytes
+// per row) as one lane sees them: the row is read in 64-byte chunks, the lane
+// taking bytes 16g..16g+15 of each (g = lane / 16; lane % 16 = n % 16).
+//  - row layout: chunk j of row n at n*Kb + 64j;
+//  - tiled layout: the 16-row x 64-byte fragment (n/16, j) is one contiguous
+//    KB at ((n/16)*(Kb/64) + j)*1024, lane-major: bytes 16*(16g + c).. hold
+//    row 16*(n/16) + c, bytes 16g.. of the chunk, so one wave-wide 16-byte load
+//    of a fragment reads 1 KB of consecutive addresses.
+struct WRow {
+  const uint8_t* p;  // chunk 0 of this lane
+  int shift;         // log2 of the bytes from chunk j to chunk j + 1
+  __device__ WRow(const void* m, int n, int Kb, int g, int tiled) {
+    const int c = n & 15;
+    p = (const uint8_t*)m + (tiled ? (size_t)(n - c) * Kb + 256 * g + 16 * c : (size_t)n * Kb + 16 * g);
+    shift = tiled ? 10 : 6;
+  }
+  __device__ u32x4 chunk(int j) const { return ld16(p + ((uint32_t)j << shift)); }
 };
-template <> struct BRow<bf16> {
-  const bf16* p;
-  __device__ BRow(const void* m, int n, int K, int g, const void*) : p((const bf16*)m + (size_t)n * K + 8 * g) {}
-  __device__ u32x4 load(int kb) const { return ld16(p + kb); }
-  __device__ float scale(int) const { return 1.f; }
-};
-template <> struct BRow<INT4> {
-  const uint8_t* p;
-  const uint16_t* s;
-  __device__ BRow(const void* m, int n, int K, int g, const void* sc)
-      : p((const uint8_t*)m + (size_t)n * (K / 2) + 16 * g), s((const uint16_t*)sc + (size_t)n * (K / kInt4Group)) {}
-  __device__ u32x4 load(int kb) const { return ld16(p + kb / 2); }
-  __device__ float scale(int kb) const { return bf16_bits_to_f32(s[kb / kInt4Group]); }
+
+// bytes of one K-contiguous weight row
+template <typename TW> __device__ constexpr int row_bytes(int K) { return K * (int)sizeof(TW); }
+template <> __device__ constexpr int row_bytes<INT4>(int K) { return K / 2; }
+
+// One weight row of a [N][K] matrix as seen by one lane; a step of KSTEP K
+// values is one 64-byte chunk of the row.  Lane K order inside a step:
+// bf16 k = kb + 8g + i; f32 k = kb + 4g + i; INT4 k = kb + 32g + 8s + i
+// (s = dword of the 16-byte load).
+template <typename TW> struct BRow {
+  WRow w;
+  const uint16_t* s;  // INT4 scales of the row (bf16, one per 128-K group)
+  __device__ BRow(const void* m, int n, int K, int g, const void* sc, int tiled)
+      : w(m, n, row_bytes<TW>(K), g, tiled),
+        s(std::is_same<TW, INT4>::value ? (const uint16_t*)sc + (size_t)n * (K / kInt4Group) : nullptr) {}
+  __device__ u32x4 load(int kb) const { return w.chunk(kb / Dec<TW>::KSTEP); }
+  __device__ float scale(int kb) const {
+    if constexpr (std::is_same<TW, INT4>::value) return bf16_bits_to_f32(s[kb / kInt4Group]);
+    else return 1.f;
+  }
 };
 
 // bytes (or elements) of one expert's [N][K] matrix, to step between experts
@@ -187,11 +202,11 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   const int nseg = (!GATEUP && shared) ? a.S : 1;
   // weight rows first: their loads do not wait for the activation row lookup
   BRow<TW> b0 = GATEUP ? BRow<TW>(shared ? a.shg : expert_mat<TW>(a.wg, e, a.F, a.d), n, K, g,
-                                  shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d))
+                                  shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d), a.wtiled)
                        : BRow<TW>(shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, K), n, K, g,
-                                  shared ? a.shsd : expert_scales(a.sd, e, a.d, K));
+                                  shared ? a.shsd : expert_scales(a.sd, e, a.d, K), a.wtiled);
   BRow<TW> b1 = GATEUP ? BRow<TW>(shared ? a.shu : expert_mat<TW>(a.wu, e, a.F, a.d), n, K, g,
-                                  shared ? a.shsu : expert_scales(a.su, e, a.F, a.d))
+                                  shared ? a.shsu : expert_scales(a.su, e, a.F, a.d), a.wtiled)
                        : b0;
 
   // activation rows (clamped into the item so every load is in bounds)
@@ -217,7 +232,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
 
   for (int seg = 0; seg < nseg; ++seg) {
     if (seg > 0) {  // next slab of the shared down projection: [S][d][FS]
-      b0 = BRow<TW>(expert_mat<TW>(a.shd, seg, a.d, K), n, K, g, expert_scales(a.shsd, seg, a.d, K));
+      b0 = BRow<TW>(expert_mat<TW>(a.shd, seg, a.d, K), n, K, g, expert_scales(a.shsd, seg, a.d, K), a.wtiled);
       b1 = b0;
     }
     const int aoff = seg * K;
@@ -329,7 +344,7 @@ template <bool G> struct Til<INT4, G> {
 };
 constexpr int TBM = 128;
 
-template <typename TW, bool GATEUP>
+template <typename TW, bool GATEUP, bool TILED>
 __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void ffn_tiled_kernel(FfnArgs a) {
   using TT = Til<TW, GATEUP>;
   constexpr int KSTEP = TT::KSTEP, SUB = TT::SUB, BL = TT::BL;
@@ -375,25 +390,25 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
   const int Kfull = GATEUP ? a.d : (shared ? a.S * a.FS : a.F);
   const int Kseg = GATEUP ? a.d : (shared ? a.FS : a.F);
 
-  // activation chunk sources: rows (tid / CPR) + RPT q, 16-byte chunk tid % CPR;
-  // 32-bit element offsets from one block-uniform base keep registers low
+  // activation chunk sources: rows (tid / CPR) + RPT q, 16-byte chunk tid % CPR
+  // (64-bit addresses: x and h may exceed 4 GiB)
   const int ch = tid % CPR;
-  const bf16* abase = GATEUP ? (const bf16*)a.x : (const bf16*)(shared ? a.hsh : a.h);
-  uint32_t aoff[CPT];  // byte offsets
+  const char* aptr[CPT];
 #pragma unroll
   for (int q = 0; q < CPT; ++q) {
     const int r = min(tid / CPR + RPT * q, mrows - 1);
     if (GATEUP) {
       int tok = shared ? row0 + r : a.row_token[row0 + r];
       tok = min(max(tok, 0), a.T - 1);
-      aoff[q] = ((uint32_t)tok * a.d + ch * 8) * 2u;
+      aptr[q] = (const char*)a.x + ((size_t)tok * a.d + ch * 8) * 2;
     } else {
-      aoff[q] = ((uint32_t)(row0 + r) * Kfull + ch * 8) * 2u;
+      aptr[q] = (const char*)(shared ? a.hsh : a.h) + ((size_t)(row0 + r) * Kfull + ch * 8) * 2;
     }
   }
-  // weight fragment f of this wave: byte offset of its row (plus the lane's K
-  // group) inside one of two block-uniform matrices (gate / up, or down; the
-  // shared down projection adds a block-uniform slab offset per K step)
+  // weight fragment f of this wave: byte offset of its lane's bytes inside one
+  // of two block-uniform matrices (gate / up, or down; the shared down
+  // projection adds a block-uniform slab offset per K step), in the row or the
+  // tiled weight layout (16-row x 64-byte fragments stored lane-major)
   const char* bmat[2];
   const uint16_t* smat[2];
   uint32_t boff[4], soff[4];
@@ -406,31 +421,23 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
     bmat[0] = bmat[1] = (const char*)(shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, Kseg));
     smat[0] = smat[1] = (const uint16_t*)(shared ? a.shsd : expert_scales(a.sd, e, a.d, Kseg));
   }
+  const int Kb = row_bytes<TW>(Kseg);
+  constexpr uint32_t cstride = TILED ? 1024u : 64u;  // bytes between the 64-byte chunks of a row
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
-    const int row = GATEUP ? n0 + 32 * w + 16 * (f & 1) + c
-                           : min(n0 + 64 * w + 16 * f + c, a.d - 1);  // a last block may be half past d
-    if constexpr (I4) {
-      boff[f] = (uint32_t)row * (Kseg / 2) + 16 * g;
-      soff[f] = (uint32_t)row * (Kseg / kInt4Group) * 2u;
-    } else {
-      boff[f] = ((uint32_t)row * Kseg + 8 * g) * 2u;
-      soff[f] = 0;
-    }
+    // first row of the fragment's 16-row group (a last down block may be half
+    // past d: its surplus fragments re-read the last group, results unused)
+    const int row16 = GATEUP ? n0 + 32 * w + 16 * (f & 1) : min(n0 + 64 * w + 16 * f, a.d - 16);
+    boff[f] = TILED ? (uint32_t)row16 * Kb + 256 * g + 16 * c : (uint32_t)(row16 + c) * Kb + 16 * g;
+    soff[f] = I4 ? (uint32_t)(row16 + c) * (Kseg / kInt4Group) * 2u : 0u;
   }
-  // byte offset of K step kt inside a weight row (plus the slab stride), and scale index
+  // byte offset of K step kt inside the weight matrix (slab plus row chunk), and scale index
   auto woff = [&](int kt, int* so) -> size_t {
     const int k0 = kt * KSTEP;
     const int slab = (!GATEUP && shared) ? k0 / Kseg : 0;
     const int kk = k0 - slab * Kseg;
-    const size_t slab_elems = (size_t)slab * a.d * Kseg;
-    if constexpr (I4) {
-      *so = (int)(slab_elems / kInt4Group) + kk / kInt4Group;
-      return (slab_elems + kk) / 2;
-    } else {
-      *so = 0;
-      return (slab_elems + kk) * sizeof(bf16);
-    }
+    *so = I4 ? slab * a.d * (Kseg / kInt4Group) + kk / kInt4Group : 0;
+    return (size_t)slab * a.d * Kb + (size_t)(row_bytes<TW>(kk) / 64) * cstride;
   };
 
   f32x4 acc[8][4];
@@ -446,7 +453,7 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
 
   auto load_a = [&](int kt) {
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) ar[q] = ld16_at(abase + kt * KSTEP, aoff[q]);
+    for (int q = 0; q < CPT; ++q) ar[q] = ld16(aptr[q] + kt * KSTEP * 2);
   };
   auto store_a = [&](bf16* dst) {
 #pragma unroll
@@ -465,7 +472,7 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
         bs[f] = bf16_bits_to_f32(*(const uint16_t*)(sm + soff[f]));
       } else {
 #pragma unroll
-        for (int s = 0; s < BL; ++s) bq[f][s] = ld16_at(m + 64 * s, boff[f]);
+        for (int s = 0; s < BL; ++s) bq[f][s] = ld16_at(m + cstride * s, boff[f]);
         bs[f] = 1.f;
       }
     }
@@ -553,6 +560,31 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
   }
 }
 
+// ------------------------------------------------------------------ weight packing
+// Tiled layout from the row layout (a byte permutation): output 16-byte unit
+// u = 64 * fragment + 16 * g + c of fragment (row group r16, chunk j) takes
+// bytes 64j + 16g .. +15 of row 16 * r16 + c.  Writes are consecutive; reads
+// gather 16 rows.  Grid-stride over all units.
+__global__ __launch_bounds__(256) void pack_tiled_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                         int64_t units, int64_t chunks_per_row) {
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+    const int64_t frag = u >> 6;
+    const int lane = (int)(u & 63), g = lane >> 4, c = lane & 15;
+    const int64_t r16 = frag / chunks_per_row, j = frag - r16 * chunks_per_row;
+    dst[u] = src[((16 * r16 + c) * chunks_per_row + j) * 4 + g];
+  }
+}
+
+hipError_t launch_pack_tiled(const void* src, void* dst, int64_t rows, int64_t row_bytes, hipStream_t s) {
+  const int64_t units = rows * row_bytes / 16;
+  if (units == 0) return hipSuccess;
+  const int64_t want = (units + 255) / 256;
+  const int grid = (int)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(pack_tiled_kernel, dim3(grid), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst, units,
+                     row_bytes / 64);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ combine
 // out[t] = sum_j gate[t,j] * y_rows[slot_row[t,j]] (+ y_shared[t]), fp32, j in order.
 template <typename TA>
@@ -629,6 +661,16 @@ static void launch_stream_mt(int wdt, const FfnArgs& a, int grid, hipStream_t s)
     launch_stream<GATEUP, 4>(wdt, a, grid, s);
 }
 
+template <bool GATEUP> void launch_tiled(int wdt, const FfnArgs& a, int grid, hipStream_t s) {
+  if (wdt == kBF16) {
+    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled_kernel<bf16, GATEUP, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((ffn_tiled_kernel<bf16, GATEUP, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled_kernel<INT4, GATEUP, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((ffn_tiled_kernel<INT4, GATEUP, false>), dim3(grid), dim3(256), 0, s, a);
+  }
+}
+
 hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s) {
   if (mode == 0) {
     const int grid = ffn_grid(a, a.F / 16, a.S * a.FS / 16);
@@ -637,10 +679,7 @@ hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipSt
   } else {
     const int grid = ffn_grid_xcd(a, a.F / 128, a.S * a.FS / 128);
     if (grid == 0) return hipSuccess;
-    if (wdt == kBF16)
-      hipLaunchKernelGGL((ffn_tiled_kernel<bf16, true>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((ffn_tiled_kernel<INT4, true>), dim3(grid), dim3(256), 0, s, a);
+    launch_tiled<true>(wdt, a, grid, s);
   }
   (void)act;
   return hipGetLastError();
@@ -654,10 +693,7 @@ hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStre
   } else {
     const int grid = ffn_grid_xcd(a, (a.d + 255) / 256, (a.d + 255) / 256);
     if (grid == 0) return hipSuccess;
-    if (wdt == kBF16)
-      hipLaunchKernelGGL((ffn_tiled_kernel<bf16, false>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((ffn_tiled_kernel<INT4, false>), dim3(grid), dim3(256), 0, s, a);
+    launch_tiled<false>(wdt, a, grid, s);
   }
   (void)act;
   return hipGetLastError();

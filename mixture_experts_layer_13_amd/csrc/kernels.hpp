@@ -49,6 +49,7 @@ struct FfnArgs {
   int items_max;             // static routed item slots of the grid
   int sh_items;              // static shared items (ceil(T / bm)) when S > 0
   int bm;
+  int wtiled;                // expert weights in the tiled layout (else one K-contiguous row per channel)
   const void *wg, *wu, *wd, *sg, *su, *sd;         // routed weights / INT4 scales
   const void *shg, *shu, *shd, *shsg, *shsu, *shsd;  // shared weights / INT4 scales
   void* h;                   // [R][F]     act dtype
@@ -71,6 +72,8 @@ hipError_t launch_tile_map(const int32_t* offsets, int E, int R, int bm, int4* i
 // expert FFN: mode 0 = streaming small-M kernels, 1 = LDS-tiled MFMA kernels
 hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s);
+// row layout -> tiled layout of `rows` weight rows of `row_bytes` bytes each
+hipError_t launch_pack_tiled(const void* src, void* dst, int64_t rows, int64_t row_bytes, hipStream_t s);
 hipError_t launch_combine(int act, const void* y, const int32_t* slot_row, const float* w, const void* ysh,
                           void* out, int T, int d, int k, int R, hipStream_t s);
 

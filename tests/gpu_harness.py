@@ -22,16 +22,23 @@ def _B():
     return binding
 
 
-def cfg_of(sp: S.LayerSpec, T: int):
+def cfg_of(sp: S.LayerSpec, T: int, layout: str = "rows"):
     return _B().make_cfg(T, sp.d, sp.E, sp.k, sp.ffn, sp.n_shared, sp.ffn_shared, act=sp.act, expert=sp.expert,
-                         score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale, capacity=sp.capacity)
+                         score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale, capacity=sp.capacity,
+                         layout=layout)
 
 
-def layer_of(sp: S.LayerSpec, lay: S.Layer):
+def layer_of(sp: S.LayerSpec, lay: S.Layer, layout: str = "rows"):
+    """A MoeLayer over the generated weights; layout "tiled" packs copies of the
+    expert matrices through moe_pack_weights first."""
     from mixture_experts_layer_13_amd.layer import MoeLayer
-    return MoeLayer(cfg_of(sp, 1), lay.w_router, lay.w_gate, lay.w_up, lay.w_down, logit_bias=lay.logit_bias,
+    mats = [lay.w_gate, lay.w_up, lay.w_down, lay.sh_gate, lay.sh_up, lay.sh_down]
+    if layout == "tiled":
+        mats = [None if m is None else _B().pack_tiled(m, sp.expert) for m in mats]
+    wg, wu, wd, shg, shu, shd = mats
+    return MoeLayer(cfg_of(sp, 1, layout), lay.w_router, wg, wu, wd, logit_bias=lay.logit_bias,
                     select_bias=lay.select_bias, s_gate=lay.s_gate, s_up=lay.s_up, s_down=lay.s_down,
-                    sh_gate=lay.sh_gate, sh_up=lay.sh_up, sh_down=lay.sh_down)
+                    sh_gate=shg, sh_up=shu, sh_down=shd)
 
 
 # ---------------------------------------------------------------- host copies for the oracle

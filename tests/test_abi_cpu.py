@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     lib.moe_abi_version.restype = ctypes.c_int32
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 @pytest.fixture(scope="module")
@@ -43,6 +43,7 @@ def test_validation_errors(B):
         dict(T=-1), dict(E=0), dict(E=257), dict(k=0), dict(k=9), dict(d=100), dict(ffn=64),
         dict(n_shared=1, ffn_shared=0), dict(act_dtype=7), dict(expert_dtype=2), dict(score=3), dict(renorm=2),
         dict(cap_num=1, cap_den=0), dict(cap_num=-1, cap_den=1), dict(gate_scale=float("nan")),
+        dict(weight_layout=2), dict(weight_layout=-1),
     ]
     for change in bad:
         c = B.MoeCfg.from_buffer_copy(ok)
@@ -58,6 +59,12 @@ def test_validation_errors(B):
     assert B.validate(c) == B.MOE_ERR_UNSUPPORTED   # k > E
     assert B.validate(B.make_cfg(32, 2048, 128, 8, 768, expert="int4")) == B.MOE_OK
     assert B.validate(B.make_cfg(32, 2048, 128, 8, 768, act="f32", expert="int4")) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(B.make_cfg(32, 2048, 128, 8, 768, layout="tiled")) == B.MOE_OK
+    # an expert matrix must stay under 2 GiB (32-bit offsets inside one matrix)
+    assert B.validate(B.make_cfg(4, 32768, 8, 2, 32768)) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(B.make_cfg(4, 32768, 8, 2, 16384)) == B.MOE_OK               # 1 GiB
+    assert B.validate(B.make_cfg(4, 32768, 8, 2, 16384, act="f32", expert="f32")) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(B.make_cfg(4, 1024, 8, 2, 512, 1, 1 << 20)) != B.MOE_OK
 
 
 def test_rows_capacity_and_workspace(B):
@@ -100,3 +107,20 @@ def test_entry_points_reject_bad_arguments_before_launch(B):
     st = B.lib.moe_permute(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, 16, None)
     assert st == B.MOE_ERR_WORKSPACE
     assert B.lib.moe_status_str(B.MOE_ERR_HIP) == b"HIP error"
+
+
+def test_pack_rejects_bad_arguments_before_launch(B):
+    P = ctypes.c_void_p
+    src, dst = P(0x100000), P(0x200000)   # never dereferenced: every call below fails validation first
+    pack = B.lib.moe_pack_weights
+    assert pack(B.MOE_BF16, src, dst, 0, 64, None) == B.MOE_OK            # nothing to do
+    assert pack(7, src, dst, 16, 64, None) == B.MOE_ERR_INVALID_ARG       # dtype
+    assert pack(B.MOE_BF16, src, dst, 8, 64, None) == B.MOE_ERR_INVALID_ARG      # rows not a multiple of 16
+    assert pack(B.MOE_BF16, src, dst, -16, 64, None) == B.MOE_ERR_INVALID_ARG
+    assert pack(B.MOE_BF16, src, dst, 16, 16, None) == B.MOE_ERR_INVALID_ARG     # 32-byte rows
+    assert pack(B.MOE_INT4_G128, src, dst, 16, 64, None) == B.MOE_ERR_INVALID_ARG  # K not a multiple of 128
+    assert pack(B.MOE_F32, src, dst, 16, 8, None) == B.MOE_ERR_INVALID_ARG
+    assert pack(B.MOE_BF16, None, dst, 16, 64, None) == B.MOE_ERR_INVALID_ARG
+    assert pack(B.MOE_BF16, P(0x100008), dst, 16, 64, None) == B.MOE_ERR_INVALID_ARG  # misaligned
+    assert pack(B.MOE_BF16, src, P(0x100400), 16, 64, None) == B.MOE_ERR_INVALID_ARG  # overlapping
+    assert pack(B.MOE_BF16, src, src, 16, 64, None) == B.MOE_ERR_INVALID_ARG
