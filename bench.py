@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--T", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
                     help="expert weight layout (tiled: repacked once before timing)")
     ap.add_argument("--decode-only", action="store_true", help="run only the decode sweep and print it")
@@ -232,6 +233,74 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4):
                                               f"{replays} replays", "points": res}
 
 
+LAUNCHES = ["router", "permute", "gateup", "down", "combine"]
+
+
+def time_layer(ml, x, steps, warmup):
+    """Eager forwards: `warmup` untimed, then `steps` timed between two events on
+    the stream, with the library's per-launch HIP events recorded on the same
+    stream.  Returns ms per step, mean ms per launch, the last outputs, launches."""
+    import torch
+
+    from mixture_experts_layer_13_amd import binding as B
+    T = x.shape[0]
+    c = ml.cfg
+    nl = B.forward_launches(ml.cfg_for(T))
+    outs = (torch.empty((T, c.d), dtype=ml.act_dtype, device="cuda"),
+            torch.empty((T, c.k), dtype=torch.int32, device="cuda"),
+            torch.empty((T, c.k), dtype=torch.float32, device="cuda"),
+            torch.empty((T, c.k), dtype=torch.uint8, device="cuda"))
+    for _ in range(warmup):
+        ml.forward(x, *outs)
+    torch.cuda.synchronize()
+    ev = HipEvents(steps * (nl + 1))
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        B.lib.moe_set_timing_events(ev.slice(i * (nl + 1), nl + 1), nl + 1)
+        ml.forward(x, *outs)
+    t1.record()
+    B.lib.moe_set_timing_events(None, 0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / steps
+    per = {n: 0.0 for n in LAUNCHES}
+    for i in range(steps):
+        b = i * (nl + 1)
+        for j, n in enumerate(LAUNCHES):
+            per[n] += ev.ms(b + j, b + j + 1) / steps
+    ev.close()
+    return ms_step, per, outs, nl, wall
+
+
+def prefill_sweep(layout, steps=20, warmup=3):
+    """The prefill layers the MFMA target is set for (T >= 8192): useful-flop
+    MFMA fraction of the whole layer and of its gate/up launch."""
+    import torch
+
+    import moe_synth as S
+    res = {}
+    for name, T in (("dsv2_lite", 8192), ("dsv2_lite_cap", 8192), ("dsv3", 16384)):
+        sp = S.SPECS[name]
+        lay = S.make_layer(sp, device="cuda")
+        ml = moe_layer(sp, lay, layout)
+        x = S.make_tokens(sp, T, device="cuda")
+        ms, per, outs, _, _ = time_layer(ml, x, steps, warmup)
+        w = alg_work(sp, T, outs[1], outs[3])
+        res[f"{name}_T{T}"] = {
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "mfma_frac_layer": round(w["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_gateup": round(w["gateup_flops"] / (per["gateup"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "per_launch_us": {n: round(v * 1e3, 2) for n, v in per.items()},
+            "kept_pairs": w["kept"], "pairs": T * sp.k}
+        del ml, lay, x, outs
+        torch.cuda.empty_cache()
+    return {"method": f"eager, {steps} timed forwards after {warmup}; useful flops only (dropped pairs and tile "
+                      "padding excluded)", "points": res}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -256,37 +325,8 @@ def main():
         return
     x = S.make_tokens(sp, T, device="cuda")
     ml = moe_layer(sp, lay, args.layout)
-    cfg = ml.cfg_for(T)
-    nl = B.forward_launches(cfg)
-    outs = (torch.empty((T, sp.d), dtype=torch.bfloat16, device="cuda"),
-            torch.empty((T, sp.k), dtype=torch.int32, device="cuda"),
-            torch.empty((T, sp.k), dtype=torch.float32, device="cuda"),
-            torch.empty((T, sp.k), dtype=torch.uint8, device="cuda"))
-    for _ in range(args.warmup):
-        ml.forward(x, *outs)
-    torch.cuda.synchronize()
-
     K = args.steps
-    ev = HipEvents(K * (nl + 1))
-    t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_all0.record()
-    for i in range(K):
-        B.lib.moe_set_timing_events(ev.slice(i * (nl + 1), nl + 1), nl + 1)
-        ml.forward(x, *outs)
-    t_all1.record()
-    B.lib.moe_set_timing_events(None, 0)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_all0.elapsed_time(t_all1) / K
-    names = ["router", "permute", "gateup", "down", "combine"]
-    per = {n: 0.0 for n in names}
-    for i in range(K):
-        b = i * (nl + 1)
-        for j, n in enumerate(names):
-            per[n] += ev.ms(b + j, b + j + 1) / K
-    ev.close()
+    ms_step, per, outs, nl, wall = time_layer(ml, x, K, args.warmup)
 
     w = alg_work(sp, T, outs[1], outs[3])
     t_gu = per["gateup"] * 1e-3
@@ -318,6 +358,10 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = decode_sweep(sp, lay, args.layout)
+    if not args.no_prefill:
+        del ml, lay, x
+        torch.cuda.empty_cache()
+        line["prefill"] = prefill_sweep(args.layout)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_tokens=256)
     print(json.dumps(line), flush=True)
