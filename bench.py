@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
                     help="expert weight layout (tiled: repacked once before timing)")
     ap.add_argument("--decode-only", action="store_true", help="run only the decode sweep and print it")
+    ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/gateup_tiled_olmoe_T4096_traffic.json from four rocprofv3 --pmc csv "
+                         "directories (FETCH_SIZE and WRITE_SIZE of this bench, then of --copy-probe) and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device-to-device copy three times (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -141,17 +144,71 @@ def alg_work(sp, T, idx, drop):
     return dict(bytes=byts, flops=flops, gateup_flops=gateup, touched=touched, kept=n_kept)
 
 
-def traffic_record(kernel_src):
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "gateup_tiled_olmoe_T4096_traffic.json")
+# the sources the dominant (bf16 tiled gate/up) kernel is compiled from
+KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", f)
+                  for f in ("ffn_tiled.hip", "ffn_common.hpp", "common.hpp", "kernels.hpp")]
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_record():
     """HBM bytes of the dominant kernel from the committed rocprofv3 counter summary,
-    valid only while the kernel source is the one the counters were taken on."""
-    path = os.path.join(ROOT, "profiles", "gateup_tiled_olmoe_T4096_traffic.json")
-    if not os.path.exists(path):
+    valid only while the kernel's sources are the ones the counters were taken on."""
+    if not os.path.exists(TRAFFIC_PATH):
         return None
-    rec = json.load(open(path))
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    rec = json.load(open(TRAFFIC_PATH))
+    if rec.get("source_sha256") != kernel_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _pmc_mean_kib(csv_dir, counter, kernel_substr, largest=None):
+    """Mean per-dispatch value of `counter` over the dispatches of kernels whose
+    name contains one of `kernel_substr` in a rocprofv3 --pmc csv output directory
+    (over the `largest` biggest values only, when given)."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and any(k in r["Kernel_Name"] for k in kernel_substr):
+                vals.append(float(r["Counter_Value"]))
+    if largest:
+        vals = sorted(vals)[-largest:]
+    if not vals:
+        raise SystemExit(f"no {counter} values for kernels matching {kernel_substr!r} under {csv_dir}")
+    return sum(vals) / len(vals)
+
+
+def write_traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+    """Writes the traffic record of the gate/up kernel from four rocprofv3 --pmc runs:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the bench, and of the copy probe,
+    whose known 1 GiB read + 1 GiB write calibrates each counter."""
+    gu = ("ffn_tiled32_kernel<true", "ffn_tiled32_kernelILb1E")  # demangled or mangled name
+    copy = ("copyBuffer",)  # the runtime's device-to-device copy kernel behind the probe's Tensor.copy_
+    f_k = _pmc_mean_kib(fetch_dir, "FETCH_SIZE", gu)
+    w_k = _pmc_mean_kib(write_dir, "WRITE_SIZE", gu)
+    cf = _pmc_mean_kib(copy_fetch_dir, "FETCH_SIZE", copy, largest=3)
+    cw = _pmc_mean_kib(copy_write_dir, "WRITE_SIZE", copy, largest=3)
+    nbytes = 1 << 30
+    fs, ws = nbytes / (cf * 1024), nbytes / (cw * 1024)
+    rec = {"kernel": "ffn_tiled32_kernel<gate/up + SwiGLU, tiled weights>", "workload": "olmoe_1b7b_layer_T4096",
+           "fetch_size_kib_per_launch": round(f_k, 1), "write_size_kib_per_launch": round(w_k, 1),
+           "copy_probe": {"bytes_read": nbytes, "bytes_written": nbytes, "fetch_size_kib": round(cf, 1),
+                          "write_size_kib": round(cw, 1), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+           "hbm_bytes_per_launch": int(f_k * 1024 * fs + w_k * 1024 * ws),
+           "commands": commands, "source_files": [os.path.relpath(f, ROOT) for f in KERNEL_SOURCES],
+           "source_sha256": kernel_sha()}
+    with open(TRAFFIC_PATH, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(sp, lay, x, n_tokens):
@@ -303,6 +360,12 @@ def prefill_sweep(layout, steps=20, warmup=3):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d <out> -o pmc -- python3 bench.py {a}"
+                for a in ("--steps 5 --warmup 2 --no-cpu --no-decode --no-prefill", "--copy-probe")
+                for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        write_traffic_record(*args.traffic_record, commands=cmds)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the layer on one GPU only (asked for {max(args.gpus, world)}): the path has no "
@@ -331,7 +394,7 @@ def main():
     w = alg_work(sp, T, outs[1], outs[3])
     t_gu = per["gateup"] * 1e-3
     achieved = w["gateup_flops"] / t_gu / 1e12
-    traffic = traffic_record(os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", "ffn.hip"))
+    traffic = traffic_record()
     line = {
         "metric": METRIC,
         "value": round(T / (ms_step * 1e-3), 1),
@@ -347,7 +410,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"olmoe_1b7b_layer_T{T}", "T": T, "d": sp.d, "E": sp.E, "k": sp.k,
                    "ffn": sp.ffn, "launches_per_layer": nl, "weight_layout": args.layout},
-        "roofline": {"bound": "mfma", "kernel": "ffn_tiled_kernel<bf16,gate/up>", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "ffn_tiled32_kernel<gate/up + SwiGLU>", "achieved": round(achieved, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic, "avg_launch_us": round(per["gateup"] * 1e3, 2),
                      "alg_flops_per_launch": w["gateup_flops"]},
@@ -358,12 +421,12 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = decode_sweep(sp, lay, args.layout)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_tokens=256)
     if not args.no_prefill:
         del ml, lay, x
         torch.cuda.empty_cache()
         line["prefill"] = prefill_sweep(args.layout)
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_tokens=256)
     print(json.dumps(line), flush=True)
 
 

@@ -1,0 +1,115 @@
+// Device helpers shared by the expert FFN kernels (streaming, tiled bf16,
+// tiled INT4): bf16 packing, INT4 nibble decoding, SiLU, weight-matrix
+// addressing and the tile list of the tiled kernels.
+#pragma once
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(bf16)lo, (bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight two's-complement nibbles (element i in bits 4i..4i+3) -> eight exact
+// bf16 values.  Flipping bit 3 of each nibble gives q + 8; OR-ing that into
+// the mantissa of 2^23 and subtracting 2^23 + 8 yields q exactly in fp32.
+__device__ __forceinline__ u32x4 int4x8_to_bf16(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float lo = __uint_as_float(0x4B000000u | ((x >> (8 * p)) & 0xFu)) - 8388616.0f;
+    const float hi = __uint_as_float(0x4B000000u | ((x >> (8 * p + 4)) & 0xFu)) - 8388616.0f;
+    r[p] = pack_bf16x2(lo, hi);
+  }
+  return r;
+}
+
+// Same, times the group scale, rounded once to bf16 (operand of the tiled kernels).
+__device__ __forceinline__ u32x4 int4x8_to_bf16_scaled(uint32_t w, float sc) {
+  const uint32_t x = w ^ 0x88888888u;
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float lo = (__uint_as_float(0x4B000000u | ((x >> (8 * p)) & 0xFu)) - 8388616.0f) * sc;
+    const float hi = (__uint_as_float(0x4B000000u | ((x >> (8 * p + 4)) & 0xFu)) - 8388616.0f) * sc;
+    r[p] = pack_bf16x2(lo, hi);
+  }
+  return r;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// bytes of one K-contiguous weight row
+template <typename TW> __device__ __forceinline__ constexpr int row_bytes(int K) { return K * (int)sizeof(TW); }
+template <> __device__ __forceinline__ constexpr int row_bytes<INT4>(int K) { return K / 2; }
+
+// bytes (or elements) of one expert's [N][K] matrix, to step between experts
+template <typename TW> __device__ __forceinline__ const void* expert_mat(const void* base, int e, int N, int K);
+template <> __device__ __forceinline__ const void* expert_mat<float>(const void* b, int e, int N, int K) {
+  return (const float*)b + (size_t)e * N * K;
+}
+template <> __device__ __forceinline__ const void* expert_mat<bf16>(const void* b, int e, int N, int K) {
+  return (const bf16*)b + (size_t)e * N * K;
+}
+template <> __device__ __forceinline__ const void* expert_mat<INT4>(const void* b, int e, int N, int K) {
+  return (const uint8_t*)b + (size_t)e * N * (K / 2);
+}
+__device__ __forceinline__ const void* expert_scales(const void* b, int e, int N, int K) {
+  return b ? (const void*)((const uint16_t*)b + (size_t)e * N * (K / kInt4Group)) : nullptr;
+}
+
+__device__ __forceinline__ f32x16 mma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+constexpr int TBM = 128;
+
+// The tile a block of a tiled kernel owns.  Tile list: routed items
+// (expert-major, so one expert's tiles are adjacent) times N blocks of NT
+// output channels, then the shared-expert tiles.  Blocks are dispatched
+// round-robin over the 8 XCDs, so XCD x = blockIdx % 8 takes the x-th of 8
+// contiguous, equal chunks of the list: the tiles of an expert then run
+// together on one XCD and share their weight and activation K slabs in its L2.
+struct TileInfo {
+  int e, row0, mrows, n0;
+  bool shared;
+};
+__device__ __forceinline__ bool tile_of(const FfnArgs& a, int NT, TileInfo& t) {
+  const bool gu = NT == 128;  // gate/up blocks cover 128 channels, down blocks 256 columns
+  const int Nr = gu ? a.F : a.d, Ns = gu ? a.S * a.FS : a.d;
+  const int nbr = (Nr + NT - 1) / NT, nbs = (Ns + NT - 1) / NT;
+  const int routed_tiles = *a.n_items * nbr;
+  const int total = routed_tiles + (a.S > 0 ? a.sh_items * nbs : 0);
+  const int xcd = blockIdx.x & 7;
+  const int lo = (int)((int64_t)total * xcd / 8), hi = (int)((int64_t)total * (xcd + 1) / 8);
+  const int tile = lo + (int)(blockIdx.x >> 3);
+  if (tile >= hi) return false;
+  int nb;
+  t.shared = tile >= routed_tiles;
+  if (!t.shared) {
+    const int slot = tile / nbr;
+    nb = tile - slot * nbr;
+    const int4 it = a.items[slot];
+    t.e = it.x;
+    t.row0 = it.y;
+    t.mrows = it.z;
+  } else {
+    const int sb = tile - routed_tiles;
+    const int slot = sb / nbs;
+    nb = sb - slot * nbs;
+    t.e = 0;
+    t.row0 = slot * a.bm;
+    t.mrows = min(a.bm, a.T - t.row0);
+  }
+  t.n0 = nb * NT;
+  return true;
+}
+
+}  // namespace moe

@@ -1,0 +1,267 @@
+// Streaming (small-M, decode) expert FFN kernels for gfx950: a block owns one
+// tile-map item (<= 64 rows of one expert) and 16 (gate/up) or 64 (down)
+// output channels; its waves read their weight slice once, straight from
+// memory into MFMA operands, so the weight stream is the whole cost.
+#include "ffn_common.hpp"
+
+namespace moe {
+
+// Per weight type: K covered by one 16-byte weight load per lane (KSTEP),
+// 16-byte activation loads per m-tile per step (AL), steps unrolled (U).
+template <typename TW> struct Dec;
+template <> struct Dec<float> {
+  using TA = float;
+  static constexpr int KSTEP = 16, AL = 1, U = 4;
+};
+template <> struct Dec<bf16> {
+  using TA = bf16;
+  static constexpr int KSTEP = 32, AL = 1, U = 4;
+};
+template <> struct Dec<INT4> {
+  using TA = bf16;
+  static constexpr int KSTEP = 128, AL = 4, U = 2;
+};
+
+// Weight bytes of one output channel n (row n of an [N][K] matrix, Kb bytes
+// per row) as one lane sees them: the row is read in 64-byte chunks, the lane
+// taking bytes 16g..16g+15 of each (g = lane / 16; lane % 16 = n % 16).
+//  - row layout: chunk j of row n at n*Kb + 64j;
+//  - tiled layout: the 16-row x 64-byte fragment (n/16, j) is one contiguous
+//    KB at ((n/16)*(Kb/64) + j)*1024, lane-major: bytes 16*(16g + c).. hold
+//    row 16*(n/16) + c, bytes 16g.. of the chunk, so one wave-wide 16-byte load
+//    of a fragment reads 1 KB of consecutive addresses.
+struct WRow {
+  const uint8_t* p;  // chunk 0 of this lane
+  int shift;         // log2 of the bytes from chunk j to chunk j + 1
+  __device__ WRow(const void* m, int n, int Kb, int g, int tiled) {
+    const int c = n & 15;
+    p = (const uint8_t*)m + (tiled ? (size_t)(n - c) * Kb + 256 * g + 16 * c : (size_t)n * Kb + 16 * g);
+    shift = tiled ? 10 : 6;
+  }
+  __device__ u32x4 chunk(int j) const { return ld16(p + ((uint32_t)j << shift)); }
+};
+
+// One weight row of a [N][K] matrix as seen by one lane; a step of KSTEP K
+// values is one 64-byte chunk of the row.  Lane K order inside a step:
+// bf16 k = kb + 8g + i; f32 k = kb + 4g + i; INT4 k = kb + 32g + 8s + i
+// (s = dword of the 16-byte load).
+template <typename TW> struct BRow {
+  WRow w;
+  const uint16_t* s;  // INT4 scales of the row (bf16, one per 128-K group)
+  __device__ BRow(const void* m, int n, int K, int g, const void* sc, int tiled)
+      : w(m, n, row_bytes<TW>(K), g, tiled),
+        s(std::is_same<TW, INT4>::value ? (const uint16_t*)sc + (size_t)n * (K / kInt4Group) : nullptr) {}
+  __device__ u32x4 load(int kb) const { return w.chunk(kb / Dec<TW>::KSTEP); }
+  __device__ float scale(int kb) const {
+    if constexpr (std::is_same<TW, INT4>::value) return bf16_bits_to_f32(s[kb / kInt4Group]);
+    else return 1.f;
+  }
+};
+
+template <typename TW>
+__device__ __forceinline__ f32x4 dstep(const u32x4 (&av)[Dec<TW>::AL], u32x4 b, float sc, f32x4 acc);
+template <> __device__ __forceinline__ f32x4 dstep<float>(const u32x4 (&av)[1], u32x4 b, float, f32x4 acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = mma_f32(__uint_as_float(av[0][i]), __uint_as_float(b[i]), acc);
+  return acc;
+}
+template <> __device__ __forceinline__ f32x4 dstep<bf16>(const u32x4 (&av)[1], u32x4 b, float, f32x4 acc) {
+  return mma_bf16(av[0], b, acc);
+}
+template <> __device__ __forceinline__ f32x4 dstep<INT4>(const u32x4 (&av)[4], u32x4 b, float sc, f32x4 acc) {
+  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) t = mma_bf16(av[s], int4x8_to_bf16(b[s]), t);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[i], acc[i]);
+  return acc;
+}
+
+// GATEUP: h[row][n] = silu(A Wg^T) * (A Wu^T); else y[row][n] = A Wd^T.
+// A block owns one item (<= 16 * MT rows of one expert).  Gate/up (K = d,
+// large): the four waves split K into quarters for the same 16 channels and
+// add their partial sums in LDS in wave order.  Down (K = ffn): each wave owns
+// 16 channels over the whole K, so a block covers 64.  Steps are unrolled U
+// deep so each lane keeps U weight loads per matrix in flight.
+// grid: items_max * (N / channels per block) routed blocks, then the shared blocks.
+template <typename TW, bool GATEUP, int MT>
+__global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
+  using D = Dec<TW>;
+  using TA = typename D::TA;
+  constexpr int NM = GATEUP ? 2 : 1;
+  constexpr int KSPLIT = GATEUP ? 4 : 1;         // waves sharing one channel block
+  constexpr int CPB = 16 * (4 / KSPLIT);          // channels per block
+  constexpr int U = (std::is_same<TW, INT4>::value || MT == 4) ? 4 : 8;
+  constexpr int AL = D::AL, KSTEP = D::KSTEP;
+  __shared__ f32x4 red[KSPLIT > 1 ? 3 : 1][NM][MT][64];
+  const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+
+  const int Nr = GATEUP ? a.F : a.d;
+  const int Ns = GATEUP ? a.S * a.FS : a.d;
+  const int nbr = Nr / CPB, nbs = Ns / CPB;
+  const int routed_blocks = a.items_max * nbr;
+  int bid = blockIdx.x, e = 0, row0, mrows, nb;
+  const bool shared = bid >= routed_blocks;
+  if (!shared) {
+    const int slot = bid / nbr;
+    nb = bid - slot * nbr;
+    if (slot >= *a.n_items) return;
+    const int4 it = a.items[slot];
+    e = it.x;
+    row0 = it.y;
+    mrows = it.z;
+  } else {
+    bid -= routed_blocks;
+    const int slot = bid / nbs;
+    nb = bid - slot * nbs;
+    row0 = slot * a.bm;
+    mrows = min(a.bm, a.T - row0);
+  }
+  const int nmt = (mrows + 15) / 16;
+  const int kpart = KSPLIT > 1 ? w : 0;
+  const int n = nb * CPB + (KSPLIT > 1 ? 0 : 16 * w) + c;
+
+  const int K = GATEUP ? a.d : (shared ? a.FS : a.F);  // K of one segment
+  const int nseg = (!GATEUP && shared) ? a.S : 1;
+  // weight rows first: their loads do not wait for the activation row lookup
+  BRow<TW> b0 = GATEUP ? BRow<TW>(shared ? a.shg : expert_mat<TW>(a.wg, e, a.F, a.d), n, K, g,
+                                  shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d), a.wtiled)
+                       : BRow<TW>(shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, K), n, K, g,
+                                  shared ? a.shsd : expert_scales(a.sd, e, a.d, K), a.wtiled);
+  BRow<TW> b1 = GATEUP ? BRow<TW>(shared ? a.shu : expert_mat<TW>(a.wu, e, a.F, a.d), n, K, g,
+                                  shared ? a.shsu : expert_scales(a.su, e, a.F, a.d), a.wtiled)
+                       : b0;
+
+  // activation rows (clamped into the item so every load is in bounds)
+  const TA* arow[MT];
+  const int Kfull = GATEUP ? a.d : (shared ? a.S * a.FS : a.F);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = min(16 * mt + c, mrows - 1);
+    if (GATEUP) {
+      int tok = shared ? row0 + r : a.row_token[row0 + r];
+      tok = min(max(tok, 0), a.T - 1);
+      arow[mt] = (const TA*)a.x + (size_t)tok * a.d;
+    } else {
+      arow[mt] = (const TA*)(shared ? a.hsh : a.h) + (size_t)(row0 + r) * Kfull;
+    }
+  }
+
+  f32x4 acc[NM][MT];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[m][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int seg = 0; seg < nseg; ++seg) {
+    if (seg > 0) {  // next slab of the shared down projection: [S][d][FS]
+      b0 = BRow<TW>(expert_mat<TW>(a.shd, seg, a.d, K), n, K, g, expert_scales(a.shsd, seg, a.d, K), a.wtiled);
+      b1 = b0;
+    }
+    const int aoff = seg * K;
+    const int nsteps = K / KSTEP;
+    const int s0 = kpart * nsteps / KSPLIT, s1 = (kpart + 1) * nsteps / KSPLIT;
+#pragma unroll 1  // U-deep unroll inside already; a further unroll only costs occupancy
+    for (int st = s0; st < s1; st += U) {
+      u32x4 bq[NM][U];
+      float sc[NM][U];
+      u32x4 av[MT][U][AL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (st + u < s1) {
+          const int kb = (st + u) * KSTEP;
+          bq[0][u] = b0.load(kb);
+          sc[0][u] = b0.scale(kb);
+          if (NM > 1) {
+            bq[NM - 1][u] = b1.load(kb);
+            sc[NM - 1][u] = b1.scale(kb);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (st + u < s1) {
+          const int kb = (st + u) * KSTEP;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (mt < nmt)
+#pragma unroll
+              for (int q = 0; q < AL; ++q)
+                av[mt][u][q] = ld16(arow[mt] + aoff + kb + (AL == 1 ? (KSTEP / 4) * g : 32 * g + 8 * q));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (st + u < s1) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              if (mt < nmt) acc[m][mt] = dstep<TW>(av[mt][u], bq[m][u], sc[m][u], acc[m][mt]);
+        }
+      }
+    }
+  }
+
+  if (KSPLIT > 1) {
+    // add the K slices (fixed order) in wave 0
+    if (w > 0) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          if (mt < nmt) red[w - 1][m][mt][lane] = acc[m][mt];
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        if (mt < nmt) acc[m][mt] = ((acc[m][mt] + red[0][m][mt][lane]) + red[1][m][mt][lane]) + red[2][m][mt][lane];
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt >= nmt) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mt + 4 * g + i;
+      if (r >= mrows) continue;
+      if (GATEUP) {
+        const float hv = silu(acc[0][mt][i]) * acc[NM - 1][mt][i];
+        TA* hout = (TA*)(shared ? a.hsh : a.h);
+        hout[(size_t)(row0 + r) * (shared ? Ns : Nr) + n] = from_f32<TA>(hv);
+      } else {
+        TA* yout = (TA*)(shared ? a.ysh : a.y);
+        yout[(size_t)(row0 + r) * a.d + n] = from_f32<TA>(acc[0][mt][i]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+template <bool GATEUP, int MT>
+static void launch_stream(int wdt, const FfnArgs& a, int grid, hipStream_t s) {
+  if (wdt == kF32)
+    hipLaunchKernelGGL((ffn_stream_kernel<float, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+  else if (wdt == kBF16)
+    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_stream_kernel<INT4, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+}
+
+// items of <= 16, 32 or 64 rows take 1, 2 or 4 row tiles of 16
+void launch_stream_ffn(bool gateup, int wdt, const FfnArgs& a, int grid, hipStream_t s) {
+  const int mt = a.bm <= 16 ? 1 : (a.bm <= 32 ? 2 : 4);
+  if (gateup) {
+    if (mt == 1) launch_stream<true, 1>(wdt, a, grid, s);
+    else if (mt == 2) launch_stream<true, 2>(wdt, a, grid, s);
+    else launch_stream<true, 4>(wdt, a, grid, s);
+  } else {
+    if (mt == 1) launch_stream<false, 1>(wdt, a, grid, s);
+    else if (mt == 2) launch_stream<false, 2>(wdt, a, grid, s);
+    else launch_stream<false, 4>(wdt, a, grid, s);
+  }
+}
+
+}  // namespace moe

@@ -69,6 +69,11 @@ hipError_t launch_permute_multi(const int32_t* idx, const int32_t* hist, const P
 hipError_t launch_tile_map(const int32_t* offsets, int E, int R, int bm, int4* items, int32_t* n_items,
                            hipStream_t s);
 
+// per-family launchers of the expert FFN kernels (grid from launch_ffn_*)
+void launch_stream_ffn(bool gateup, int wdt, const FfnArgs& a, int grid, hipStream_t s);
+void launch_tiled_bf16(bool gateup, const FfnArgs& a, int grid, hipStream_t s);
+void launch_tiled_int4(bool gateup, const FfnArgs& a, int grid, hipStream_t s);
+
 // expert FFN: mode 0 = streaming small-M kernels, 1 = LDS-tiled MFMA kernels
 hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s);
