@@ -238,26 +238,30 @@ def cpu_baseline(sp, lay, x, n_tokens):
                       f"all selected expert FFNs from bf16 bit patterns, combine); {dt:.1f} s"}
 
 
-def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4):
+def clone_weights(lay):
+    """A copy of a layer with every weight tensor in new device memory."""
+    import dataclasses
+    kw = {f.name: getattr(lay, f.name).clone() for f in dataclasses.fields(lay)
+          if f.name != "spec" and getattr(lay, f.name) is not None}
+    return dataclasses.replace(lay, **kw)
+
+
+def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name="olmoe_1b7b"):
     """Decode-sized forwards as hipGraph replays over `copies` weight copies (cold in
     the 256 MB Infinity Cache), reported as achieved HBM bandwidth."""
     import torch
 
     import moe_synth as S
     layers = [moe_layer(sp, lay, layout)]
-    keep = []
     for c in range(1, copies):
-        cp = S.Layer(sp, lay.w_router.clone(), lay.logit_bias, lay.select_bias, lay.w_gate.clone(),
-                     lay.w_up.clone(), lay.w_down.clone())
-        keep.append(cp)
-        layers.append(moe_layer(sp, cp, layout))
+        layers.append(moe_layer(sp, clone_weights(lay), layout))
     res = {}
     s = torch.cuda.Stream()
     for T in Ts:
         x = S.make_tokens(sp, T, device="cuda")
         graphs, outs = [], []
         for ml in layers:
-            o = (torch.empty((T, sp.d), dtype=torch.bfloat16, device="cuda"),
+            o = (torch.empty((T, sp.d), dtype=ml.act_dtype, device="cuda"),
                  torch.empty((T, sp.k), dtype=torch.int32, device="cuda"),
                  torch.empty((T, sp.k), dtype=torch.float32, device="cuda"),
                  torch.empty((T, sp.k), dtype=torch.uint8, device="cuda"))
@@ -286,8 +290,25 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4):
                         "alg_bytes": w["bytes"], "touched_experts": w["touched"], "hbm_GBps": round(gbs, 1),
                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
         del graphs
-    return {"layer": "olmoe_1b7b", "method": f"hipGraph replay, {copies} weight copies round-robin, "
-                                              f"{replays} replays", "points": res}
+    return {"layer": name, "method": f"hipGraph replay, {copies} weight copies round-robin, {replays} replays",
+            "points": res}
+
+
+def decode_other(layout):
+    """The other decode-sized layers the HBM target covers: Qwen3 INT4 at T=32 (4
+    copies of its 0.31 GB of expert weights) and DeepSeek-V3 at T=1 and 16 (2 copies:
+    one token already touches 0.8 GB)."""
+    import torch
+
+    import moe_synth as S
+    out = {}
+    for name, Ts, copies in (("qwen3_int4", (32,), 4), ("dsv3", (1, 16), 2)):
+        sp = S.SPECS[name]
+        lay = S.make_layer(sp, device="cuda")
+        out[name] = decode_sweep(sp, lay, layout, Ts=Ts, replays=100, copies=copies, name=name)
+        del lay
+        torch.cuda.empty_cache()
+    return out
 
 
 LAUNCHES = ["router", "permute", "gateup", "down", "combine"]
@@ -385,6 +406,7 @@ def main():
     lay = S.make_layer(sp, device="cuda")
     if args.decode_only:
         print(json.dumps(decode_sweep(sp, lay, args.layout)), flush=True)
+        print(json.dumps(decode_other(args.layout)), flush=True)
         return
     x = S.make_tokens(sp, T, device="cuda")
     ml = moe_layer(sp, lay, args.layout)
@@ -421,6 +443,7 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = decode_sweep(sp, lay, args.layout)
+        line["decode_other"] = decode_other(args.layout)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_tokens=256)
     if not args.no_prefill:

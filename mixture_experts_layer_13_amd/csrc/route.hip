@@ -355,31 +355,41 @@ __global__ __launch_bounds__(1024) void route_permute_single_kernel(const float*
     const int G = kLog / E;  // tokens per group (E <= 256 -> G >= 64)
     for (int tg = 0; tg < T; tg += G) {
       const int nt = min(G, T - tg);
-      // logits (before the skew bias) = sum of the K-chunk partials in chunk
-      // order; each thread issues the loads of up to 4 elements x 8 chunks at once
+      // logits (before the skew bias) = sum of the KS K-chunk partials.  KG
+      // consecutive lanes share an element when there are few elements (small
+      // T): lane g of the group adds chunks g, g + KG, ... in order, then the
+      // group adds its KG sums in a fixed butterfly; each thread issues all its
+      // loads (up to 4 elements x 16 chunks) at once, one round trip per batch
+      const int nout = nt * E;
+      int KG = 1;
+      while (KG < 16 && 2 * KG * nout <= (int)blockDim.x && 2 * KG <= KS) KG *= 2;
+      const int g = tid % KG, per = (int)blockDim.x / KG;
       const size_t zs = (size_t)T * E;
-      for (int i0 = tid; i0 < nt * E; i0 += 4 * blockDim.x) {
+      for (int i0 = tid / KG; i0 < nout; i0 += 4 * per) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int z0 = 0; z0 < KS; z0 += 8) {
-          float v[4][8];
+        for (int z0 = g; z0 < KS; z0 += 16 * KG) {
+          float v[4][16];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int i = i0 + q * blockDim.x;
+            const int i = i0 + q * per;
             const int t = tg + i / E, e = i - (i / E) * E;
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-              v[q][u] = (i < nt * E && z0 + u < KS) ? part[(size_t)(z0 + u) * zs + (size_t)t * E + e] : 0.f;
+            for (int u = 0; u < 16; ++u) {
+              const int z = z0 + u * KG;
+              v[q][u] = (i < nout && z < KS) ? part[(size_t)z * zs + (size_t)t * E + e] : 0.f;
+            }
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-              if (z0 + u < KS) acc[q] += v[q][u];
+            for (int u = 0; u < 16; ++u)
+              if (z0 + u * KG < KS) acc[q] += v[q][u];
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int i = i0 + q * blockDim.x;
-          if (i < nt * E) slog[i] = acc[q];
+          for (int o = 1; o < KG; o <<= 1) acc[q] += __shfl_xor(acc[q], o);
+          const int i = i0 + q * per;
+          if (g == 0 && i < nout) slog[i] = acc[q];
         }
       }
       __syncthreads();
