@@ -354,13 +354,14 @@ def time_layer(ml, x, steps, warmup):
 
 
 def prefill_sweep(layout, steps=20, warmup=3):
-    """The prefill layers the MFMA target is set for (T >= 8192): useful-flop
-    MFMA fraction of the whole layer and of its gate/up launch."""
+    """The prefill layers the MFMA target is set for (T >= 8192), and the INT4
+    layer's prefill: useful-flop MFMA fraction of the whole layer and of its
+    gate/up launch."""
     import torch
 
     import moe_synth as S
     res = {}
-    for name, T in (("dsv2_lite", 8192), ("dsv2_lite_cap", 8192), ("dsv3", 16384)):
+    for name, T in (("dsv2_lite", 8192), ("dsv2_lite_cap", 8192), ("dsv3", 16384), ("qwen3_int4", 4096)):
         sp = S.SPECS[name]
         lay = S.make_layer(sp, device="cuda")
         ml = moe_layer(sp, lay, layout)

@@ -26,9 +26,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
 
-__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
-__device__ __forceinline__ float to_f32(float v) { return v; }
-
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }  // RNE
@@ -62,7 +59,9 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
 // steps combine each lane with a partner inside its row of 16 (swap neighbours,
 // swap pairs, mirror halves of 8, mirror the row of 16), leaving every row
 // uniform; the four row values are then read into scalars and combined in a
-// fixed order, so every lane gets the same, deterministic result.
+// fixed order, so every lane gets the same, deterministic result.  The _n forms
+// reduce N independent values at once (N tokens per wave), so the N
+// dependency chains interleave and hide each other's latency.
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 constexpr int kDppSwap1 = 0xB1;        // quad_perm [1,0,3,2]
@@ -79,40 +78,6 @@ template <int CTRL> __device__ __forceinline__ float dpp_f32(float x) {
 __device__ __forceinline__ float readlane_f32(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-template <int CTRL> __device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
-  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(x >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)x);
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f32<kDppSwap1>(v));
-  v = fmaxf(v, dpp_f32<kDppSwap2>(v));
-  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp_f32<kDppMirror>(v));
-  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_f32<kDppSwap1>(v);
-  v += dpp_f32<kDppSwap2>(v);
-  v += dpp_f32<kDppHalfMirror>(v);
-  v += dpp_f32<kDppMirror>(v);
-  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
-}
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<kDppSwap1>(v));
-  v = max_u64(v, dpp_u64<kDppSwap2>(v));
-  v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
-  v = max_u64(v, dpp_u64<kDppMirror>(v));
-  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)), max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
-}
-
-// The same reductions for N independent values at once (N tokens per wave):
-// the N dependency chains interleave, hiding each other's latency.
 template <int N> __device__ __forceinline__ void wave_max_n(float (&v)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<kDppSwap1>(v[i]));
@@ -140,21 +105,6 @@ template <int N> __device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
   for (int i = 0; i < N; ++i)
     v[i] = (readlane_f32(v[i], 0) + readlane_f32(v[i], 16)) + (readlane_f32(v[i], 32) + readlane_f32(v[i], 48));
 }
-template <int N> __device__ __forceinline__ void wave_max_u64_n(uint64_t (&v)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = max_u64(v[i], dpp_u64<kDppSwap1>(v[i]));
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = max_u64(v[i], dpp_u64<kDppSwap2>(v[i]));
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = max_u64(v[i], dpp_u64<kDppHalfMirror>(v[i]));
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = max_u64(v[i], dpp_u64<kDppMirror>(v[i]));
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-    v[i] = max_u64(max_u64(readlane_u64(v[i], 0), readlane_u64(v[i], 16)),
-                   max_u64(readlane_u64(v[i], 32), readlane_u64(v[i], 48)));
-}
-
 template <int N> __device__ __forceinline__ void wave_max_u32_n(uint32_t (&v)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = max(v[i], dpp_u32<kDppSwap1>(v[i]));

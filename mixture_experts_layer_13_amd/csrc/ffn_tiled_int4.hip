@@ -1,51 +1,69 @@
-// Tiled (large-M, prefill) expert FFN kernels with INT4 weights for gfx950:
-// nibbles dequantised in registers to bf16 MFMA operands (16x16x32).
+// Tiled (large-M, prefill) expert FFN kernels with INT4 weights for gfx950,
+// on the 32x32x16 bf16 MFMA: nibbles dequantised in registers (times their
+// group scale, rounded once to bf16) right before the MFMAs that use them.
 #include "ffn_common.hpp"
 
 namespace moe {
 
-// Block: 128 rows of one item x 256 weight rows, four waves.  The gathered
-// activation tile goes through double-buffered LDS (every wave needs all 128
-// rows); each wave owns 64 weight rows (four 16-row MFMA fragments) that no
-// other wave reads, so they travel from global memory straight into MFMA
-// operand registers, prefetched one K step ahead.  Per K step a wave issues
-// 8 x 4 MFMA 16x16x32 per 32-wide K slice against 8 LDS fragment reads, half
-// the LDS traffic per MFMA of a 64 x 64 wave tile.
-// Gate/up: wave w's fragments are gate rows n0+32w .. +32 and the up rows of
-// the same channels, so the SwiGLU epilogue stays in registers.
-// Lane K order inside a step: bf16 (64-wide steps) k = kb + 32 s + 8 g + i;
-// INT4 (128-wide steps, one scale group) k = kb + 32 g + 8 s + i, so a lane's
-// 16-byte weight load covers 32 nibbles of one group.
-// K step per weight type and projection (measured: the gate/up kernel, with
-// two weight matrices, runs best with 64-wide steps; the down kernel with
-// 32-wide steps, whose smaller register footprint avoids spills).
-template <typename TW, bool GATEUP> struct Til;
-template <bool G> struct Til<INT4, G> {
-  static constexpr int KSTEP = 128, SUB = 4, BL = 1;   // BL: 16-byte weight loads per fragment per step
-};
-template <typename TW, bool GATEUP, bool TILED>
-__global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void ffn_tiled_kernel(FfnArgs a) {
-  using TT = Til<TW, GATEUP>;
-  constexpr int KSTEP = TT::KSTEP, SUB = TT::SUB, BL = TT::BL;
-  constexpr bool I4 = std::is_same<TW, INT4>::value;
-  constexpr int LDA = KSTEP + 16;         // padded LDS row (bf16 elements)
+// Block: 128 rows of one item x 256 weight rows, four waves, each owning 128
+// rows x 64 weight rows as 4 x 2 tiles of 32 x 32 (the bf16 tiled kernel's
+// structure).  A K step is one 128-wide scale group: the activation tile
+// (128 rows x 128 bf16) goes through double-buffered LDS; each wave's weight
+// rows arrive as two 16-byte loads per lane (32 nibbles each) plus one scale
+// per row, one step ahead.  Lane l (row l % 32 of a tile, h = l / 32) reads
+// quarters 2p + h (p = 0, 1) of the row's 64-byte group; slice s (16 K) of
+// the step takes dword s % 4 of load s / 4, i.e. K = 32 (2 (s / 4) + h) +
+// 8 (s % 4) + i, and the activation fragments are read from LDS in the same
+// order.  Each dequantised 8-value operand feeds four MFMAs (the four 32-row
+// tiles).
+template <bool GATEUP, bool TILED>
+__global__ __launch_bounds__(256, 2) void ffn_tiled_int4_kernel(FfnArgs a) {
+  constexpr int KSTEP = kInt4Group, SUB = KSTEP / 16;
+  constexpr int LDA = KSTEP + 8;          // padded LDS row (bf16 elements), conflict-free operand reads
   constexpr int CPR = KSTEP / 8;          // 16-byte chunks per A row per step
   constexpr int CPT = TBM * CPR / 256;    // A chunks per thread per step
   constexpr int RPT = 256 / CPR;          // row stride between a thread's chunks
-  constexpr int NT = GATEUP ? 128 : 256;  // output channels per block (F, S*FS multiples of 128)
-  __shared__ bf16 As[2][TBM * LDA];
-  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6, g = lane >> 4, c = lane & 15;
-  const int Nr = GATEUP ? a.F : a.d;
-  const int Ns = GATEUP ? a.S * a.FS : a.d;
+  constexpr int NT = GATEUP ? 128 : 256;  // output channels per block
+  constexpr uint32_t cstride = TILED ? 1024u : 64u;  // bytes between the 64-byte groups of a weight row
+  constexpr uint32_t pstride = TILED ? 512u : 32u;   // bytes from quarter h to quarter 2 + h
+  constexpr int NC = GATEUP ? 128 : 256;
+  constexpr int LDH = NC + 8;
+  constexpr int SMEM = 2 * TBM * LDA > TBM * LDH ? 2 * TBM * LDA : TBM * LDH;
+  __shared__ bf16 smem[SMEM];
+  bf16* const As[2] = {smem, smem + TBM * LDA};
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6, h = lane >> 5, c = lane & 31;
   TileInfo ti;
   if (!tile_of(a, NT, ti)) return;
   const int e = ti.e, row0 = ti.row0, mrows = ti.mrows, n0 = ti.n0;
   const bool shared = ti.shared;
   const int Kfull = GATEUP ? a.d : (shared ? a.S * a.FS : a.F);
   const int Kseg = GATEUP ? a.d : (shared ? a.FS : a.F);
+  const int Kb = Kseg / 2;                 // packed bytes per weight row
+  const int G = Kseg / kInt4Group;         // scale groups per weight row
 
+  // weight tile nt of this wave: 32 rows from rb; byte offset of this lane's quarter h,
+  // and of its row's scales
+  const char* bmat[2];
+  const uint16_t* smat[2];
+  if (GATEUP) {
+    bmat[0] = (const char*)(shared ? a.shg : expert_mat<INT4>(a.wg, e, a.F, a.d));
+    bmat[1] = (const char*)(shared ? a.shu : expert_mat<INT4>(a.wu, e, a.F, a.d));
+    smat[0] = (const uint16_t*)(shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d));
+    smat[1] = (const uint16_t*)(shared ? a.shsu : expert_scales(a.su, e, a.F, a.d));
+  } else {
+    bmat[0] = bmat[1] = (const char*)(shared ? a.shd : expert_mat<INT4>(a.wd, e, a.d, Kseg));
+    smat[0] = smat[1] = (const uint16_t*)(shared ? a.shsd : expert_scales(a.sd, e, a.d, Kseg));
+  }
+  uint32_t boff[2], soff[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    // a last down block may be half past d: its surplus tiles re-read the last 32 rows, results unused
+    const int rb = GATEUP ? n0 + 32 * w : min(n0 + 64 * w + 32 * nt, a.d - 32);
+    const int row = rb + c;
+    boff[nt] = TILED ? (uint32_t)(row & ~15) * Kb + 256 * h + 16 * (row & 15) : (uint32_t)row * Kb + 16 * h;
+    soff[nt] = (uint32_t)row * G * 2u;
+  }
   // activation chunk sources: rows (tid / CPR) + RPT q, 16-byte chunk tid % CPR
-  // (64-bit addresses: x and h may exceed 4 GiB)
   const int ch = tid % CPR;
   const char* aptr[CPT];
 #pragma unroll
@@ -59,50 +77,24 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
       aptr[q] = (const char*)(shared ? a.hsh : a.h) + ((size_t)(row0 + r) * Kfull + ch * 8) * 2;
     }
   }
-  // weight fragment f of this wave: byte offset of its lane's bytes inside one
-  // of two block-uniform matrices (gate / up, or down; the shared down
-  // projection adds a block-uniform slab offset per K step), in the row or the
-  // tiled weight layout (16-row x 64-byte fragments stored lane-major)
-  const char* bmat[2];
-  const uint16_t* smat[2];
-  uint32_t boff[4], soff[4];
-  if (GATEUP) {
-    bmat[0] = (const char*)(shared ? a.shg : expert_mat<TW>(a.wg, e, a.F, a.d));
-    bmat[1] = (const char*)(shared ? a.shu : expert_mat<TW>(a.wu, e, a.F, a.d));
-    smat[0] = (const uint16_t*)(shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d));
-    smat[1] = (const uint16_t*)(shared ? a.shsu : expert_scales(a.su, e, a.F, a.d));
-  } else {
-    bmat[0] = bmat[1] = (const char*)(shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, Kseg));
-    smat[0] = smat[1] = (const uint16_t*)(shared ? a.shsd : expert_scales(a.sd, e, a.d, Kseg));
-  }
-  const int Kb = row_bytes<TW>(Kseg);
-  constexpr uint32_t cstride = TILED ? 1024u : 64u;  // bytes between the 64-byte chunks of a row
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    // first row of the fragment's 16-row group (a last down block may be half
-    // past d: its surplus fragments re-read the last group, results unused)
-    const int row16 = GATEUP ? n0 + 32 * w + 16 * (f & 1) : min(n0 + 64 * w + 16 * f, a.d - 16);
-    boff[f] = TILED ? (uint32_t)row16 * Kb + 256 * g + 16 * c : (uint32_t)(row16 + c) * Kb + 16 * g;
-    soff[f] = I4 ? (uint32_t)(row16 + c) * (Kseg / kInt4Group) * 2u : 0u;
-  }
-  // byte offset of K step kt inside the weight matrix (slab plus row chunk), and scale index
+  // byte offset of K step kt inside the weight matrix (shared down slab plus group), and its scale index
   auto woff = [&](int kt, int* so) -> size_t {
     const int k0 = kt * KSTEP;
     const int slab = (!GATEUP && shared) ? k0 / Kseg : 0;
-    const int kk = k0 - slab * Kseg;
-    *so = I4 ? slab * a.d * (Kseg / kInt4Group) + kk / kInt4Group : 0;
-    return (size_t)slab * a.d * Kb + (size_t)(row_bytes<TW>(kk) / 64) * cstride;
+    const int kg = (k0 - slab * Kseg) / kInt4Group;
+    *so = slab * a.d * G + kg;
+    return (size_t)slab * a.d * Kb + (size_t)kg * cstride;
   };
 
-  f32x4 acc[8][4];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
 
   u32x4 ar[CPT];
-  u32x4 bcur[4][BL], bnext[4][BL];
-  float scur[4], snext[4];
+  u32x4 b0q[2][2], b1q[2][2];
+  float s0q[2], s1q[2];
   const int nkt = Kfull / KSTEP;
 
   auto load_a = [&](int kt) {
@@ -114,114 +106,92 @@ __global__ __launch_bounds__(256, (std::is_same<TW, INT4>::value ? 1 : 2)) void 
     for (int q = 0; q < CPT; ++q)
       *reinterpret_cast<u32x4*>(&dst[(tid / CPR + RPT * q) * LDA + ch * 8]) = ar[q];
   };
-  auto load_b = [&](u32x4 (&bq)[4][BL], float (&bs)[4], int kt) {
+  auto load_b = [&](u32x4 (&bq)[2][2], float (&bs)[2], int kt) {
     int so;
     const size_t o = woff(kt, &so);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const char* m = bmat[GATEUP ? (f >> 1) : 0] + o;
-      if constexpr (I4) {
-        bq[f][0] = ld16_at(m, boff[f]);
-        const char* sm = (const char*)(smat[GATEUP ? (f >> 1) : 0] + so);
-        bs[f] = bf16_bits_to_f32(*(const uint16_t*)(sm + soff[f]));
-      } else {
+    for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-        for (int s = 0; s < BL; ++s) bq[f][s] = ld16_at(m + cstride * s, boff[f]);
-        bs[f] = 1.f;
-      }
+      for (int p = 0; p < 2; ++p) bq[nt][p] = ld16_at(bmat[nt] + o + p * pstride, boff[nt]);
+      bs[nt] = bf16_bits_to_f32(*(const uint16_t*)((const char*)(smat[nt] + so) + soff[nt]));
     }
   };
-
-  // one K step: SUB slices of 32; the activation fragment of the next m is
-  // read from LDS before the four MFMAs of the current one are issued
-  auto compute = [&](const bf16* A, const u32x4 (&bq)[4][BL], const float (&bs)[4]) {
+  auto compute = [&](const bf16* A, const u32x4 (&bq)[2][2], const float (&bs)[2]) {
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
-      u32x4 bf[4];
+      const int col = 32 * (2 * (s >> 2) + h) + 8 * (s & 3);
+      u32x4 af[4], bf[2];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if constexpr (I4) bf[f] = int4x8_to_bf16_scaled(bq[f][0][s], bs[f]);
-        else bf[f] = bq[f][s];
-      }
-      const int col = I4 ? (32 * g + 8 * s) : (32 * s + 8 * g);
-      u32x4 af = *reinterpret_cast<const u32x4*>(&A[c * LDA + col]);
+      for (int mt = 0; mt < 4; ++mt) af[mt] = *reinterpret_cast<const u32x4*>(&A[(32 * mt + c) * LDA + col]);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        u32x4 an = af;
-        if (m + 1 < 8) an = *reinterpret_cast<const u32x4*>(&A[(16 * (m + 1) + c) * LDA + col]);
+      for (int nt = 0; nt < 2; ++nt) bf[nt] = int4x8_to_bf16_scaled(bq[nt][s >> 2][s & 3], bs[nt]);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) acc[m][f] = mma_bf16(af, bf[f], acc[m][f]);
-        af = an;
-      }
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma32_bf16(af[mt], bf[nt], acc[mt][nt]);
     }
   };
 
-  // two-step ping-pong without branches: step kt computes from (As[kt & 1],
-  // register set kt & 1) while step kt + 1 loads into the other pair; past the
-  // last step the prefetch repeats step nkt - 1 (harmless, never used)
-  u32x4 b1q[4][BL];
-  float s1q[4];
+  // two-step ping-pong without branches (as in the bf16 tiled kernel)
+  load_b(b0q, s0q, 0);  // weights first: they do not wait for the row -> token lookup
   load_a(0);
-  load_b(bcur, scur, 0);
   store_a(As[0]);
   __syncthreads();
   int kt = 0;
-  // the scheduling barriers keep the next step's loads ahead of this step's
-  // MFMAs (left alone, the scheduler sinks them next to their first use)
   for (; kt + 2 <= nkt; kt += 2) {
     load_a(min(kt + 1, nkt - 1));
     load_b(b1q, s1q, min(kt + 1, nkt - 1));
     __builtin_amdgcn_sched_barrier(0);
-    compute(As[0], bcur, scur);
+    compute(As[0], b0q, s0q);
     __builtin_amdgcn_sched_barrier(0);
     store_a(As[1]);
     __syncthreads();
     load_a(min(kt + 2, nkt - 1));
-    load_b(bcur, scur, min(kt + 2, nkt - 1));
+    load_b(b0q, s0q, min(kt + 2, nkt - 1));
     __builtin_amdgcn_sched_barrier(0);
     compute(As[1], b1q, s1q);
     __builtin_amdgcn_sched_barrier(0);
     store_a(As[0]);
     __syncthreads();
   }
-  if (kt < nkt) compute(As[0], bcur, scur);
-  (void)bnext;
-  (void)snext;
+  if (kt < nkt) compute(As[0], b0q, s0q);
 
+  // epilogue through LDS (as in the bf16 tiled kernel)
+  __syncthreads();
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * m + 4 * g + i;
-      if (r >= mrows) continue;
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
       if (GATEUP) {
-        bf16* hout = (bf16*)(shared ? a.hsh : a.h);
-        const int ld = shared ? Ns : Nr;
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const float hv = silu(acc[m][f][i]) * acc[m][f + 2][i];
-          hout[(size_t)(row0 + r) * ld + n0 + 32 * w + 16 * f + c] = (bf16)hv;
-        }
+        smem[r * LDH + 32 * w + c] = (bf16)(silu(acc[mt][0][i]) * acc[mt][1][i]);
       } else {
-        bf16* yout = (bf16*)(shared ? a.ysh : a.y);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const int col = n0 + 64 * w + 16 * f + c;
-          if (col < a.d) yout[(size_t)(row0 + r) * a.d + col] = (bf16)acc[m][f][i];
-        }
+        for (int nt = 0; nt < 2; ++nt) smem[r * LDH + 64 * w + 32 * nt + c] = (bf16)acc[mt][nt][i];
       }
     }
+  }
+  __syncthreads();
+  bf16* const out = (bf16*)(GATEUP ? (shared ? a.hsh : a.h) : (shared ? a.ysh : a.y));
+  const int ld = GATEUP ? (shared ? a.S * a.FS : a.F) : a.d;
+  const int ncols = GATEUP ? ld : a.d;
+  constexpr int CK = NC / 8;
+#pragma unroll
+  for (int q = 0; q < TBM * CK / 256; ++q) {
+    const int idx = tid + 256 * q, r = idx / CK, ck = idx % CK, col = n0 + 8 * ck;
+    if (r < mrows && col < ncols)
+      st16(out + (size_t)(row0 + r) * ld + col, *reinterpret_cast<const u32x4*>(&smem[r * LDH + 8 * ck]));
   }
 }
 
 // ------------------------------------------------------------------ launch
 void launch_tiled_int4(bool gateup, const FfnArgs& a, int grid, hipStream_t s) {
   if (gateup) {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled_kernel<INT4, true, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled_kernel<INT4, true, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled_int4_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((ffn_tiled_int4_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
   } else {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled_kernel<INT4, false, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled_kernel<INT4, false, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled_int4_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((ffn_tiled_int4_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
   }
 }
 

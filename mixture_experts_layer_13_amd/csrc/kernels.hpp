@@ -10,7 +10,6 @@ enum { kF32 = 0, kBF16 = 1, kINT4 = 2 };
 enum { kScoreSoftmax = 0, kScoreSigmoid = 1 };
 
 constexpr int kSingleMaxPairs = 8192;   // T*k handled by the single-block route+permute
-constexpr int kDecodeRows = 64;         // rows per item in the streaming (small-M) expert kernels
 constexpr int kPrefillRows = 128;       // rows per item in the tiled (large-M) expert kernels
 
 struct RouteArgs {
