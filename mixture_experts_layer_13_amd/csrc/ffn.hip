@@ -100,9 +100,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const TA* __restrict__ y, 
 static int ffn_grid(const FfnArgs& a, int nt_routed, int nt_shared) {
   return a.items_max * nt_routed + (a.S > 0 ? a.sh_items * nt_shared : 0);
 }
-// tiled kernels: one block per tile slot, rounded up to whole rounds of the 8 XCDs
-static int ffn_grid_xcd(const FfnArgs& a, int nt_routed, int nt_shared) {
-  return (ffn_grid(a, nt_routed, nt_shared) + 7) / 8 * 8;
+// tiled kernels: 8 XCD chunks of equal work, each given enough blocks for its
+// largest possible tile count (blocks past a chunk's end return at once)
+static int ffn_grid_xcd(const FfnArgs& a, bool gateup, int nt_routed, int nt_shared) {
+  if (ffn_grid(a, nt_routed, nt_shared) == 0) return 0;
+  int64_t wr, ws;
+  tile_work(gateup, a.F, a.S, a.FS, wr, ws);
+  return 8 * tiled_blocks_per_xcd((int64_t)a.items_max * nt_routed, a.S > 0 ? (int64_t)a.sh_items * nt_shared : 0,
+                                  wr, ws);
 }
 
 hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s) {
@@ -111,7 +116,7 @@ hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipSt
     if (grid == 0) return hipSuccess;
     launch_stream_ffn(true, wdt, a, grid, s);
   } else {
-    const int grid = ffn_grid_xcd(a, a.F / 128, a.S * a.FS / 128);
+    const int grid = ffn_grid_xcd(a, true, a.F / 128, a.S * a.FS / 128);
     if (grid == 0) return hipSuccess;
     if (wdt == kBF16) launch_tiled_bf16(true, a, grid, s);
     else launch_tiled_int4(true, a, grid, s);
@@ -126,7 +131,7 @@ hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStre
     if (grid == 0) return hipSuccess;
     launch_stream_ffn(false, wdt, a, grid, s);
   } else {
-    const int grid = ffn_grid_xcd(a, (a.d + 255) / 256, (a.d + 255) / 256);
+    const int grid = ffn_grid_xcd(a, false, (a.d + 255) / 256, (a.d + 255) / 256);
     if (grid == 0) return hipSuccess;
     if (wdt == kBF16) launch_tiled_bf16(false, a, grid, s);
     else launch_tiled_int4(false, a, grid, s);

@@ -75,8 +75,24 @@ constexpr int TBM = 128;
 // (expert-major, so one expert's tiles are adjacent) times N blocks of NT
 // output channels, then the shared-expert tiles.  Blocks are dispatched
 // round-robin over the 8 XCDs, so XCD x = blockIdx % 8 takes the x-th of 8
-// contiguous, equal chunks of the list: the tiles of an expert then run
-// together on one XCD and share their weight and activation K slabs in its L2.
+// contiguous chunks of the list: the tiles of an expert then run together on
+// one XCD and share their weight and activation K slabs in its L2.  The chunks
+// hold equal work, a tile weighing its K length: a shared down tile runs over
+// the S shared experts' concatenated K, S FS against F for a routed one.
+// tile_work() gives the two weights; the grid (tiled_blocks_per_xcd) covers
+// the largest chunk any routing can produce.
+__host__ __device__ inline void tile_work(bool gateup, int F, int S, int FS, int64_t& wr, int64_t& ws) {
+  wr = gateup ? 1 : F;
+  ws = gateup ? 1 : (int64_t)S * FS;
+}
+// Tiles per chunk are at most (chunk work + 1) / (lightest tile) + 1; with at
+// most Wmax work in all, one more block per XCD of slack.
+__host__ __device__ inline int tiled_blocks_per_xcd(int64_t routed_tiles_max, int64_t shared_tiles, int64_t wr,
+                                                    int64_t ws) {
+  const int64_t wmin = shared_tiles > 0 && ws < wr ? ws : wr;
+  const int64_t wmax = routed_tiles_max * wr + shared_tiles * ws;
+  return (int)((wmax / 8 + 1 + wmin - 1) / wmin + 2);
+}
 struct TileInfo {
   int e, row0, mrows, n0;
   bool shared;
@@ -86,9 +102,18 @@ __device__ __forceinline__ bool tile_of(const FfnArgs& a, int NT, TileInfo& t) {
   const int Nr = gu ? a.F : a.d, Ns = gu ? a.S * a.FS : a.d;
   const int nbr = (Nr + NT - 1) / NT, nbs = (Ns + NT - 1) / NT;
   const int routed_tiles = *a.n_items * nbr;
-  const int total = routed_tiles + (a.S > 0 ? a.sh_items * nbs : 0);
+  const int shared_tiles = a.S > 0 ? a.sh_items * nbs : 0;
+  int64_t wr, ws;
+  tile_work(gu, a.F, a.S, a.FS, wr, ws);
+  const int64_t W = routed_tiles * wr + shared_tiles * ws;
+  // first tile whose starting work is at least W x / 8
+  auto first_tile = [&](int x) -> int {
+    const int64_t target = W * x / 8;
+    if (target <= routed_tiles * wr) return (int)((target + wr - 1) / wr);
+    return routed_tiles + (int)((target - routed_tiles * wr + ws - 1) / ws);
+  };
   const int xcd = blockIdx.x & 7;
-  const int lo = (int)((int64_t)total * xcd / 8), hi = (int)((int64_t)total * (xcd + 1) / 8);
+  const int lo = first_tile(xcd), hi = first_tile(xcd + 1);
   const int tile = lo + (int)(blockIdx.x >> 3);
   if (tile >= hi) return false;
   int nb;

@@ -18,7 +18,7 @@ namespace moe {
 // Gate/up: wave w's two tiles are gate rows n0 + 32w .. +31 and the up rows of
 // the same channels, so the SwiGLU epilogue stays in registers.
 template <bool GATEUP> struct Til32 {
-  static constexpr int KSTEP = GATEUP ? 64 : 32;
+  static constexpr int KSTEP = 64;
 };
 
 template <bool GATEUP, bool TILED>
