@@ -46,7 +46,7 @@ struct Plan {
   int mode, bm;
   int64_t items_max;
   int sh_items;
-  size_t o_part, o_hist, o_counts, o_off, o_rowtok, o_slot, o_items, o_nitems, o_h, o_hsh, o_y, o_ysh, total;
+  size_t o_part, o_arrived, o_hist, o_counts, o_off, o_rowtok, o_slot, o_items, o_nitems, o_h, o_hsh, o_y, o_ysh, total;
 };
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -142,6 +142,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     return at;
   };
   q.o_part = take(q.single ? (size_t)q.KS * q.T * q.E * 4 : 0);
+  q.o_arrived = take(4);
   q.o_hist = take(q.single ? 0 : (size_t)q.n_rt * q.E * 4);
   q.o_counts = take((size_t)q.E * 4);
   q.o_off = take((size_t)(q.E + 1) * 4);
@@ -265,14 +266,18 @@ FfnArgs ffn_args(const Plan& p, void* ws, const void* x, const int32_t* row_toke
   return a;
 }
 
+// decode sizes: the many-block route with the one-wave permutation
+bool small_pairs(const Plan& p) { return (int64_t)p.T * p.k <= kSmallMaxPairs; }
+
 // router (logits, scores, top-k, gates) for the planned mode
 moe_status enqueue_route(const Plan& p, const void* x, const void* wr, const RouteArgs& ra, void* ws, hipStream_t s) {
   moe_status st;
   if (p.single) {
     float* part = at<float>(ws, p.o_part);
-    if ((st = hip_ok(launch_router_partial(p.act, x, wr, p.T, p.d, p.E, p.kchunk, p.KS, part, s), "router")))
+    if ((st = hip_ok(launch_router_partial(p.act, x, wr, p.T, p.d, p.E, p.kchunk, p.KS, part, nullptr, s), "router")))
       return st;
     PermArgs none{};
+    if (small_pairs(p)) return hip_ok(launch_route_small(part, p.KS, ra, nullptr, none, 1, 0, nullptr, s), "route");
     return hip_ok(launch_route_permute_single(part, p.KS, ra, nullptr, none, 1, 0, s), "route");
   }
   return hip_ok(launch_router_fused(p.act, x, wr, ra, p.rt, at<int32_t>(ws, p.o_hist), s), "router");
@@ -344,6 +349,7 @@ moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* cou
   PermArgs pa = perm_args(p, ws, counts, offsets, row_token, slot_row, drop_mask);
   if (p.single) {
     RouteArgs ra = route_args(p, nullptr, nullptr, nullptr, nullptr, nullptr);
+    if (small_pairs(p)) return hip_ok(launch_route_small(nullptr, 0, ra, topk_idx, pa, 0, 1, nullptr, s), "permute");
     return hip_ok(launch_route_permute_single(nullptr, 0, ra, topk_idx, pa, 0, 1, s), "permute");
   }
   int32_t* hist = at<int32_t>(ws, p.o_hist);
@@ -411,10 +417,16 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   mark(0, nl, s);
   if (p.single) {
     float* part = at<float>(ws, p.o_part);
-    if ((st = hip_ok(launch_router_partial(p.act, x, w_router, p.T, p.d, p.E, p.kchunk, p.KS, part, s), "router")))
+    const bool small = small_pairs(p);
+    int32_t* arrived = at<int32_t>(ws, p.o_arrived);
+    if ((st = hip_ok(launch_router_partial(p.act, x, w_router, p.T, p.d, p.E, p.kchunk, p.KS, part,
+                                           small ? arrived : nullptr, s),
+                     "router")))
       return st;
     mark(1, nl, s);
-    if ((st = hip_ok(launch_route_permute_single(part, p.KS, ra, nullptr, pa, 1, 1, s), "route/permute"))) return st;
+    if (small) st = hip_ok(launch_route_small(part, p.KS, ra, nullptr, pa, 1, 1, arrived, s), "route/permute");
+    else st = hip_ok(launch_route_permute_single(part, p.KS, ra, nullptr, pa, 1, 1, s), "route/permute");
+    if (st) return st;
   } else {
     int32_t* hist = at<int32_t>(ws, p.o_hist);
     if ((st = hip_ok(launch_router_fused(p.act, x, w_router, ra, p.rt, hist, s), "router"))) return st;

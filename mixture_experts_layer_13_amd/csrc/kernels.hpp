@@ -10,6 +10,7 @@ enum { kF32 = 0, kBF16 = 1, kINT4 = 2 };
 enum { kScoreSoftmax = 0, kScoreSigmoid = 1 };
 
 constexpr int kSingleMaxPairs = 8192;   // T*k handled by the single-block route+permute
+constexpr int kSmallMaxPairs = 512;     // T*k handled by the many-block route with a one-wave permute
 constexpr int kPrefillRows = 128;       // rows per item in the tiled (large-M) expert kernels
 
 struct RouteArgs {
@@ -58,7 +59,9 @@ struct FfnArgs {
 };
 
 hipError_t launch_router_partial(int act, const void* x, const void* wr, int T, int d, int E, int kchunk, int KS,
-                                 float* part, hipStream_t s);
+                                 float* part, int32_t* zero, hipStream_t s);
+hipError_t launch_route_small(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
+                              const PermArgs& pa, int do_route, int do_perm, int32_t* arrived, hipStream_t s);
 hipError_t launch_route_permute_single(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
                                        const PermArgs& pa, int do_route, int do_perm, hipStream_t s);
 hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int rt, int32_t* hist,

@@ -259,12 +259,14 @@ __device__ void write_tile_map(const int* kept, const int* off, int E, int bm, i
 // ------------------------------------------------------------------ router GEMM
 // Partial logits part[z][t][e] = sum over the z-th K chunk of x[t,:] . w_router[e,:].
 // grid (ceil(T/16), ceil(E/64), KS), block 256: wave w owns experts
-// blockIdx.y*64 + 16w .. +16 for a 16-token tile.
+// blockIdx.y*64 + 16w .. +16 for a 16-token tile.  `zero` (if set) is the
+// arrival counter of the route launch that follows; the first block clears it.
 template <typename TIN>
 __global__ __launch_bounds__(256) void router_partial_kernel(const TIN* __restrict__ x,
                                                              const TIN* __restrict__ wr, int T, int d, int E,
-                                                             int kchunk, float* __restrict__ part) {
+                                                             int kchunk, float* __restrict__ part, int32_t* zero) {
   constexpr int EPC = Chunk<TIN>::EPC;
+  if (zero && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *zero = 0;
   constexpr int KSTEP = 4 * EPC;
   const int lane = lane_id(), w = threadIdx.x / 64;
   const int e0 = blockIdx.y * 64 + w * 16;
@@ -435,6 +437,134 @@ __global__ __launch_bounds__(1024) void route_permute_single_kernel(const float*
     const int r = rank_pass(e, valid, wcnt, base, E);
     if (i < n) place_pair(pa, i, e, valid, r, off);
   }
+}
+
+// ------------------------------------------------------------------ small-T route + permute
+// Ranks every pair with one wave (no barriers): pair i = 64 j + lane.  One
+// pass in token-major order gives each pair its stable rank inside its expert
+// (lanes holding the same expert found with ballots; a running per-expert
+// count in LDS, bumped by the lowest such lane) and leaves the expert counts;
+// then the capacity rule, the exclusive scan, the tile map and the placement.
+// LDS: base [256], off [257], tmp [512] ints.
+__device__ void permute_one_wave(const PermArgs& p, const int32_t* idx, int* base, int* off, int* tmp) {
+  constexpr int PPL = kSmallMaxPairs / 64;
+  const int lane = lane_id(), n = p.T * p.k, E = p.E;
+  const int nbits = E <= 1 ? 0 : 32 - __clz(E - 1);
+  for (int x = lane; x < 256; x += 64) base[x] = 0;
+  int raw[PPL];
+#pragma unroll
+  for (int j = 0; j < PPL; ++j) {
+    const int i = 64 * j + lane;
+    raw[j] = i < n ? idx[i] : -1;
+  }
+  int ev[PPL], rk[PPL];
+#pragma unroll
+  for (int j = 0; j < PPL; ++j) {
+    ev[j] = -1;
+    rk[j] = 0;
+    if (64 * j >= n) continue;
+    const bool valid = raw[j] >= 0 && raw[j] < E;
+    const int e = valid ? raw[j] : 0;
+    const uint64_t peers = match_peers((uint32_t)e, __ballot(valid), nbits);
+    const int before = __popcll(peers & lanemask_lt());
+    const int b = valid ? base[e] : 0;
+    if (valid && before == 0) base[e] = b + __popcll(peers);
+    ev[j] = valid ? e : -1;
+    rk[j] = b + before;
+  }
+  for (int x = lane; x < E; x += 64) {
+    p.counts[x] = base[x];
+    tmp[x] = p.cap < 0 ? base[x] : min(base[x], p.cap);
+  }
+  const int total = wave_exclusive_scan256(tmp, off, E);
+  if (lane == 0) off[E] = total;
+  for (int x = lane; x <= E; x += 64) p.offsets[x] = off[x];
+  if (p.items) {
+    for (int x = lane; x < E; x += 64) tmp[256 + x] = (tmp[x] + p.bm - 1) / p.bm;
+    const int nit = wave_exclusive_scan256(tmp + 256, tmp, E);  // tmp[e] = first item of expert e
+    if (lane == 0) *p.n_items = nit;
+    for (int x = lane; x < E; x += 64) {
+      const int kept = off[x + 1] - off[x], start = tmp[x];
+      for (int i = 0; i * p.bm < kept; ++i)
+        p.items[start + i] = make_int4(x, off[x] + i * p.bm, min(p.bm, kept - i * p.bm), 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PPL; ++j) {
+    const int i = 64 * j + lane;
+    if (i < n) place_pair(p, i, ev[j], ev[j] >= 0, rk[j], off);
+  }
+}
+
+// For T*k <= kSmallMaxPairs (decode): block b takes tokens tpb*b .. +tpb-1.
+// Its threads add the KS K-chunk partial logits of those tokens (each output's
+// chunks in order by one lane, or split over KG lanes and added in a fixed
+// butterfly), then wave w scores and selects token tpb*b + w.  The permutation
+// needs every token's picks: each block publishes its topk_idx rows (release
+// fence, then one device-scope increment of `arrived`, which the router launch
+// zeroed), and the block that arrives last ranks all pairs with one wave after
+// an acquire fence.  do_route = 0: one block permutes idx_in.
+__global__ __launch_bounds__(256) void route_small_kernel(const float* __restrict__ part, int KS, int tpb,
+                                                          RouteArgs ra, const int32_t* idx_in, PermArgs pa,
+                                                          int do_route, int do_perm, int32_t* arrived) {
+  __shared__ float slog[4 * 256];
+  __shared__ int base[256], off[257], tmp[512];
+  __shared__ int last;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int T = ra.T, E = ra.E;
+  const int32_t* idx = idx_in;
+  if (do_route) {
+    const int t0 = blockIdx.x * tpb, nt = min(tpb, T - t0), nout = nt * E;
+    int KG = 1;
+    while (KG < 64 && 2 * KG * nout <= (int)blockDim.x && 2 * KG <= KS) KG *= 2;
+    const int g = tid % KG, per = (int)blockDim.x / KG;
+    const size_t zs = (size_t)T * E;
+    for (int i = tid / KG; i < ((nout + per - 1) / per) * per; i += per) {
+      const bool ok = i < nout;
+      const size_t src = ok ? (size_t)(t0 + i / E) * E + i % E : 0;
+      float acc = 0.f;
+      for (int z0 = g; z0 < KS; z0 += 8 * KG) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int z = z0 + u * KG;
+          v[u] = (ok && z < KS) ? part[(size_t)z * zs + src] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (z0 + u * KG < KS) acc += v[u];
+      }
+      for (int o = 1; o < KG; o <<= 1) acc += __shfl_xor(acc, o);
+      if (ok && g == 0) slog[i] = acc;
+    }
+    __syncthreads();
+    if (w < nt) {
+      const int t = t0 + w;
+      if (E <= 64) {
+        float lg[1][1];
+        load_logits<1, 1>(lg, slog + w * E, E, E, ra.logit_bias);
+        route_tokens<1, 1>(lg, ra, t, 1, nullptr);
+      } else if (E <= 128) {
+        float lg[1][2];
+        load_logits<1, 2>(lg, slog + w * E, E, E, ra.logit_bias);
+        route_tokens<1, 2>(lg, ra, t, 1, nullptr);
+      } else {
+        float lg[1][4];
+        load_logits<1, 4>(lg, slog + w * E, E, E, ra.logit_bias);
+        route_tokens<1, 4>(lg, ra, t, 1, nullptr);
+      }
+    }
+    if (!do_perm) return;
+    __threadfence();  // release this block's topk_idx rows
+    __syncthreads();
+    if (tid == 0)
+      last = __hip_atomic_fetch_add(arrived, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();  // acquire every block's rows
+    idx = ra.idx;
+  }
+  if (w == 0) permute_one_wave(pa, idx, base, off, tmp);
 }
 
 // ------------------------------------------------------------------ fused router (large T)
@@ -644,14 +774,23 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict
 
 // ------------------------------------------------------------------ host launchers
 hipError_t launch_router_partial(int act, const void* x, const void* wr, int T, int d, int E, int kchunk, int KS,
-                                 float* part, hipStream_t s) {
+                                 float* part, int32_t* zero, hipStream_t s) {
   dim3 grid((T + 15) / 16, (E + 63) / 64, KS);
   if (act == kF32)
     hipLaunchKernelGGL(router_partial_kernel<float>, grid, dim3(256), 0, s, (const float*)x, (const float*)wr, T, d,
-                       E, kchunk, part);
+                       E, kchunk, part, zero);
   else
     hipLaunchKernelGGL(router_partial_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, T, d, E,
-                       kchunk, part);
+                       kchunk, part, zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_small(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
+                              const PermArgs& pa, int do_route, int do_perm, int32_t* arrived, hipStream_t s) {
+  const int tpb = ra.T <= 32 ? 1 : 4;
+  const int grid = do_route ? (ra.T + tpb - 1) / tpb : 1;
+  hipLaunchKernelGGL(route_small_kernel, dim3(grid), dim3(256), 0, s, part, KS, tpb, ra, idx_in, pa, do_route,
+                     do_perm, arrived);
   return hipGetLastError();
 }
 
