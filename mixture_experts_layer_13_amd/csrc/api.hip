@@ -110,9 +110,11 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     q.R = q.cap * q.E < pairs ? q.cap * q.E : pairs;
   }
   q.single = q.T <= kSingleMaxT;
-  // K split of the small-T router so that the single route block reads at most ~32K partial logits
+  // K split of the small-T router: the route launch's blocks read at most kSmallPartials partial
+  // logits each (decode sizes), the single route block ~32K in all (larger T)
   if (q.single && q.T > 0) {
-    int64_t ks = 32768 / ((int64_t)q.T * q.E);
+    int64_t ks = (int64_t)q.T * q.k <= kSmallMaxPairs ? kSmallPartials / ((int64_t)route_small_tpb(q.T) * q.E)
+                                                      : 32768 / ((int64_t)q.T * q.E);
     const int64_t ksmax = q.d / 128;
     ks = ks < 1 ? 1 : (ks > ksmax ? ksmax : ks);
     const int64_t steps = q.d / 128;

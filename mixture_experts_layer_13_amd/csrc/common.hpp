@@ -75,6 +75,19 @@ template <int CTRL> __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
 template <int CTRL> __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele steps inside each
+// 16-lane row (row_shr 1, 2, 4, 8), then each row adds the running total of
+// the rows before it (row_bcast 15 into rows 1 and 3, row_bcast 31 into rows
+// 2 and 3).  Lanes without a source add 0.
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  return v;
+}
 __device__ __forceinline__ float readlane_f32(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }

@@ -16,22 +16,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Eight two's-complement nibbles (element i in bits 4i..4i+3) -> eight exact
-// bf16 values.  Flipping bit 3 of each nibble gives q + 8; OR-ing that into
-// the mantissa of 2^23 and subtracting 2^23 + 8 yields q exactly in fp32.
-__device__ __forceinline__ u32x4 int4x8_to_bf16(uint32_t w) {
-  const uint32_t x = w ^ 0x88888888u;
+// Eight nibbles q (two's complement, element i at bits 4i..4i+3) to eight
+// bf16 values 136 + q, exactly: with u = q + 8 in 0..15, bf16 bits 0x4300 | u
+// are 128 + u (exponent 2^7, mantissa step 1).  Per pair one byte permute
+// puts byte p of the nibbles (low nibble) and of the nibbles >> 4 (high
+// nibble) into the two halves, one and-or keeps the nibbles and sets 0x43.
+// A product with x then carries 136 x extra, taken off as 136 sum(x).
+__device__ __forceinline__ u32x4 int4x8_to_bf16_off136(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u, xs = x >> 4;
   u32x4 r;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const float lo = __uint_as_float(0x4B000000u | ((x >> (8 * p)) & 0xFu)) - 8388616.0f;
-    const float hi = __uint_as_float(0x4B000000u | ((x >> (8 * p + 4)) & 0xFu)) - 8388616.0f;
-    r[p] = pack_bf16x2(lo, hi);
+    const uint32_t sel = (uint32_t)p | (0x0Cu << 8) | ((uint32_t)(4 + p) << 16) | (0x0Cu << 24);
+    r[p] = (__builtin_amdgcn_perm(xs, x, sel) & 0x000F000Fu) | 0x43004300u;
   }
   return r;
 }
 
-// Same, times the group scale, rounded once to bf16 (operand of the tiled kernels).
+// Eight two's-complement nibbles (element i in bits 4i..4i+3) times the group
+// scale, rounded once to bf16 (operand of the tiled kernels): flipping bit 3 of
+// a nibble gives q + 8; OR-ing that into the mantissa of 2^23 and subtracting
+// 2^23 + 8 yields q exactly in fp32.
 __device__ __forceinline__ u32x4 int4x8_to_bf16_scaled(uint32_t w, float sc) {
   const uint32_t x = w ^ 0x88888888u;
   u32x4 r;

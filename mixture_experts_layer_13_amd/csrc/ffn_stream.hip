@@ -68,13 +68,27 @@ template <> __device__ __forceinline__ f32x4 dstep<float>(const u32x4 (&av)[1], 
 template <> __device__ __forceinline__ f32x4 dstep<bf16>(const u32x4 (&av)[1], u32x4 b, float, f32x4 acc) {
   return mma_bf16(av[0], b, acc);
 }
-template <> __device__ __forceinline__ f32x4 dstep<INT4>(const u32x4 (&av)[4], u32x4 b, float sc, f32x4 acc) {
-  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+// INT4: one 128-K scale group.  The MFMAs take the nibbles as 136 + q (see
+// int4x8_to_bf16_off136) on an accumulator that starts at -136 sum(x) over the
+// group (xn), so they leave sum(q x); the group scale is applied once.
+__device__ __forceinline__ f32x4 dstep_int4(const u32x4 (&av)[4], u32x4 b, float sc, f32x4 xn, f32x4 acc) {
+  f32x4 t = xn;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) t = mma_bf16(av[s], int4x8_to_bf16(b[s]), t);
+  for (int s = 0; s < 4; ++s) t = mma_bf16(av[s], int4x8_to_bf16_off136(b[s]), t);
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[i], acc[i]);
   return acc;
+}
+// -136 times the sum over the group of each activation row, in the MFMA
+// output layout (an all-ones weight operand: every column holds the row sum).
+__device__ __forceinline__ f32x4 int4_group_offset(const u32x4 (&av)[4]) {
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) x = mma_bf16(av[s], ones, x);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] *= -136.f;
+  return x;
 }
 
 // GATEUP: h[row][n] = silu(A Wg^T) * (A Wu^T); else y[row][n] = A Wd^T.
@@ -193,11 +207,21 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (st + u < s1) {
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
+          if constexpr (std::is_same<TW, INT4>::value) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              if (mt < nmt) acc[m][mt] = dstep<TW>(av[mt][u], bq[m][u], sc[m][u], acc[m][mt]);
+              if (mt < nmt) {
+                const f32x4 xn = int4_group_offset(av[mt][u]);  // shared by gate and up
+#pragma unroll
+                for (int m = 0; m < NM; ++m) acc[m][mt] = dstep_int4(av[mt][u], bq[m][u], sc[m][u], xn, acc[m][mt]);
+              }
+          } else {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (mt < nmt) acc[m][mt] = dstep<TW>(av[mt][u], bq[m][u], sc[m][u], acc[m][mt]);
+          }
         }
       }
     }

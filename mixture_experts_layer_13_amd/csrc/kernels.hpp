@@ -11,6 +11,11 @@ enum { kScoreSoftmax = 0, kScoreSigmoid = 1 };
 
 constexpr int kSingleMaxPairs = 8192;   // T*k handled by the single-block route+permute
 constexpr int kSmallMaxPairs = 512;     // T*k handled by the many-block route with a one-wave permute
+// tokens per block of the small-T route launch: one block for a single token
+// (no hand-off), else a block per token up to 32 tokens, then 4 per block
+inline int route_small_tpb(int T) { return T <= 32 ? 1 : 4; }
+// partial logits one small-T route block sums (K chunks x experts x its tokens)
+constexpr int kSmallPartials = 8192;
 constexpr int kPrefillRows = 128;       // rows per item in the tiled (large-M) expert kernels
 
 struct RouteArgs {

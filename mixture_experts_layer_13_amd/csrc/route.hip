@@ -219,13 +219,8 @@ __device__ __forceinline__ int wave_exclusive_scan256(const int* in, int* out, i
     const int p = 4 * lane + i;
     v[i] = p < n ? in[p] : 0;
   }
-  int local = v[0] + v[1] + v[2] + v[3];
-  int incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int local = v[0] + v[1] + v[2] + v[3];
+  const int incl = wave_incl_scan_i32(local);
   run = incl - local;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -233,7 +228,7 @@ __device__ __forceinline__ int wave_exclusive_scan256(const int* in, int* out, i
     if (p < n) out[p] = run;
     run += v[i];
   }
-  return __shfl(incl, 63);
+  return __builtin_amdgcn_readlane(incl, 63);
 }
 
 // Tile map for the grouped expert GEMMs: one item {expert, first row, rows}
@@ -280,15 +275,15 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const TIN* __restri
   const TIN* pb = wr + (size_t)eb * d + g * EPC;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   int kk = k0;
-  for (; kk + 4 * KSTEP <= k1; kk += 4 * KSTEP) {
-    u32x4 a[4], b[4];
+  for (; kk + 8 * KSTEP <= k1; kk += 8 * KSTEP) {  // 8 loads per operand in flight
+    u32x4 a[8], b[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       a[u] = ld16(pa + kk + u * KSTEP);
       b[u] = ld16(pb + kk + u * KSTEP);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc = Chunk<TIN>::mma(a[u], b[u], acc);
+    for (int u = 0; u < 8; ++u) acc = Chunk<TIN>::mma(a[u], b[u], acc);
   }
   for (; kk < k1; kk += KSTEP) acc = Chunk<TIN>::mma(ld16(pa + kk), ld16(pb + kk), acc);
   const int e = e0 + (lane & 15);
@@ -446,17 +441,19 @@ __global__ __launch_bounds__(1024) void route_permute_single_kernel(const float*
 // count in LDS, bumped by the lowest such lane) and leaves the expert counts;
 // then the capacity rule, the exclusive scan, the tile map and the placement.
 // LDS: base [256], off [257], tmp [512] ints.
-__device__ void permute_one_wave(const PermArgs& p, const int32_t* idx, int* base, int* off, int* tmp) {
+// The picks come from idx (global, [T][k]) or, when idx is null, from sel (LDS).
+__device__ void permute_one_wave(const PermArgs& p, const int32_t* idx, const uint16_t* sel, int* base, int* off,
+                                 int* tmp) {
   constexpr int PPL = kSmallMaxPairs / 64;
   const int lane = lane_id(), n = p.T * p.k, E = p.E;
   const int nbits = E <= 1 ? 0 : 32 - __clz(E - 1);
-  for (int x = lane; x < 256; x += 64) base[x] = 0;
   int raw[PPL];
 #pragma unroll
   for (int j = 0; j < PPL; ++j) {
     const int i = 64 * j + lane;
-    raw[j] = i < n ? idx[i] : -1;
+    raw[j] = i >= n ? -1 : (idx ? idx[i] : (int)sel[i]);
   }
+  for (int x = lane; x < 256; x += 64) base[x] = 0;
   int ev[PPL], rk[PPL];
 #pragma unroll
   for (int j = 0; j < PPL; ++j) {
@@ -499,72 +496,95 @@ __device__ void permute_one_wave(const PermArgs& p, const int32_t* idx, int* bas
 // For T*k <= kSmallMaxPairs (decode): block b takes tokens tpb*b .. +tpb-1.
 // Its threads add the KS K-chunk partial logits of those tokens (each output's
 // chunks in order by one lane, or split over KG lanes and added in a fixed
-// butterfly), then wave w scores and selects token tpb*b + w.  The permutation
-// needs every token's picks: each block publishes its topk_idx rows (release
-// fence, then one device-scope increment of `arrived`, which the router launch
-// zeroed), and the block that arrives last ranks all pairs with one wave after
-// an acquire fence.  do_route = 0: one block permutes idx_in.
+// butterfly); the biases are fetched at entry, so the selection does not wait
+// for them.  One block (tpb >= T): its waves score and select the tokens in
+// groups of four, the picks stay in LDS and wave 0 ranks them.  Several
+// blocks: wave w scores and selects token tpb*b + w; each block publishes its
+// topk_idx rows (release fence, then one device-scope increment of
+// `arrived`, which the router launch zeroed), and the block that arrives last
+// ranks all pairs with one wave after an acquire fence.  do_route = 0: one
+// block permutes idx_in.
 __global__ __launch_bounds__(256) void route_small_kernel(const float* __restrict__ part, int KS, int tpb,
                                                           RouteArgs ra, const int32_t* idx_in, PermArgs pa,
                                                           int do_route, int do_perm, int32_t* arrived) {
   __shared__ float slog[4 * 256];
+  __shared__ float sbias[256], ssel[256];
+  __shared__ uint16_t sel[kSmallMaxPairs];
   __shared__ int base[256], off[257], tmp[512];
   __shared__ int last;
   const int tid = threadIdx.x, w = tid >> 6;
   const int T = ra.T, E = ra.E;
-  const int32_t* idx = idx_in;
-  if (do_route) {
-    const int t0 = blockIdx.x * tpb, nt = min(tpb, T - t0), nout = nt * E;
-    int KG = 1;
-    while (KG < 64 && 2 * KG * nout <= (int)blockDim.x && 2 * KG <= KS) KG *= 2;
-    const int g = tid % KG, per = (int)blockDim.x / KG;
-    const size_t zs = (size_t)T * E;
-    for (int i = tid / KG; i < ((nout + per - 1) / per) * per; i += per) {
-      const bool ok = i < nout;
-      const size_t src = ok ? (size_t)(t0 + i / E) * E + i % E : 0;
-      float acc = 0.f;
-      for (int z0 = g; z0 < KS; z0 += 8 * KG) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int z = z0 + u * KG;
-          v[u] = (ok && z < KS) ? part[(size_t)z * zs + src] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (z0 + u * KG < KS) acc += v[u];
-      }
-      for (int o = 1; o < KG; o <<= 1) acc += __shfl_xor(acc, o);
-      if (ok && g == 0) slog[i] = acc;
-    }
-    __syncthreads();
-    if (w < nt) {
-      const int t = t0 + w;
-      if (E <= 64) {
-        float lg[1][1];
-        load_logits<1, 1>(lg, slog + w * E, E, E, ra.logit_bias);
-        route_tokens<1, 1>(lg, ra, t, 1, nullptr);
-      } else if (E <= 128) {
-        float lg[1][2];
-        load_logits<1, 2>(lg, slog + w * E, E, E, ra.logit_bias);
-        route_tokens<1, 2>(lg, ra, t, 1, nullptr);
-      } else {
-        float lg[1][4];
-        load_logits<1, 4>(lg, slog + w * E, E, E, ra.logit_bias);
-        route_tokens<1, 4>(lg, ra, t, 1, nullptr);
-      }
-    }
-    if (!do_perm) return;
-    __threadfence();  // release this block's topk_idx rows
-    __syncthreads();
-    if (tid == 0)
-      last = __hip_atomic_fetch_add(arrived, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
-    __syncthreads();
-    if (!last) return;
-    __threadfence();  // acquire every block's rows
-    idx = ra.idx;
+  if (!do_route) {
+    if (w == 0) permute_one_wave(pa, idx_in, nullptr, base, off, tmp);
+    return;
   }
-  if (w == 0) permute_one_wave(pa, idx, base, off, tmp);
+  const float lb = (ra.logit_bias && tid < E) ? ra.logit_bias[tid] : 0.f;
+  const float sb = (ra.select_bias && tid < E) ? ra.select_bias[tid] : 0.f;
+  const int t0 = blockIdx.x * tpb, nt = min(tpb, T - t0), nout = nt * E;
+  int KG = 1;
+  while (KG < 64 && 2 * KG * nout <= (int)blockDim.x && 2 * KG <= KS) KG *= 2;
+  const int g = tid % KG, per = (int)blockDim.x / KG;
+  const size_t zs = (size_t)T * E;
+  for (int i = tid / KG; i < ((nout + per - 1) / per) * per; i += per) {
+    const bool ok = i < nout;
+    const size_t src = ok ? (size_t)(t0 + i / E) * E + i % E : 0;
+    float acc = 0.f;
+    for (int z0 = g; z0 < KS; z0 += 32 * KG) {  // up to 32 loads in flight per lane
+      float v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int z = z0 + u * KG;
+        v[u] = (ok && z < KS) ? part[(size_t)z * zs + src] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (z0 + u * KG < KS) acc += v[u];
+    }
+    for (int o = 1; o < KG; o <<= 1) acc += __shfl_xor(acc, o);
+    if (ok && g == 0) slog[i] = acc;
+  }
+  if (tid < E) {
+    sbias[tid] = lb;
+    ssel[tid] = sb;
+  }
+  __syncthreads();
+  RouteArgs rl = ra;
+  if (ra.select_bias) rl.select_bias = ssel;
+  const float* bias = ra.logit_bias ? sbias : nullptr;
+  if (nt == T) {  // one block: picks stay in LDS
+    if (E <= 64) route_rows<1>(slog, E, T, 0, rl, bias, sel, w, 4);
+    else if (E <= 128) route_rows<2>(slog, E, T, 0, rl, bias, sel, w, 4);
+    else route_rows<4>(slog, E, T, 0, rl, bias, sel, w, 4);
+    if (!do_perm) return;
+    __syncthreads();
+    if (w == 0) permute_one_wave(pa, nullptr, sel, base, off, tmp);
+    return;
+  }
+  if (w < nt) {
+    const int t = t0 + w;
+    if (E <= 64) {
+      float lg[1][1];
+      load_logits<1, 1>(lg, slog + w * E, E, E, bias);
+      route_tokens<1, 1>(lg, rl, t, 1, nullptr);
+    } else if (E <= 128) {
+      float lg[1][2];
+      load_logits<1, 2>(lg, slog + w * E, E, E, bias);
+      route_tokens<1, 2>(lg, rl, t, 1, nullptr);
+    } else {
+      float lg[1][4];
+      load_logits<1, 4>(lg, slog + w * E, E, E, bias);
+      route_tokens<1, 4>(lg, rl, t, 1, nullptr);
+    }
+  }
+  if (!do_perm) return;
+  __threadfence();  // release this block's topk_idx rows
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(arrived, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();  // acquire every block's rows
+  if (w == 0) permute_one_wave(pa, ra.idx, nullptr, base, off, tmp);
 }
 
 // ------------------------------------------------------------------ fused router (large T)
@@ -787,7 +807,7 @@ hipError_t launch_router_partial(int act, const void* x, const void* wr, int T, 
 
 hipError_t launch_route_small(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
                               const PermArgs& pa, int do_route, int do_perm, int32_t* arrived, hipStream_t s) {
-  const int tpb = ra.T <= 32 ? 1 : 4;
+  const int tpb = route_small_tpb(ra.T);
   const int grid = do_route ? (ra.T + tpb - 1) / tpb : 1;
   hipLaunchKernelGGL(route_small_kernel, dim3(grid), dim3(256), 0, s, part, KS, tpb, ra, idx_in, pa, do_route,
                      do_perm, arrived);
