@@ -112,7 +112,8 @@ static int ffn_grid_xcd(const FfnArgs& a, bool gateup, int nt_routed, int nt_sha
 
 hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s) {
   if (mode == 0) {
-    const int grid = ffn_grid(a, a.F / 16, a.S * a.FS / 16);
+    const int cpb = stream_channels_per_block(true, wdt);
+    const int grid = ffn_grid(a, a.F / cpb, a.S * a.FS / cpb);
     if (grid == 0) return hipSuccess;
     launch_stream_ffn(true, wdt, a, grid, s);
   } else {
@@ -127,7 +128,8 @@ hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipSt
 
 hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s) {
   if (mode == 0) {
-    const int grid = ffn_grid(a, a.d / 64, a.d / 64);
+    const int cpb = stream_channels_per_block(false, wdt);
+    const int grid = ffn_grid(a, a.d / cpb, a.d / cpb);
     if (grid == 0) return hipSuccess;
     launch_stream_ffn(false, wdt, a, grid, s);
   } else {

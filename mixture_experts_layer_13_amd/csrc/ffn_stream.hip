@@ -33,6 +33,7 @@ template <> struct Dec<INT4> {
 struct WRow {
   const uint8_t* p;  // chunk 0 of this lane
   int shift;         // log2 of the bytes from chunk j to chunk j + 1
+  __device__ WRow() {}
   __device__ WRow(const void* m, int n, int Kb, int g, int tiled) {
     const int c = n & 15;
     p = (const uint8_t*)m + (tiled ? (size_t)(n - c) * Kb + 256 * g + 16 * c : (size_t)n * Kb + 16 * g);
@@ -48,6 +49,7 @@ struct WRow {
 template <typename TW> struct BRow {
   WRow w;
   const uint16_t* s;  // INT4 scales of the row (bf16, one per 128-K group)
+  __device__ BRow() {}
   __device__ BRow(const void* m, int n, int K, int g, const void* sc, int tiled)
       : w(m, n, row_bytes<TW>(K), g, tiled),
         s(std::is_same<TW, INT4>::value ? (const uint16_t*)sc + (size_t)n * (K / kInt4Group) : nullptr) {}
@@ -91,23 +93,31 @@ __device__ __forceinline__ f32x4 int4_group_offset(const u32x4 (&av)[4]) {
   return x;
 }
 
+// 16-channel tiles per wave of the streaming kernels (channels per block:
+// gate/up 16 NT, down 64 NT; the host grid uses the same numbers)
+template <typename TW> constexpr int stream_tiles() { return std::is_same<TW, INT4>::value ? 2 : 1; }
+int stream_channels_per_block(bool gateup, int wdt) { return (gateup ? 16 : 64) * (wdt == kINT4 ? 2 : 1); }
+
 // GATEUP: h[row][n] = silu(A Wg^T) * (A Wu^T); else y[row][n] = A Wd^T.
-// A block owns one item (<= 16 * MT rows of one expert).  Gate/up (K = d,
-// large): the four waves split K into quarters for the same 16 channels and
-// add their partial sums in LDS in wave order.  Down (K = ffn): each wave owns
-// 16 channels over the whole K, so a block covers 64.  Steps are unrolled U
-// deep so each lane keeps U weight loads per matrix in flight.
+// A block owns one item (<= 16 * MT rows of one expert).  A wave covers NT
+// tiles of 16 channels (INT4: two, so one set of activation registers feeds
+// twice the weight bytes in flight; else one).  Gate/up (K = d, large): the
+// four waves split K into quarters for the same channels and add their
+// partial sums in LDS in wave order.  Down (K = ffn): each wave owns its
+// channels over the whole K, so a block covers 4 NT tiles.  Steps are unrolled
+// U deep so each lane keeps U weight loads per matrix and tile in flight.
 // grid: items_max * (N / channels per block) routed blocks, then the shared blocks.
 template <typename TW, bool GATEUP, int MT>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   using D = Dec<TW>;
   using TA = typename D::TA;
   constexpr int NM = GATEUP ? 2 : 1;
+  constexpr int NT = stream_tiles<TW>();
   constexpr int KSPLIT = GATEUP ? 4 : 1;         // waves sharing one channel block
-  constexpr int CPB = 16 * (4 / KSPLIT);          // channels per block
+  constexpr int CPB = 16 * NT * (4 / KSPLIT);     // channels per block
   constexpr int U = (std::is_same<TW, INT4>::value || MT == 4) ? 4 : 8;
   constexpr int AL = D::AL, KSTEP = D::KSTEP;
-  __shared__ f32x4 red[KSPLIT > 1 ? 3 : 1][NM][MT][64];
+  __shared__ f32x4 red[KSPLIT > 1 ? 3 : 1][NM][NT][MT][64];
   const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
 
   const int Nr = GATEUP ? a.F : a.d;
@@ -133,18 +143,23 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   }
   const int nmt = (mrows + 15) / 16;
   const int kpart = KSPLIT > 1 ? w : 0;
-  const int n = nb * CPB + (KSPLIT > 1 ? 0 : 16 * w) + c;
+  const int n0 = nb * CPB + (KSPLIT > 1 ? 0 : 16 * NT * w) + c;  // channel of tile j: n0 + 16 j
 
   const int K = GATEUP ? a.d : (shared ? a.FS : a.F);  // K of one segment
   const int nseg = (!GATEUP && shared) ? a.S : 1;
   // weight rows first: their loads do not wait for the activation row lookup
-  BRow<TW> b0 = GATEUP ? BRow<TW>(shared ? a.shg : expert_mat<TW>(a.wg, e, a.F, a.d), n, K, g,
-                                  shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d), a.wtiled)
-                       : BRow<TW>(shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, K), n, K, g,
-                                  shared ? a.shsd : expert_scales(a.sd, e, a.d, K), a.wtiled);
-  BRow<TW> b1 = GATEUP ? BRow<TW>(shared ? a.shu : expert_mat<TW>(a.wu, e, a.F, a.d), n, K, g,
-                                  shared ? a.shsu : expert_scales(a.su, e, a.F, a.d), a.wtiled)
-                       : b0;
+  const void* m0 = GATEUP ? (shared ? a.shg : expert_mat<TW>(a.wg, e, a.F, a.d))
+                          : (shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, K));
+  const void* s0 = GATEUP ? (shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d))
+                          : (shared ? a.shsd : expert_scales(a.sd, e, a.d, K));
+  const void* m1 = GATEUP ? (shared ? a.shu : expert_mat<TW>(a.wu, e, a.F, a.d)) : m0;
+  const void* s1p = GATEUP ? (shared ? a.shsu : expert_scales(a.su, e, a.F, a.d)) : s0;
+  BRow<TW> b0[NT], b1[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    b0[j] = BRow<TW>(m0, n0 + 16 * j, K, g, s0, a.wtiled);
+    b1[j] = BRow<TW>(m1, n0 + 16 * j, K, g, s1p, a.wtiled);
+  }
 
   // activation rows (clamped into the item so every load is in bounds)
   const TA* arow[MT];
@@ -161,34 +176,41 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
     }
   }
 
-  f32x4 acc[NM][MT];
+  f32x4 acc[NM][NT][MT];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[m][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[m][j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int seg = 0; seg < nseg; ++seg) {
     if (seg > 0) {  // next slab of the shared down projection: [S][d][FS]
-      b0 = BRow<TW>(expert_mat<TW>(a.shd, seg, a.d, K), n, K, g, expert_scales(a.shsd, seg, a.d, K), a.wtiled);
-      b1 = b0;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        b0[j] = b1[j] = BRow<TW>(expert_mat<TW>(a.shd, seg, a.d, K), n0 + 16 * j, K, g,
+                                 expert_scales(a.shsd, seg, a.d, K), a.wtiled);
     }
     const int aoff = seg * K;
     const int nsteps = K / KSTEP;
     const int s0 = kpart * nsteps / KSPLIT, s1 = (kpart + 1) * nsteps / KSPLIT;
 #pragma unroll 1  // U-deep unroll inside already; a further unroll only costs occupancy
     for (int st = s0; st < s1; st += U) {
-      u32x4 bq[NM][U];
-      float sc[NM][U];
+      u32x4 bq[NM][NT][U];
+      float sc[NM][NT][U];
       u32x4 av[MT][U][AL];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (st + u < s1) {
           const int kb = (st + u) * KSTEP;
-          bq[0][u] = b0.load(kb);
-          sc[0][u] = b0.scale(kb);
-          if (NM > 1) {
-            bq[NM - 1][u] = b1.load(kb);
-            sc[NM - 1][u] = b1.scale(kb);
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            bq[0][j][u] = b0[j].load(kb);
+            sc[0][j][u] = b0[j].scale(kb);
+            if (NM > 1) {
+              bq[NM - 1][j][u] = b1[j].load(kb);
+              sc[NM - 1][j][u] = b1[j].scale(kb);
+            }
           }
         }
       }
@@ -213,14 +235,19 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
               if (mt < nmt) {
                 const f32x4 xn = int4_group_offset(av[mt][u]);  // shared by gate and up
 #pragma unroll
-                for (int m = 0; m < NM; ++m) acc[m][mt] = dstep_int4(av[mt][u], bq[m][u], sc[m][u], xn, acc[m][mt]);
+                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                  for (int j = 0; j < NT; ++j)
+                    acc[m][j][mt] = dstep_int4(av[mt][u], bq[m][j][u], sc[m][j][u], xn, acc[m][j][mt]);
               }
           } else {
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-                if (mt < nmt) acc[m][mt] = dstep<TW>(av[mt][u], bq[m][u], sc[m][u], acc[m][mt]);
+              for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                  if (mt < nmt) acc[m][j][mt] = dstep<TW>(av[mt][u], bq[m][j][u], sc[m][j][u], acc[m][j][mt]);
           }
         }
       }
@@ -233,16 +260,21 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          if (mt < nmt) red[w - 1][m][mt][lane] = acc[m][mt];
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (mt < nmt) red[w - 1][m][j][mt][lane] = acc[m][j][mt];
     }
     __syncthreads();
     if (w != 0) return;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (mt < nmt) acc[m][mt] = ((acc[m][mt] + red[0][m][mt][lane]) + red[1][m][mt][lane]) + red[2][m][mt][lane];
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          if (mt < nmt)
+            acc[m][j][mt] = ((acc[m][j][mt] + red[0][m][j][mt][lane]) + red[1][m][j][mt][lane]) + red[2][m][j][mt][lane];
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -251,13 +283,17 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * mt + 4 * g + i;
       if (r >= mrows) continue;
-      if (GATEUP) {
-        const float hv = silu(acc[0][mt][i]) * acc[NM - 1][mt][i];
-        TA* hout = (TA*)(shared ? a.hsh : a.h);
-        hout[(size_t)(row0 + r) * (shared ? Ns : Nr) + n] = from_f32<TA>(hv);
-      } else {
-        TA* yout = (TA*)(shared ? a.ysh : a.y);
-        yout[(size_t)(row0 + r) * a.d + n] = from_f32<TA>(acc[0][mt][i]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int n = n0 + 16 * j;
+        if (GATEUP) {
+          const float hv = silu(acc[0][j][mt][i]) * acc[NM - 1][j][mt][i];
+          TA* hout = (TA*)(shared ? a.hsh : a.h);
+          hout[(size_t)(row0 + r) * (shared ? Ns : Nr) + n] = from_f32<TA>(hv);
+        } else {
+          TA* yout = (TA*)(shared ? a.ysh : a.y);
+          yout[(size_t)(row0 + r) * a.d + n] = from_f32<TA>(acc[0][j][mt][i]);
+        }
       }
     }
   }

@@ -78,6 +78,7 @@ hipError_t launch_tile_map(const int32_t* offsets, int E, int R, int bm, int4* i
 
 // per-family launchers of the expert FFN kernels (grid from launch_ffn_*)
 void launch_stream_ffn(bool gateup, int wdt, const FfnArgs& a, int grid, hipStream_t s);
+int stream_channels_per_block(bool gateup, int wdt);
 void launch_tiled_bf16(bool gateup, const FfnArgs& a, int grid, hipStream_t s);
 void launch_tiled_int4(bool gateup, const FfnArgs& a, int grid, hipStream_t s);
 
