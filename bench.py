@@ -344,10 +344,10 @@ def time_layer(ml, x, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / steps
-    per = {n: 0.0 for n in LAUNCHES}
+    per = {n: 0.0 for n in LAUNCHES[:nl]}
     for i in range(steps):
         b = i * (nl + 1)
-        for j, n in enumerate(LAUNCHES):
+        for j, n in enumerate(LAUNCHES[:nl]):
             per[n] += ev.ms(b + j, b + j + 1) / steps
     ev.close()
     return ms_step, per, outs, nl, wall

@@ -115,6 +115,31 @@ def test_capacity_zero_leaves_shared_experts():
     assert ref["drop"].all()
 
 
+def test_capacity_zero_at_decode_sizes():
+    """Decode sizes fuse the combine into the down launch.  C = 0 drops every
+    routed pair: with a shared expert the output is the shared FFN (checked
+    against the oracle); with none, no down block is live and the output must
+    still be written, as exact zeros."""
+    sp = S.SPECS["dsv2_lite"].replace(name="capzero_dec", cfg_id=18, d=512, E=16, ffn=256, ffn_shared=256,
+                                      capacity=(0, 1))
+    lay = S.make_layer(sp, device="cuda")
+    ml = layer_of(sp, lay)
+    for T in (1, 40):
+        x = S.make_tokens(sp, T, device="cuda", seed=T)
+        out, idx, gates, drop, ref = run_and_check(sp, lay, ml, x)
+        assert drop.cpu().numpy().all()
+    sp0 = S.SPECS["olmoe"].replace(name="capzero_dec_noshared", cfg_id=19, d=512, E=16, ffn=256, capacity=(0, 1))
+    lay0 = S.make_layer(sp0, device="cuda")
+    ml0 = layer_of(sp0, lay0)
+    for T in (1, 40):
+        x = S.make_tokens(sp0, T, device="cuda", seed=T)
+        o = torch.full((T, sp0.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        out, idx, gates, drop = ml0.forward(x, o)
+        torch.cuda.synchronize()
+        assert drop.cpu().numpy().all()
+        assert (out.float() == 0).all()
+
+
 def test_extreme_skew_single_hot_set():
     """Every token identical: every token picks the same k experts, so k experts
     each get all T rows (many tiles per expert) and the rest get none."""
