@@ -440,12 +440,14 @@ __global__ __launch_bounds__(1024) void route_permute_single_kernel(const float*
 // (lanes holding the same expert found with ballots; a running per-expert
 // count in LDS, bumped by the lowest such lane) and leaves the expert counts;
 // then the capacity rule, the exclusive scan, the tile map and the placement.
-// LDS: base [256], off [257], tmp [512] ints.
-// The picks come from idx (global, [T][k]) or, when idx is null, from sel (LDS).
+// The picks are loaded first (all at once); the per-pair loops are kept
+// rolled and run over the occupied 64-pair chunks only, so the code a launch
+// executes once stays short.  LDS: base [256], off [257], tmp [512],
+// pr [kSmallMaxPairs] (rank * 256 + expert, or -1).
 __device__ void permute_one_wave(const PermArgs& p, const int32_t* idx, const uint16_t* sel, int* base, int* off,
-                                 int* tmp) {
+                                 int* tmp, int* pr) {
   constexpr int PPL = kSmallMaxPairs / 64;
-  const int lane = lane_id(), n = p.T * p.k, E = p.E;
+  const int lane = lane_id(), n = p.T * p.k, E = p.E, nch = (n + 63) / 64;
   const int nbits = E <= 1 ? 0 : 32 - __clz(E - 1);
   int raw[PPL];
 #pragma unroll
@@ -453,21 +455,21 @@ __device__ void permute_one_wave(const PermArgs& p, const int32_t* idx, const ui
     const int i = 64 * j + lane;
     raw[j] = i >= n ? -1 : (idx ? idx[i] : (int)sel[i]);
   }
-  for (int x = lane; x < 256; x += 64) base[x] = 0;
-  int ev[PPL], rk[PPL];
 #pragma unroll
-  for (int j = 0; j < PPL; ++j) {
-    ev[j] = -1;
-    rk[j] = 0;
-    if (64 * j >= n) continue;
-    const bool valid = raw[j] >= 0 && raw[j] < E;
-    const int e = valid ? raw[j] : 0;
+  for (int j = 0; j < PPL; ++j)
+    if (64 * j + lane < n) pr[64 * j + lane] = raw[j];
+  for (int x = lane; x < 256; x += 64) base[x] = 0;
+#pragma unroll 1
+  for (int j = 0; j < nch; ++j) {
+    const int i = 64 * j + lane;
+    const int r = i < n ? pr[i] : -1;
+    const bool valid = r >= 0 && r < E;
+    const int e = valid ? r : 0;
     const uint64_t peers = match_peers((uint32_t)e, __ballot(valid), nbits);
     const int before = __popcll(peers & lanemask_lt());
     const int b = valid ? base[e] : 0;
     if (valid && before == 0) base[e] = b + __popcll(peers);
-    ev[j] = valid ? e : -1;
-    rk[j] = b + before;
+    if (i < n) pr[i] = valid ? (b + before) * 256 + e : -1;
   }
   for (int x = lane; x < E; x += 64) {
     p.counts[x] = base[x];
@@ -480,111 +482,104 @@ __device__ void permute_one_wave(const PermArgs& p, const int32_t* idx, const ui
     for (int x = lane; x < E; x += 64) tmp[256 + x] = (tmp[x] + p.bm - 1) / p.bm;
     const int nit = wave_exclusive_scan256(tmp + 256, tmp, E);  // tmp[e] = first item of expert e
     if (lane == 0) *p.n_items = nit;
+#pragma unroll 1
     for (int x = lane; x < E; x += 64) {
       const int kept = off[x + 1] - off[x], start = tmp[x];
+#pragma unroll 1
       for (int i = 0; i * p.bm < kept; ++i)
         p.items[start + i] = make_int4(x, off[x] + i * p.bm, min(p.bm, kept - i * p.bm), 0);
     }
   }
-#pragma unroll
-  for (int j = 0; j < PPL; ++j) {
+#pragma unroll 1
+  for (int j = 0; j < nch; ++j) {
     const int i = 64 * j + lane;
-    if (i < n) place_pair(p, i, ev[j], ev[j] >= 0, rk[j], off);
+    if (i < n) {
+      const int v = pr[i];
+      place_pair(p, i, v & 255, v >= 0, v >> 8, off);
+    }
   }
 }
 
-// For T*k <= kSmallMaxPairs (decode): block b takes tokens tpb*b .. +tpb-1.
+// For T*k <= kSmallMaxPairs (decode), E <= 64 EPL: block b takes tokens tpb*b .. +tpb-1.
 // Its threads add the KS K-chunk partial logits of those tokens (each output's
 // chunks in order by one lane, or split over KG lanes and added in a fixed
 // butterfly); the biases are fetched at entry, so the selection does not wait
-// for them.  One block (tpb >= T): its waves score and select the tokens in
-// groups of four, the picks stay in LDS and wave 0 ranks them.  Several
-// blocks: wave w scores and selects token tpb*b + w; each block publishes its
-// topk_idx rows (release fence, then one device-scope increment of
-// `arrived`, which the router launch zeroed), and the block that arrives last
-// ranks all pairs with one wave after an acquire fence.  do_route = 0: one
-// block permutes idx_in.
+// for them.  Wave w scores and selects token tpb*b + w.  One block (T = 1):
+// the picks stay in LDS and wave 0 ranks them.  Several blocks: each block
+// publishes its topk_idx rows (release fence, then one device-scope increment
+// of `arrived`, which the router launch zeroed), and the block that arrives
+// last ranks all pairs with one wave after an acquire fence.  do_route = 0:
+// one block permutes idx_in.
+template <int EPL>
 __global__ __launch_bounds__(256) void route_small_kernel(const float* __restrict__ part, int KS, int tpb,
                                                           RouteArgs ra, const int32_t* idx_in, PermArgs pa,
                                                           int do_route, int do_perm, int32_t* arrived) {
   __shared__ float slog[4 * 256];
   __shared__ float sbias[256], ssel[256];
   __shared__ uint16_t sel[kSmallMaxPairs];
-  __shared__ int base[256], off[257], tmp[512];
+  __shared__ int base[256], off[257], tmp[512], pr[kSmallMaxPairs];
   __shared__ int last;
   const int tid = threadIdx.x, w = tid >> 6;
   const int T = ra.T, E = ra.E;
-  if (!do_route) {
-    if (w == 0) permute_one_wave(pa, idx_in, nullptr, base, off, tmp);
-    return;
-  }
-  const float lb = (ra.logit_bias && tid < E) ? ra.logit_bias[tid] : 0.f;
-  const float sb = (ra.select_bias && tid < E) ? ra.select_bias[tid] : 0.f;
-  const int t0 = blockIdx.x * tpb, nt = min(tpb, T - t0), nout = nt * E;
-  int KG = 1;
-  while (KG < 64 && 2 * KG * nout <= (int)blockDim.x && 2 * KG <= KS) KG *= 2;
-  const int g = tid % KG, per = (int)blockDim.x / KG;
-  const size_t zs = (size_t)T * E;
-  for (int i = tid / KG; i < ((nout + per - 1) / per) * per; i += per) {
-    const bool ok = i < nout;
-    const size_t src = ok ? (size_t)(t0 + i / E) * E + i % E : 0;
-    float acc = 0.f;
-    for (int z0 = g; z0 < KS; z0 += 32 * KG) {  // up to 32 loads in flight per lane
-      float v[32];
+  const int32_t* pidx = idx_in;  // where the permutation reads the picks
+  const uint16_t* psel = nullptr;
+  if (do_route) {
+    const float lb = (ra.logit_bias && tid < E) ? ra.logit_bias[tid] : 0.f;
+    const float sb = (ra.select_bias && tid < E) ? ra.select_bias[tid] : 0.f;
+    const int t0 = blockIdx.x * tpb, nt = min(tpb, T - t0), nout = nt * E;
+    int KG = 1;
+    while (KG < 64 && 2 * KG * nout <= (int)blockDim.x && 2 * KG <= KS) KG *= 2;
+    const int g = tid % KG, per = (int)blockDim.x / KG;
+    const size_t zs = (size_t)T * E;
+    for (int i = tid / KG; i < ((nout + per - 1) / per) * per; i += per) {
+      const bool ok = i < nout;
+      const size_t src = ok ? (size_t)(t0 + i / E) * E + i % E : 0;
+      float acc = 0.f;
+      for (int z0 = g; z0 < KS; z0 += 32 * KG) {  // up to 32 loads in flight per lane
+        float v[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int z = z0 + u * KG;
-        v[u] = (ok && z < KS) ? part[(size_t)z * zs + src] : 0.f;
+        for (int u = 0; u < 32; ++u) {
+          const int z = z0 + u * KG;
+          v[u] = (ok && z < KS) ? part[(size_t)z * zs + src] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+          if (z0 + u * KG < KS) acc += v[u];
       }
-#pragma unroll
-      for (int u = 0; u < 32; ++u)
-        if (z0 + u * KG < KS) acc += v[u];
+      for (int o = 1; o < KG; o <<= 1) acc += __shfl_xor(acc, o);
+      if (ok && g == 0) slog[i] = acc;
     }
-    for (int o = 1; o < KG; o <<= 1) acc += __shfl_xor(acc, o);
-    if (ok && g == 0) slog[i] = acc;
-  }
-  if (tid < E) {
-    sbias[tid] = lb;
-    ssel[tid] = sb;
-  }
-  __syncthreads();
-  RouteArgs rl = ra;
-  if (ra.select_bias) rl.select_bias = ssel;
-  const float* bias = ra.logit_bias ? sbias : nullptr;
-  if (nt == T) {  // one block: picks stay in LDS
-    if (E <= 64) route_rows<1>(slog, E, T, 0, rl, bias, sel, w, 4);
-    else if (E <= 128) route_rows<2>(slog, E, T, 0, rl, bias, sel, w, 4);
-    else route_rows<4>(slog, E, T, 0, rl, bias, sel, w, 4);
-    if (!do_perm) return;
+    if (tid < E) {
+      sbias[tid] = lb;
+      ssel[tid] = sb;
+    }
     __syncthreads();
-    if (w == 0) permute_one_wave(pa, nullptr, sel, base, off, tmp);
-    return;
-  }
-  if (w < nt) {
-    const int t = t0 + w;
-    if (E <= 64) {
-      float lg[1][1];
-      load_logits<1, 1>(lg, slog + w * E, E, E, bias);
-      route_tokens<1, 1>(lg, rl, t, 1, nullptr);
-    } else if (E <= 128) {
-      float lg[1][2];
-      load_logits<1, 2>(lg, slog + w * E, E, E, bias);
-      route_tokens<1, 2>(lg, rl, t, 1, nullptr);
+    RouteArgs rl = ra;
+    if (ra.select_bias) rl.select_bias = ssel;
+    const float* bias = ra.logit_bias ? sbias : nullptr;
+    const bool one = nt == T;  // a single block (T = 1): the picks stay in LDS, no hand-off
+    if (w < nt) {
+      float lg[1][EPL];
+      load_logits<1, EPL>(lg, slog + w * E, E, E, bias);
+      route_tokens<1, EPL>(lg, rl, t0 + w, 1, one ? sel + w * ra.k : nullptr);
+    }
+    if (!do_perm) return;
+    if (one) {
+      __syncthreads();
+      pidx = nullptr;
+      psel = sel;
     } else {
-      float lg[1][4];
-      load_logits<1, 4>(lg, slog + w * E, E, E, bias);
-      route_tokens<1, 4>(lg, rl, t, 1, nullptr);
+      __threadfence();  // release this block's topk_idx rows
+      __syncthreads();
+      if (tid == 0)
+        last = __hip_atomic_fetch_add(arrived, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+      __syncthreads();
+      if (!last) return;
+      __threadfence();  // acquire every block's rows
+      pidx = ra.idx;
     }
   }
-  if (!do_perm) return;
-  __threadfence();  // release this block's topk_idx rows
-  __syncthreads();
-  if (tid == 0)
-    last = __hip_atomic_fetch_add(arrived, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();  // acquire every block's rows
-  if (w == 0) permute_one_wave(pa, ra.idx, nullptr, base, off, tmp);
+  if (w == 0) permute_one_wave(pa, pidx, psel, base, off, tmp, pr);
 }
 
 // ------------------------------------------------------------------ fused router (large T)
@@ -809,8 +804,8 @@ hipError_t launch_route_small(const float* part, int KS, const RouteArgs& ra, co
                               const PermArgs& pa, int do_route, int do_perm, int32_t* arrived, hipStream_t s) {
   const int tpb = route_small_tpb(ra.T);
   const int grid = do_route ? (ra.T + tpb - 1) / tpb : 1;
-  hipLaunchKernelGGL(route_small_kernel, dim3(grid), dim3(256), 0, s, part, KS, tpb, ra, idx_in, pa, do_route,
-                     do_perm, arrived);
+  auto kern = ra.E <= 64 ? route_small_kernel<1> : (ra.E <= 128 ? route_small_kernel<2> : route_small_kernel<4>);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, part, KS, tpb, ra, idx_in, pa, do_route, do_perm, arrived);
   return hipGetLastError();
 }
 
