@@ -211,7 +211,7 @@ def write_traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, c
     print(json.dumps(rec))
 
 
-def cpu_baseline(sp, lay, x, n_tokens):
+def cpu_baseline(sp, lay, x, n_tokens, min_s=10.0):
     import oracle as O
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_harness import ExpertSource, to_f64
@@ -229,13 +229,16 @@ def cpu_baseline(sp, lay, x, n_tokens):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
-    t0 = time.perf_counter()
-    O.moe_layer(xf, wr, host, sp.E, sp.k, score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale,
-                logit_bias=lb, capacity=sp.capacity)
+    # whole runs of the sample until at least `min_s` seconds of host time (at most 20 runs)
+    runs, t0 = 0, time.perf_counter()
+    while runs < 20 and (runs == 0 or time.perf_counter() - t0 < min_s):
+        O.moe_layer(xf, wr, host, sp.E, sp.k, score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale,
+                    logit_bias=lb, capacity=sp.capacity)
+        runs += 1
     dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": runs * n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n_tokens} of the {x.shape[0]} tokens (full FP64 layer on the sample: routing, "
-                      f"all selected expert FFNs from bf16 bit patterns, combine); {dt:.1f} s"}
+                      f"all selected expert FFNs from bf16 bit patterns, combine), {runs} runs in {dt:.1f} s"}
 
 
 def clone_weights(lay):
@@ -297,12 +300,12 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name
 def decode_other(layout):
     """The other decode-sized layers the HBM target covers: Qwen3 INT4 at T=32 (4
     copies of its 0.31 GB of expert weights) and DeepSeek-V3 at T=1 and 16 (2 copies:
-    one token already touches 0.8 GB)."""
+    one token already touches 0.8 GB), plus DeepSeek-V3 T=256 from its token sweep."""
     import torch
 
     import moe_synth as S
     out = {}
-    for name, Ts, copies in (("qwen3_int4", (32,), 4), ("dsv3", (1, 16), 2)):
+    for name, Ts, copies in (("qwen3_int4", (32,), 4), ("dsv3", (1, 16, 256), 2)):
         sp = S.SPECS[name]
         lay = S.make_layer(sp, device="cuda")
         out[name] = decode_sweep(sp, lay, layout, Ts=Ts, replays=100, copies=copies, name=name)
@@ -361,20 +364,24 @@ def prefill_sweep(layout, steps=20, warmup=3):
 
     import moe_synth as S
     res = {}
-    for name, T in (("dsv2_lite", 8192), ("dsv2_lite_cap", 8192), ("dsv3", 16384), ("qwen3_int4", 4096)):
+    # DeepSeek-V3 also at T=4096, the step of its token sweep below the prefill target
+    for name, Ts in (("dsv2_lite", (8192,)), ("dsv2_lite_cap", (8192,)), ("dsv3", (4096, 16384)),
+                     ("qwen3_int4", (4096,))):
         sp = S.SPECS[name]
         lay = S.make_layer(sp, device="cuda")
         ml = moe_layer(sp, lay, layout)
-        x = S.make_tokens(sp, T, device="cuda")
-        ms, per, outs, _, _ = time_layer(ml, x, steps, warmup)
-        w = alg_work(sp, T, outs[1], outs[3])
-        res[f"{name}_T{T}"] = {
-            "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
-            "mfma_frac_layer": round(w["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "mfma_frac_gateup": round(w["gateup_flops"] / (per["gateup"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "per_launch_us": {n: round(v * 1e3, 2) for n, v in per.items()},
-            "kept_pairs": w["kept"], "pairs": T * sp.k}
-        del ml, lay, x, outs
+        for T in Ts:
+            x = S.make_tokens(sp, T, device="cuda")
+            ms, per, outs, _, _ = time_layer(ml, x, steps, warmup)
+            w = alg_work(sp, T, outs[1], outs[3])
+            res[f"{name}_T{T}"] = {
+                "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                "mfma_frac_layer": round(w["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "mfma_frac_gateup": round(w["gateup_flops"] / (per["gateup"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "per_launch_us": {n: round(v * 1e3, 2) for n, v in per.items()},
+                "kept_pairs": w["kept"], "pairs": T * sp.k}
+            del x, outs
+        del ml, lay
         torch.cuda.empty_cache()
     return {"method": f"eager, {steps} timed forwards after {warmup}; useful flops only (dropped pairs and tile "
                       "padding excluded)", "points": res}
@@ -446,7 +453,7 @@ def main():
         line["decode"] = decode_sweep(sp, lay, args.layout)
         line["decode_other"] = decode_other(args.layout)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_tokens=256)
+        line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_tokens=T)  # the whole workload, ~10 s of host time
     if not args.no_prefill:
         del ml, lay, x
         torch.cuda.empty_cache()
