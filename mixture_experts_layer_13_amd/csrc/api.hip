@@ -129,10 +129,11 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   q.n_rt = (q.T + q.rt - 1) / q.rt;
   q.mode = (q.act == MOE_F32 || q.T <= kStreamMaxT) ? 0 : 1;
   // streaming kernels take items of 16 rows (T <= 16: an expert gets each token at most once; or
-  // at most 4 pairs per expert on average, where splitting a hot expert costs less than the
-  // registers of 32-row items) or 32 rows; above 32 a hot expert is split into two items (its
-  // weights are read twice), which costs less than the registers (occupancy) of 64-row items
-  q.bm = q.mode == 1 ? kPrefillRows : ((q.T <= 16 || (int64_t)q.T * q.k <= 4 * (int64_t)q.E) ? 16 : 32);
+  // at most 8 pairs per expert on average, where splitting a hot expert costs less than the
+  // registers of 32-row items: measured on OLMoE T=64, 170 -> 161 us) or 32 rows; above 32 a hot
+  // expert is split into two items (its weights are read twice), which costs less than the
+  // registers (occupancy) of 64-row items
+  q.bm = q.mode == 1 ? kPrefillRows : ((q.T <= 16 || (int64_t)q.T * q.k <= 8 * (int64_t)q.E) ? 16 : 32);
   q.items_max = q.R / q.bm + (q.R < q.E ? q.R : q.E);
   q.sh_items = q.S > 0 ? (q.T + q.bm - 1) / q.bm : 0;
 
