@@ -30,6 +30,13 @@ template <> struct Dec<INT4> {
 //    KB at ((n/16)*(Kb/64) + j)*1024, lane-major: bytes 16*(16g + c).. hold
 //    row 16*(n/16) + c, bytes 16g.. of the chunk, so one wave-wide 16-byte load
 //    of a fragment reads 1 KB of consecutive addresses.
+// Weight bytes are read exactly once per forward: non-temporal 16-byte loads
+// (measured on a plain 2 GiB read: 6.9-7.0 TB/s against 6.1-6.2 TB/s with
+// ordinary loads).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 struct WRow {
   const uint8_t* p;  // chunk 0 of this lane
   int shift;         // log2 of the bytes from chunk j to chunk j + 1
@@ -39,7 +46,7 @@ struct WRow {
     p = (const uint8_t*)m + (tiled ? (size_t)(n - c) * Kb + 256 * g + 16 * c : (size_t)n * Kb + 16 * g);
     shift = tiled ? 10 : 6;
   }
-  __device__ u32x4 chunk(int j) const { return ld16(p + ((uint32_t)j << shift)); }
+  __device__ u32x4 chunk(int j) const { return ld16_stream(p + ((uint32_t)j << shift)); }
 };
 
 // One weight row of a [N][K] matrix as seen by one lane; a step of KSTEP K
