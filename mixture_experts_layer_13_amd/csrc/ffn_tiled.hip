@@ -21,7 +21,9 @@ template <bool GATEUP> struct Til32 {
   static constexpr int KSTEP = 64;
 };
 
-template <bool GATEUP, bool TILED>
+// STREAMW: weights loaded non-temporally (when an expert's weights are read by a
+// single row tile, nothing is lost by not keeping them in L2).
+template <bool GATEUP, bool TILED, bool STREAMW>
 __global__ __launch_bounds__(256, 2) void ffn_tiled32_kernel(FfnArgs a) {
   constexpr int KSTEP = Til32<GATEUP>::KSTEP, SUB = KSTEP / 16;
   constexpr int LDA = KSTEP + 8;          // padded LDS row (bf16 elements)
@@ -107,8 +109,11 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled32_kernel(FfnArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int s = 0; s < SUB; ++s)
-        bq[nt][s] = ld16_at(bmat[nt] + o + (s >> 1) * cstride + (s & 1) * hstride, boff[nt]);
+      for (int s = 0; s < SUB; ++s) {
+        const char* src = bmat[nt] + o + (s >> 1) * cstride + (s & 1) * hstride;
+        if constexpr (STREAMW) bq[nt][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + boff[nt]));
+        else bq[nt][s] = ld16_at(src, boff[nt]);
+      }
   };
   // one K step: SUB slices of 16.  The four activation fragments of slice s + 1
   // are read from LDS while the eight MFMAs of slice s issue: the group
@@ -200,13 +205,19 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled32_kernel(FfnArgs a) {
 }
 
 // ------------------------------------------------------------------ launch
+template <bool GATEUP, bool TILED>
+static void launch_tiled32(const FfnArgs& a, int grid, hipStream_t s) {
+  if (a.wstream) hipLaunchKernelGGL((ffn_tiled32_kernel<GATEUP, TILED, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_tiled32_kernel<GATEUP, TILED, false>), dim3(grid), dim3(256), 0, s, a);
+}
+
 void launch_tiled_bf16(bool gateup, const FfnArgs& a, int grid, hipStream_t s) {
   if (gateup) {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled32_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled32_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.wtiled) launch_tiled32<true, true>(a, grid, s);
+    else launch_tiled32<true, false>(a, grid, s);
   } else {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled32_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled32_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.wtiled) launch_tiled32<false, true>(a, grid, s);
+    else launch_tiled32<false, false>(a, grid, s);
   }
 }
 

@@ -16,7 +16,8 @@ namespace moe {
 // 8 (s % 4) + i, and the activation fragments are read from LDS in the same
 // order.  Each dequantised 8-value operand feeds four MFMAs (the four 32-row
 // tiles).
-template <bool GATEUP, bool TILED>
+// STREAMW: weights loaded non-temporally (each expert's weights read by one row tile).
+template <bool GATEUP, bool TILED, bool STREAMW>
 __global__ __launch_bounds__(256, 2) void ffn_tiled_int4_kernel(FfnArgs a) {
   constexpr int KSTEP = kInt4Group, SUB = KSTEP / 16;
   constexpr int LDA = KSTEP + 8;          // padded LDS row (bf16 elements), conflict-free operand reads
@@ -112,7 +113,11 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_int4_kernel(FfnArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) bq[nt][p] = ld16_at(bmat[nt] + o + p * pstride, boff[nt]);
+      for (int p = 0; p < 2; ++p) {
+        const char* src = bmat[nt] + o + p * pstride;
+        if constexpr (STREAMW) bq[nt][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + boff[nt]));
+        else bq[nt][p] = ld16_at(src, boff[nt]);
+      }
       bs[nt] = bf16_bits_to_f32(*(const uint16_t*)((const char*)(smat[nt] + so) + soff[nt]));
     }
   };
@@ -185,13 +190,19 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_int4_kernel(FfnArgs a) {
 }
 
 // ------------------------------------------------------------------ launch
+template <bool GATEUP, bool TILED>
+static void launch_int4(const FfnArgs& a, int grid, hipStream_t s) {
+  if (a.wstream) hipLaunchKernelGGL((ffn_tiled_int4_kernel<GATEUP, TILED, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_tiled_int4_kernel<GATEUP, TILED, false>), dim3(grid), dim3(256), 0, s, a);
+}
+
 void launch_tiled_int4(bool gateup, const FfnArgs& a, int grid, hipStream_t s) {
   if (gateup) {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled_int4_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled_int4_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.wtiled) launch_int4<true, true>(a, grid, s);
+    else launch_int4<true, false>(a, grid, s);
   } else {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled_int4_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled_int4_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.wtiled) launch_int4<false, true>(a, grid, s);
+    else launch_int4<false, false>(a, grid, s);
   }
 }
 

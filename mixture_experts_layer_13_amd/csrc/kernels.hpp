@@ -55,6 +55,7 @@ struct FfnArgs {
   int sh_items;              // static shared items (ceil(T / bm)) when S > 0
   int bm;
   int wtiled;                // expert weights in the tiled layout (else one K-contiguous row per channel)
+  int wstream;               // tiled kernels: non-temporal weight loads (each expert's weights read by one row tile)
   const void *wg, *wu, *wd, *sg, *su, *sd;         // routed weights / INT4 scales
   const void *shg, *shu, *shd, *shsg, *shsu, *shsd;  // shared weights / INT4 scales
   void* h;                   // [R][F]     act dtype
