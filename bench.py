@@ -262,6 +262,9 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name
     s = torch.cuda.Stream()
     for T in Ts:
         x = S.make_tokens(sp, T, device="cuda")
+        # the weights, their packing and x were made on the default stream: finish them before
+        # anything runs on `s`
+        torch.cuda.synchronize()
         graphs, outs = [], []
         for ml in layers:
             o = (torch.empty((T, sp.d), dtype=ml.act_dtype, device="cuda"),
@@ -269,6 +272,7 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name
                  torch.empty((T, sp.k), dtype=torch.float32, device="cuda"),
                  torch.empty((T, sp.k), dtype=torch.uint8, device="cuda"))
             ml.workspace(ml.cfg_for(T))
+            torch.cuda.synchronize()
             with torch.cuda.stream(s):
                 ml.forward(x, *o)  # eager warm-up on the capture stream
             torch.cuda.synchronize()
