@@ -34,16 +34,16 @@ __device__ __forceinline__ u32x4 int4x8_to_bf16_off136(uint32_t w) {
 }
 
 // Eight two's-complement nibbles (element i in bits 4i..4i+3) times the group
-// scale, rounded once to bf16 (operand of the tiled kernels): flipping bit 3 of
-// a nibble gives q + 8; OR-ing that into the mantissa of 2^23 and subtracting
-// 2^23 + 8 yields q exactly in fp32.
-__device__ __forceinline__ u32x4 int4x8_to_bf16_scaled(uint32_t w, float sc) {
-  const uint32_t x = w ^ 0x88888888u;
+// scale, rounded once to bf16 (operand of the tiled kernels).  sc16 is 16
+// times the scale: v_cvt_off_f32_i4 turns the low 4 bits of its operand into
+// q / 16 exactly, and (q / 16) * (16 s) = q s exactly in fp32 (a 4-bit by
+// 8-bit product), so the only rounding is the final one to bf16.
+__device__ __forceinline__ u32x4 int4x8_to_bf16_scaled(uint32_t w, float sc16) {
   u32x4 r;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const float lo = (__uint_as_float(0x4B000000u | ((x >> (8 * p)) & 0xFu)) - 8388616.0f) * sc;
-    const float hi = (__uint_as_float(0x4B000000u | ((x >> (8 * p + 4)) & 0xFu)) - 8388616.0f) * sc;
+    const float lo = __builtin_amdgcn_cvt_off_f32_i4(w >> (8 * p)) * sc16;
+    const float hi = __builtin_amdgcn_cvt_off_f32_i4(w >> (8 * p + 4)) * sc16;
     r[p] = pack_bf16x2(lo, hi);
   }
   return r;

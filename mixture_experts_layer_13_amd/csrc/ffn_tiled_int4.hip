@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_int4_kernel(FfnArgs a) {
         if constexpr (STREAMW) bq[nt][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + boff[nt]));
         else bq[nt][p] = ld16_at(src, boff[nt]);
       }
-      bs[nt] = bf16_bits_to_f32(*(const uint16_t*)((const char*)(smat[nt] + so) + soff[nt]));
+      bs[nt] = 16.f * bf16_bits_to_f32(*(const uint16_t*)((const char*)(smat[nt] + so) + soff[nt]));  // 16 s
     }
   };
   auto compute = [&](const bf16* A, const u32x4 (&bq)[2][2], const float (&bs)[2]) {
