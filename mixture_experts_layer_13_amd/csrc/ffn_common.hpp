@@ -49,7 +49,10 @@ __device__ __forceinline__ u32x4 int4x8_to_bf16_scaled(uint32_t w, float sc16) {
   return r;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z sigma(z) with the hardware exponential and reciprocal (a few ulp in
+// fp32, far below the bf16 rounding of h; measured -5.5 us on the OLMoE T=4096
+// gate/up epilogue against expf and IEEE division)
+__device__ __forceinline__ float silu(float z) { return z * __frcp_rn(1.0f + __expf(-z)); }
 
 // bytes of one K-contiguous weight row
 template <typename TW> __device__ __forceinline__ constexpr int row_bytes(int K) { return K * (int)sizeof(TW); }
