@@ -122,7 +122,18 @@ __device__ __forceinline__ bool tile_of(const FfnArgs& a, int NT, TileInfo& t) {
   };
   const int xcd = blockIdx.x & 7;
   const int lo = first_tile(xcd), hi = first_tile(xcd + 1);
-  const int tile = lo + (int)(blockIdx.x >> 3);
+  // Dispatch order inside the chunk.  With many N blocks per item (>= 11: the
+  // DeepSeek-V3 layers, DeepSeek-V2-Lite gate/up) blocks take groups of 8
+  // consecutive items N-block major, so the tiles that share a weight slab
+  // start together and find it in L2 (measured: DeepSeek-V3 T=16384 gate/up
+  // 11.36 -> 9.59 ms, down 5.66 -> 4.69 ms); with fewer, item-major order keeps
+  // an item's activation rows in L2 and was 1-2% faster.
+  const int j = (int)(blockIdx.x >> 3);
+  int tile = lo + j;
+  if (nbr >= 11) {
+    const int gsz = 8 * nbr, full = (hi - lo) / gsz * gsz;
+    if (j < full) tile = lo + (j / gsz) * gsz + (j % 8) * nbr + (j % gsz) / 8;
+  }
   if (tile >= hi) return false;
   int nb;
   t.shared = tile >= routed_tiles;
