@@ -123,9 +123,10 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   constexpr int KSPLIT = GATEUP ? 4 : 1;         // waves sharing one channel block
   constexpr int CPB = 16 * NT * (4 / KSPLIT);     // channels per block
   // steps whose loads go out together (per step: weights, scales, then activations, so a step's
-  // MFMAs can start while later steps land).  Measured on decode layers: INT4 1 (its small
-  // register footprint keeps 5 blocks per CU), bf16 16 / 8 / 4 for items of 16 / 32 / 64 rows
-  constexpr int U = std::is_same<TW, INT4>::value ? 1 : (MT == 1 ? 16 : (MT == 2 ? 8 : 4));
+  // MFMAs can start while later steps land).  Measured on decode layers: INT4 gate/up 1 (its
+  // small register footprint keeps 5 blocks per CU), INT4 down 2, bf16 16 / 8 / 4 for items of
+  // 16 / 32 / 64 rows
+  constexpr int U = std::is_same<TW, INT4>::value ? (GATEUP ? 1 : 2) : (MT == 1 ? 16 : (MT == 2 ? 8 : 4));
   constexpr int AL = D::AL, KSTEP = D::KSTEP;
   __shared__ f32x4 red[KSPLIT > 1 ? 3 : 1][NM][NT][MT][64];
   const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
