@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled32_kernel(FfnArgs a) {
   constexpr int NC = GATEUP ? 128 : 256;  // output columns of a block
   constexpr int LDH = NC + 8;             // padded row of the output staging tile
   constexpr int SMEM = 2 * TBM * LDA > TBM * LDH ? 2 * TBM * LDA : TBM * LDH;
+  static_assert(CPT == 4 && RPT == 32, "a thread's activation chunk q must lie in row tile q");
   __shared__ bf16 smem[SMEM];
   bf16* const As[2] = {smem, smem + TBM * LDA};
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6, h = lane >> 5, c = lane & 31;
@@ -85,25 +86,8 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled32_kernel(FfnArgs a) {
     return (size_t)slab * a.d * Kb + (size_t)(kk / 32) * cstride;
   };
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
-
-  u32x4 ar[CPT];
   u32x4 b0q[2][SUB], b1q[2][SUB];
   const int nkt = Kfull / KSTEP;
-
-  auto load_a = [&](int kt) {
-#pragma unroll
-    for (int q = 0; q < CPT; ++q) ar[q] = ld16(aptr[q] + kt * KSTEP * 2);
-  };
-  auto store_a = [&](bf16* dst) {
-#pragma unroll
-    for (int q = 0; q < CPT; ++q)
-      *reinterpret_cast<u32x4*>(&dst[(tid / CPR + RPT * q) * LDA + ch * 8]) = ar[q];
-  };
   auto load_b = [&](u32x4 (&bq)[2][SUB], int kt) {
     const size_t o = woff(kt);
 #pragma unroll
@@ -115,93 +99,122 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled32_kernel(FfnArgs a) {
         else bq[nt][s] = ld16_at(src, boff[nt]);
       }
   };
-  // one K step: SUB slices of 16.  The four activation fragments of slice s + 1
-  // are read from LDS while the eight MFMAs of slice s issue: the group
-  // barriers at the end pin that order (left alone, the scheduler places each
-  // read right before its first use and the LDS latency shows every time).
-  auto compute = [&](const bf16* A, const u32x4 (&bq)[2][SUB]) {
-    u32x4 af[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) af[mt] = *reinterpret_cast<const u32x4*>(&A[(32 * mt + c) * LDA + 8 * h]);
-#pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      u32x4 an[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        an[mt] = s + 1 < SUB ? *reinterpret_cast<const u32x4*>(&A[(32 * mt + c) * LDA + 16 * (s + 1) + 8 * h])
-                             : af[mt];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma32_bf16(af[mt], bq[nt][s], acc[mt][nt]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) af[mt] = an[mt];
-    }
-    // order: 4 reads (slice 0); per slice but the last: (1 MFMA, 1 read) x 4, 4 MFMAs; last slice: 8 MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int s = 0; s + 1 < SUB; ++s) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  };
 
-  // two-step ping-pong without branches (as in the kernel above)
-  load_b(b0q, 0);  // weights first: they do not wait for the row -> token lookup
-  load_a(0);
-  store_a(As[0]);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= nkt; kt += 2) {
-    load_a(min(kt + 1, nkt - 1));
-    load_b(b1q, min(kt + 1, nkt - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(As[0], b0q);
-    __builtin_amdgcn_sched_barrier(0);
-    store_a(As[1]);
-    __syncthreads();
-    load_a(min(kt + 2, nkt - 1));
-    load_b(b0q, min(kt + 2, nkt - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(As[1], b1q);
-    __builtin_amdgcn_sched_barrier(0);
+  // Main loop and epilogue for MTA active 32-row tiles (1..4): the last item of
+  // an expert usually holds fewer than 128 rows, and its idle row tiles then
+  // cost no MFMAs, LDS traffic or activation loads.
+  auto body = [&](auto mta_tag) {
+    constexpr int MTA = decltype(mta_tag)::value;
+    f32x16 acc[MTA][2];
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
+    u32x4 ar[CPT];
+    // a thread's chunk q lies in row tile q (RPT = 32): only q < MTA is needed
+    auto load_a = [&](int kt) {
+#pragma unroll
+      for (int q = 0; q < MTA; ++q) ar[q] = ld16(aptr[q] + kt * KSTEP * 2);
+    };
+    auto store_a = [&](bf16* dst) {
+#pragma unroll
+      for (int q = 0; q < MTA; ++q)
+        *reinterpret_cast<u32x4*>(&dst[(tid / CPR + RPT * q) * LDA + ch * 8]) = ar[q];
+    };
+    // one K step: SUB slices of 16.  The MTA activation fragments of slice s + 1
+    // are read from LDS while the MFMAs of slice s issue: the group barriers at
+    // the end pin that order (left alone, the scheduler places each read right
+    // before its first use and the LDS latency shows every time).
+    auto compute = [&](const bf16* A, const u32x4 (&bq)[2][SUB]) {
+      u32x4 af[MTA];
+#pragma unroll
+      for (int mt = 0; mt < MTA; ++mt) af[mt] = *reinterpret_cast<const u32x4*>(&A[(32 * mt + c) * LDA + 8 * h]);
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        u32x4 an[MTA];
+#pragma unroll
+        for (int mt = 0; mt < MTA; ++mt)
+          an[mt] = s + 1 < SUB ? *reinterpret_cast<const u32x4*>(&A[(32 * mt + c) * LDA + 16 * (s + 1) + 8 * h])
+                               : af[mt];
+#pragma unroll
+        for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma32_bf16(af[mt], bq[nt][s], acc[mt][nt]);
+#pragma unroll
+        for (int mt = 0; mt < MTA; ++mt) af[mt] = an[mt];
+      }
+      // order: MTA reads (slice 0); per slice but the last: (1 MFMA, 1 read) x MTA,
+      // MTA MFMAs; last slice: 2 MTA MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, MTA, 0);
+#pragma unroll
+      for (int s = 0; s + 1 < SUB; ++s) {
+#pragma unroll
+        for (int i = 0; i < MTA; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MTA, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * MTA, 0);
+    };
+
+    // two-step ping-pong without branches
+    load_b(b0q, 0);  // weights first: they do not wait for the row -> token lookup
+    load_a(0);
     store_a(As[0]);
     __syncthreads();
-  }
-  if (kt < nkt) compute(As[0], b0q);
+    int kt = 0;
+    for (; kt + 2 <= nkt; kt += 2) {
+      load_a(min(kt + 1, nkt - 1));
+      load_b(b1q, min(kt + 1, nkt - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(As[0], b0q);
+      __builtin_amdgcn_sched_barrier(0);
+      store_a(As[1]);
+      __syncthreads();
+      load_a(min(kt + 2, nkt - 1));
+      load_b(b0q, min(kt + 2, nkt - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(As[1], b1q);
+      __builtin_amdgcn_sched_barrier(0);
+      store_a(As[0]);
+      __syncthreads();
+    }
+    if (kt < nkt) compute(As[0], b0q);
 
-  // epilogue through LDS: each wave writes its 32 x 32 tiles (SwiGLU applied)
-  // into a 128 x NC staging tile, then the block stores 16-byte row chunks
-  __syncthreads();  // every wave is done reading the activation tiles
+    // epilogue through LDS: each wave writes its 32 x 32 tiles (SwiGLU applied)
+    // into a 32 MTA x NC staging tile, then the block stores 16-byte row chunks
+    __syncthreads();  // every wave is done reading the activation tiles
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < MTA; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (GATEUP) {
-        smem[r * LDH + 32 * w + c] = (bf16)(silu(acc[mt][0][i]) * acc[mt][1][i]);
-      } else {
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (GATEUP) {
+          smem[r * LDH + 32 * w + c] = (bf16)(silu(acc[mt][0][i]) * acc[mt][1][i]);
+        } else {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) smem[r * LDH + 64 * w + 32 * nt + c] = (bf16)acc[mt][nt][i];
+          for (int nt = 0; nt < 2; ++nt) smem[r * LDH + 64 * w + 32 * nt + c] = (bf16)acc[mt][nt][i];
+        }
       }
     }
-  }
-  __syncthreads();
-  bf16* const out = (bf16*)(GATEUP ? (shared ? a.hsh : a.h) : (shared ? a.ysh : a.y));
-  const int ld = GATEUP ? (shared ? a.S * a.FS : a.F) : a.d;
-  const int ncols = GATEUP ? ld : a.d;  // a last down block may be half past d
-  constexpr int CK = NC / 8;              // 16-byte chunks per staged row
+    __syncthreads();
+    bf16* const out = (bf16*)(GATEUP ? (shared ? a.hsh : a.h) : (shared ? a.ysh : a.y));
+    const int ld = GATEUP ? (shared ? a.S * a.FS : a.F) : a.d;
+    const int ncols = GATEUP ? ld : a.d;  // a last down block may be half past d
+    constexpr int CK = NC / 8;              // 16-byte chunks per staged row
 #pragma unroll
-  for (int q = 0; q < TBM * CK / 256; ++q) {
-    const int idx = tid + 256 * q, r = idx / CK, ck = idx % CK, col = n0 + 8 * ck;
-    if (r < mrows && col < ncols)
-      st16(out + (size_t)(row0 + r) * ld + col, *reinterpret_cast<const u32x4*>(&smem[r * LDH + 8 * ck]));
-  }
+    for (int q = 0; q < 32 * MTA * CK / 256; ++q) {
+      const int idx = tid + 256 * q, r = idx / CK, ck = idx % CK, col = n0 + 8 * ck;
+      if (r < mrows && col < ncols)
+        st16(out + (size_t)(row0 + r) * ld + col, *reinterpret_cast<const u32x4*>(&smem[r * LDH + 8 * ck]));
+    }
+  };
+  const int mta = (GATEUP ? a.rowskip_gu : a.rowskip_dn) ? (mrows + 31) >> 5 : 4;
+  if (mta >= 4) body(std::integral_constant<int, 4>{});
+  else if (mta == 3) body(std::integral_constant<int, 3>{});
+  else if (mta == 2) body(std::integral_constant<int, 2>{});
+  else body(std::integral_constant<int, 1>{});
 }
 
 // ------------------------------------------------------------------ launch

@@ -30,6 +30,7 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_int4_kernel(FfnArgs a) {
   constexpr int NC = GATEUP ? 128 : 256;
   constexpr int LDH = NC + 8;
   constexpr int SMEM = 2 * TBM * LDA > TBM * LDH ? 2 * TBM * LDA : TBM * LDH;
+  static_assert(CPT == 8 && RPT == 16, "a thread's activation chunk q must lie in row tile q / 2");
   __shared__ bf16 smem[SMEM];
   bf16* const As[2] = {smem, smem + TBM * LDA};
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6, h = lane >> 5, c = lane & 31;
@@ -87,26 +88,9 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_int4_kernel(FfnArgs a) {
     return (size_t)slab * a.d * Kb + (size_t)kg * cstride;
   };
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
-
-  u32x4 ar[CPT];
   u32x4 b0q[2][2], b1q[2][2];
   float s0q[2], s1q[2];
   const int nkt = Kfull / KSTEP;
-
-  auto load_a = [&](int kt) {
-#pragma unroll
-    for (int q = 0; q < CPT; ++q) ar[q] = ld16(aptr[q] + kt * KSTEP * 2);
-  };
-  auto store_a = [&](bf16* dst) {
-#pragma unroll
-    for (int q = 0; q < CPT; ++q)
-      *reinterpret_cast<u32x4*>(&dst[(tid / CPR + RPT * q) * LDA + ch * 8]) = ar[q];
-  };
   auto load_b = [&](u32x4 (&bq)[2][2], float (&bs)[2], int kt) {
     int so;
     const size_t o = woff(kt, &so);
@@ -121,72 +105,99 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_int4_kernel(FfnArgs a) {
       bs[nt] = 16.f * bf16_bits_to_f32(*(const uint16_t*)((const char*)(smat[nt] + so) + soff[nt]));  // 16 s
     }
   };
-  auto compute = [&](const bf16* A, const u32x4 (&bq)[2][2], const float (&bs)[2]) {
-#pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      const int col = 32 * (2 * (s >> 2) + h) + 8 * (s & 3);
-      u32x4 af[4], bf[2];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) af[mt] = *reinterpret_cast<const u32x4*>(&A[(32 * mt + c) * LDA + col]);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) bf[nt] = int4x8_to_bf16_scaled(bq[nt][s >> 2][s & 3], bs[nt]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma32_bf16(af[mt], bf[nt], acc[mt][nt]);
-    }
-  };
 
-  // two-step ping-pong without branches (as in the bf16 tiled kernel)
-  load_b(b0q, s0q, 0);  // weights first: they do not wait for the row -> token lookup
-  load_a(0);
-  store_a(As[0]);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= nkt; kt += 2) {
-    load_a(min(kt + 1, nkt - 1));
-    load_b(b1q, s1q, min(kt + 1, nkt - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(As[0], b0q, s0q);
-    __builtin_amdgcn_sched_barrier(0);
-    store_a(As[1]);
-    __syncthreads();
-    load_a(min(kt + 2, nkt - 1));
-    load_b(b0q, s0q, min(kt + 2, nkt - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(As[1], b1q, s1q);
-    __builtin_amdgcn_sched_barrier(0);
+  // Main loop and epilogue for MTA active 32-row tiles (1..4), as in the bf16
+  // tiled kernel: the idle row tiles of a partly filled item cost nothing.
+  auto body = [&](auto mta_tag) {
+    constexpr int MTA = decltype(mta_tag)::value;
+    constexpr int QA = 2 * MTA;  // a thread's chunk q lies in row tile q / 2 (RPT = 16)
+    f32x16 acc[MTA][2];
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
+    u32x4 ar[QA];
+    auto load_a = [&](int kt) {
+#pragma unroll
+      for (int q = 0; q < QA; ++q) ar[q] = ld16(aptr[q] + kt * KSTEP * 2);
+    };
+    auto store_a = [&](bf16* dst) {
+#pragma unroll
+      for (int q = 0; q < QA; ++q)
+        *reinterpret_cast<u32x4*>(&dst[(tid / CPR + RPT * q) * LDA + ch * 8]) = ar[q];
+    };
+    auto compute = [&](const bf16* A, const u32x4 (&bq)[2][2], const float (&bs)[2]) {
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        const int col = 32 * (2 * (s >> 2) + h) + 8 * (s & 3);
+        u32x4 af[MTA], bf[2];
+#pragma unroll
+        for (int mt = 0; mt < MTA; ++mt) af[mt] = *reinterpret_cast<const u32x4*>(&A[(32 * mt + c) * LDA + col]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) bf[nt] = int4x8_to_bf16_scaled(bq[nt][s >> 2][s & 3], bs[nt]);
+#pragma unroll
+        for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma32_bf16(af[mt], bf[nt], acc[mt][nt]);
+      }
+    };
+
+    // two-step ping-pong without branches (as in the bf16 tiled kernel)
+    load_b(b0q, s0q, 0);  // weights first: they do not wait for the row -> token lookup
+    load_a(0);
     store_a(As[0]);
     __syncthreads();
-  }
-  if (kt < nkt) compute(As[0], b0q, s0q);
+    int kt = 0;
+    for (; kt + 2 <= nkt; kt += 2) {
+      load_a(min(kt + 1, nkt - 1));
+      load_b(b1q, s1q, min(kt + 1, nkt - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(As[0], b0q, s0q);
+      __builtin_amdgcn_sched_barrier(0);
+      store_a(As[1]);
+      __syncthreads();
+      load_a(min(kt + 2, nkt - 1));
+      load_b(b0q, s0q, min(kt + 2, nkt - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(As[1], b1q, s1q);
+      __builtin_amdgcn_sched_barrier(0);
+      store_a(As[0]);
+      __syncthreads();
+    }
+    if (kt < nkt) compute(As[0], b0q, s0q);
 
-  // epilogue through LDS (as in the bf16 tiled kernel)
-  __syncthreads();
+    // epilogue through LDS (as in the bf16 tiled kernel)
+    __syncthreads();
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < MTA; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (GATEUP) {
-        smem[r * LDH + 32 * w + c] = (bf16)(silu(acc[mt][0][i]) * acc[mt][1][i]);
-      } else {
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (GATEUP) {
+          smem[r * LDH + 32 * w + c] = (bf16)(silu(acc[mt][0][i]) * acc[mt][1][i]);
+        } else {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) smem[r * LDH + 64 * w + 32 * nt + c] = (bf16)acc[mt][nt][i];
+          for (int nt = 0; nt < 2; ++nt) smem[r * LDH + 64 * w + 32 * nt + c] = (bf16)acc[mt][nt][i];
+        }
       }
     }
-  }
-  __syncthreads();
-  bf16* const out = (bf16*)(GATEUP ? (shared ? a.hsh : a.h) : (shared ? a.ysh : a.y));
-  const int ld = GATEUP ? (shared ? a.S * a.FS : a.F) : a.d;
-  const int ncols = GATEUP ? ld : a.d;
-  constexpr int CK = NC / 8;
+    __syncthreads();
+    bf16* const out = (bf16*)(GATEUP ? (shared ? a.hsh : a.h) : (shared ? a.ysh : a.y));
+    const int ld = GATEUP ? (shared ? a.S * a.FS : a.F) : a.d;
+    const int ncols = GATEUP ? ld : a.d;
+    constexpr int CK = NC / 8;
 #pragma unroll
-  for (int q = 0; q < TBM * CK / 256; ++q) {
-    const int idx = tid + 256 * q, r = idx / CK, ck = idx % CK, col = n0 + 8 * ck;
-    if (r < mrows && col < ncols)
-      st16(out + (size_t)(row0 + r) * ld + col, *reinterpret_cast<const u32x4*>(&smem[r * LDH + 8 * ck]));
-  }
+    for (int q = 0; q < 32 * MTA * CK / 256; ++q) {
+      const int idx = tid + 256 * q, r = idx / CK, ck = idx % CK, col = n0 + 8 * ck;
+      if (r < mrows && col < ncols)
+        st16(out + (size_t)(row0 + r) * ld + col, *reinterpret_cast<const u32x4*>(&smem[r * LDH + 8 * ck]));
+    }
+  };
+  const int mta = (GATEUP ? a.rowskip_gu : a.rowskip_dn) ? (mrows + 31) >> 5 : 4;
+  if (mta >= 4) body(std::integral_constant<int, 4>{});
+  else if (mta == 3) body(std::integral_constant<int, 3>{});
+  else if (mta == 2) body(std::integral_constant<int, 2>{});
+  else body(std::integral_constant<int, 1>{});
 }
 
 // ------------------------------------------------------------------ launch

@@ -56,6 +56,7 @@ struct FfnArgs {
   int bm;
   int wtiled;                // expert weights in the tiled layout (else one K-contiguous row per channel)
   int wstream;               // tiled kernels: non-temporal weight loads (each expert's weights read by one row tile)
+  int rowskip_gu, rowskip_dn;  // tiled gate/up, down: skip the idle 32-row tiles of partly filled items
   const void *wg, *wu, *wd, *sg, *su, *sd;         // routed weights / INT4 scales
   const void *shg, *shu, *shd, *shsg, *shsu, *shsd;  // shared weights / INT4 scales
   void* h;                   // [R][F]     act dtype

@@ -57,6 +57,21 @@ def test_ragged_token_counts(mid, T):
     run_and_check(sp, lay, ml, x, nsamp=300)
 
 
+@pytest.mark.parametrize("T", [2100, 3001])
+def test_partly_filled_items_skip_idle_row_tiles(mid, T):
+    """From T*k >= 256 E on (experts averaging two 128-row items), the tiled
+    kernels skip the idle 32-row tiles of each expert's partly filled last
+    item; every row is checked, and the experts' last items cover several
+    counts of active row tiles."""
+    sp, lay, ml = mid
+    assert T * sp.k >= 256 * sp.E
+    x = S.make_tokens(sp, T, device="cuda", seed=T)
+    _, idx, _, _, _ = run_and_check(sp, lay, ml, x)
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=sp.E)
+    active = {int(c % 128 + 31) // 32 for c in counts if c % 128}
+    assert len(active) >= 3, active
+
+
 def test_dense_limit_matches_textbook_swiglu():
     """E = 1, k = 1: the gate is softmax of one logit = 1, so the layer is a dense
     SwiGLU FFN.  Checked against the formula written out with scipy's expit."""
