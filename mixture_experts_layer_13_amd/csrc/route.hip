@@ -711,16 +711,17 @@ __global__ __launch_bounds__(512) void permute_multi_kernel(const int32_t* __res
     int sb = 0, st = 0;
     const int e = tid % E, part = tid / E;
     if (part < P) {
-      // 8 tile rows per batch: the loads are issued together
-      for (int r0 = part; r0 < n_tiles; r0 += 8 * P) {
-        int v[8];
+      // 32 tile rows per batch: the loads are issued together (one batch covers 256 tiles of
+      // 64 experts; measured against 8: DeepSeek-V3 T=16384 permute 34 -> 30 us)
+      for (int r0 = part; r0 < n_tiles; r0 += 32 * P) {
+        int v[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 32; ++u) {
           const int r = r0 + u * P;
           v[u] = r < n_tiles ? hist[(size_t)r * E + e] : 0;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 32; ++u) {
           st += v[u];
           if (r0 + u * P < tile) sb += v[u];
         }
