@@ -304,12 +304,12 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name
 def decode_other(layout):
     """The other decode-sized layers the HBM target covers: Qwen3 INT4 at T=32 (4
     copies of its 0.31 GB of expert weights) and DeepSeek-V3 at T=1 and 16 (2 copies:
-    one token already touches 0.8 GB)."""
+    one token already touches 0.8 GB), plus DeepSeek-V3 T=256 from its token sweep."""
     import torch
 
     import moe_synth as S
     out = {}
-    for name, Ts, copies in (("qwen3_int4", (32,), 4), ("dsv3", (1, 16), 2)):
+    for name, Ts, copies in (("qwen3_int4", (32,), 4), ("dsv3", (1, 16, 256), 2)):
         sp = S.SPECS[name]
         lay = S.make_layer(sp, device="cuda")
         out[name] = decode_sweep(sp, lay, layout, Ts=Ts, replays=100, copies=copies, name=name)

@@ -10,7 +10,7 @@ enum { kF32 = 0, kBF16 = 1, kINT4 = 2 };
 enum { kScoreSoftmax = 0, kScoreSigmoid = 1 };
 
 constexpr int kSingleMaxPairs = 8192;   // T*k handled by the single-block route+permute
-constexpr int kSmallMaxPairs = 512;     // T*k handled by the many-block route with a one-wave permute
+constexpr int kSmallMaxPairs = 2048;    // T*k handled by the many-block route with a one-wave permute
 // tokens per block of the small-T route launch: one block for a single token
 // (no hand-off), else a block per token up to 32 tokens, then 4 per block
 inline int route_small_tpb(int T) { return T <= 32 ? 1 : 4; }
