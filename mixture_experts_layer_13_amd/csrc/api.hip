@@ -31,7 +31,8 @@ moe_status fail(moe_status s, const char* fmt, ...) {
   return s;
 }
 
-constexpr int kSingleMaxT = 256;   // T up to which routing runs as split router + one route/permute block
+constexpr int kSingleMaxT = 256;   // T up to which routing runs as split router + route_small
+static_assert(kSingleMaxT * kMaxK <= kSmallMaxPairs, "every small-T forward must fit the one-wave permutation");
 constexpr int kStreamMaxT = 64;    // T up to which the expert GEMMs use the streaming kernels
 constexpr int64_t kMaxT = 1 << 20;
 
@@ -112,11 +113,10 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     q.R = q.cap * q.E < pairs ? q.cap * q.E : pairs;
   }
   q.single = q.T <= kSingleMaxT;
-  // K split of the small-T router: the route launch's blocks read at most kSmallPartials partial
-  // logits each (decode sizes), the single route block ~32K in all (larger T)
+  // K split of the small-T router: each block of the route launch reads at most kSmallPartials
+  // partial logits
   if (q.single && q.T > 0) {
-    int64_t ks = (int64_t)q.T * q.k <= kSmallMaxPairs ? kSmallPartials / ((int64_t)route_small_tpb(q.T) * q.E)
-                                                      : 32768 / ((int64_t)q.T * q.E);
+    int64_t ks = kSmallPartials / ((int64_t)route_small_tpb(q.T) * q.E);
     const int64_t ksmax = q.d / 128;
     ks = ks < 1 ? 1 : (ks > ksmax ? ksmax : ks);
     const int64_t steps = q.d / 128;
@@ -289,9 +289,6 @@ FfnArgs ffn_args(const Plan& p, void* ws, const void* x, const int32_t* row_toke
   return a;
 }
 
-// decode sizes: the many-block route with the one-wave permutation
-bool small_pairs(const Plan& p) { return (int64_t)p.T * p.k <= kSmallMaxPairs; }
-
 // router (logits, scores, top-k, gates) for the planned mode
 moe_status enqueue_route(const Plan& p, const void* x, const void* wr, const RouteArgs& ra, void* ws, hipStream_t s) {
   moe_status st;
@@ -300,8 +297,7 @@ moe_status enqueue_route(const Plan& p, const void* x, const void* wr, const Rou
     if ((st = hip_ok(launch_router_partial(p.act, x, wr, p.T, p.d, p.E, p.kchunk, p.KS, part, nullptr, s), "router")))
       return st;
     PermArgs none{};
-    if (small_pairs(p)) return hip_ok(launch_route_small(part, p.KS, ra, nullptr, none, 1, 0, nullptr, s), "route");
-    return hip_ok(launch_route_permute_single(part, p.KS, ra, nullptr, none, 1, 0, s), "route");
+    return hip_ok(launch_route_small(part, p.KS, ra, nullptr, none, 1, 0, nullptr, s), "route");
   }
   return hip_ok(launch_router_fused(p.act, x, wr, ra, p.rt, at<int32_t>(ws, p.o_hist), s), "router");
 }
@@ -372,8 +368,7 @@ moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* cou
   PermArgs pa = perm_args(p, ws, counts, offsets, row_token, slot_row, drop_mask);
   if (p.single) {
     RouteArgs ra = route_args(p, nullptr, nullptr, nullptr, nullptr, nullptr);
-    if (small_pairs(p)) return hip_ok(launch_route_small(nullptr, 0, ra, topk_idx, pa, 0, 1, nullptr, s), "permute");
-    return hip_ok(launch_route_permute_single(nullptr, 0, ra, topk_idx, pa, 0, 1, s), "permute");
+    return hip_ok(launch_route_small(nullptr, 0, ra, topk_idx, pa, 0, 1, nullptr, s), "permute");
   }
   int32_t* hist = at<int32_t>(ws, p.o_hist);
   if ((st = hip_ok(launch_tile_hist(topk_idx, p.T, p.k, p.E, p.rt, hist, s), "histogram"))) return st;
@@ -440,16 +435,12 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   mark(0, nl, s);
   if (p.single) {
     float* part = at<float>(ws, p.o_part);
-    const bool small = small_pairs(p);
     int32_t* arrived = at<int32_t>(ws, p.o_arrived);
-    if ((st = hip_ok(launch_router_partial(p.act, x, w_router, p.T, p.d, p.E, p.kchunk, p.KS, part,
-                                           small ? arrived : nullptr, s),
+    if ((st = hip_ok(launch_router_partial(p.act, x, w_router, p.T, p.d, p.E, p.kchunk, p.KS, part, arrived, s),
                      "router")))
       return st;
     mark(1, nl, s);
-    if (small) st = hip_ok(launch_route_small(part, p.KS, ra, nullptr, pa, 1, 1, arrived, s), "route/permute");
-    else st = hip_ok(launch_route_permute_single(part, p.KS, ra, nullptr, pa, 1, 1, s), "route/permute");
-    if (st) return st;
+    if ((st = hip_ok(launch_route_small(part, p.KS, ra, nullptr, pa, 1, 1, arrived, s), "route/permute"))) return st;
   } else {
     int32_t* hist = at<int32_t>(ws, p.o_hist);
     if ((st = hip_ok(launch_router_fused(p.act, x, w_router, ra, p.rt, hist, s), "router"))) return st;

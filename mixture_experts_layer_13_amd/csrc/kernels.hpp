@@ -9,7 +9,6 @@ namespace moe {
 enum { kF32 = 0, kBF16 = 1, kINT4 = 2 };
 enum { kScoreSoftmax = 0, kScoreSigmoid = 1 };
 
-constexpr int kSingleMaxPairs = 8192;   // T*k handled by the single-block route+permute
 constexpr int kSmallMaxPairs = 2048;    // T*k handled by the many-block route with a one-wave permute
 // tokens per block of the small-T route launch: one block for a single token
 // (no hand-off), else a block per token up to 32 tokens, then 4 per block
@@ -69,8 +68,6 @@ hipError_t launch_router_partial(int act, const void* x, const void* wr, int T, 
                                  float* part, int32_t* zero, hipStream_t s);
 hipError_t launch_route_small(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
                               const PermArgs& pa, int do_route, int do_perm, int32_t* arrived, hipStream_t s);
-hipError_t launch_route_permute_single(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
-                                       const PermArgs& pa, int do_route, int do_perm, hipStream_t s);
 hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int rt, int32_t* hist,
                                hipStream_t s);
 hipError_t launch_tile_hist(const int32_t* idx, int T, int k, int E, int rt, int32_t* hist, hipStream_t s);

@@ -200,16 +200,6 @@ __device__ void route_rows(const float* slog, int ld, int nt, int t0, const Rout
   }
 }
 
-__device__ __forceinline__ void route_rows_any(const float* slog, int ld, int nt, int t0, const RouteArgs& ra,
-                                               const float* bias, uint16_t* sel, int w, int nw) {
-  if (ra.E <= 64)
-    route_rows<1>(slog, ld, nt, t0, ra, bias, sel, w, nw);
-  else if (ra.E <= 128)
-    route_rows<2>(slog, ld, nt, t0, ra, bias, sel, w, nw);
-  else
-    route_rows<4>(slog, ld, nt, t0, ra, bias, sel, w, nw);
-}
-
 // Exclusive scan of n <= 256 ints in LDS by one wave; returns the total.
 __device__ __forceinline__ int wave_exclusive_scan256(const int* in, int* out, int n) {
   const int lane = lane_id();
@@ -331,106 +321,6 @@ __device__ __forceinline__ void place_pair(const PermArgs& p, int i, int e, bool
   } else {
     p.slot_row[i] = -1;
     p.drop[i] = 1;
-  }
-}
-
-// ------------------------------------------------------------------ single-block route + permute
-// For small T (T*k <= kSingleMaxPairs): one block of 1024 threads sums the partial
-// logits, scores and selects every token (a wave per token), then counts, scans
-// and ranks all pairs.  Either half can be switched off (route-only, permute-only).
-__global__ __launch_bounds__(1024) void route_permute_single_kernel(const float* __restrict__ part, int KS,
-                                                                    RouteArgs ra, const int32_t* idx_in,
-                                                                    PermArgs pa, int do_route, int do_perm) {
-  constexpr int kLog = 16384;  // logits staged in LDS per token group
-  __shared__ float slog[kLog];
-  __shared__ uint16_t sel[kSingleMaxPairs];
-  __shared__ int wcnt[16 * 256];
-  __shared__ int base[256], kept[256], off[257], tmp[512];
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / 64;
-  const int T = ra.T, E = ra.E, k = ra.k, n = T * k;
-  if (do_route) {
-    const int G = kLog / E;  // tokens per group (E <= 256 -> G >= 64)
-    for (int tg = 0; tg < T; tg += G) {
-      const int nt = min(G, T - tg);
-      // logits (before the skew bias) = sum of the KS K-chunk partials.  KG
-      // consecutive lanes share an element when there are few elements (small
-      // T): lane g of the group adds chunks g, g + KG, ... in order, then the
-      // group adds its KG sums in a fixed butterfly; each thread issues all its
-      // loads (up to 4 elements x 16 chunks) at once, one round trip per batch
-      const int nout = nt * E;
-      int KG = 1;
-      while (KG < 16 && 2 * KG * nout <= (int)blockDim.x && 2 * KG <= KS) KG *= 2;
-      const int g = tid % KG, per = (int)blockDim.x / KG;
-      const size_t zs = (size_t)T * E;
-      for (int i0 = tid / KG; i0 < nout; i0 += 4 * per) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int z0 = g; z0 < KS; z0 += 16 * KG) {
-          float v[4][16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int i = i0 + q * per;
-            const int t = tg + i / E, e = i - (i / E) * E;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-              const int z = z0 + u * KG;
-              v[q][u] = (i < nout && z < KS) ? part[(size_t)z * zs + (size_t)t * E + e] : 0.f;
-            }
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-              if (z0 + u * KG < KS) acc[q] += v[q][u];
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          for (int o = 1; o < KG; o <<= 1) acc[q] += __shfl_xor(acc[q], o);
-          const int i = i0 + q * per;
-          if (g == 0 && i < nout) slog[i] = acc[q];
-        }
-      }
-      __syncthreads();
-      route_rows_any(slog, E, nt, tg, ra, ra.logit_bias, sel + tg * k, w, 16);
-      __syncthreads();
-    }
-  } else if (do_perm) {
-    for (int i = tid; i < n; i += blockDim.x) {
-      const int e = idx_in[i];
-      sel[i] = (e >= 0 && e < E) ? (uint16_t)e : (uint16_t)0xFFFF;
-    }
-  }
-  if (!do_perm) return;
-  __syncthreads();
-  (void)lane;
-  // phase A: per-expert counts
-  for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;
-  __syncthreads();
-  for (int p0 = 0; p0 < n; p0 += blockDim.x) {
-    const int i = p0 + tid;
-    const int e = i < n ? (int)sel[i] : 0xFFFF;
-    rank_pass(e, e < E, wcnt, base, E);
-  }
-  for (int x = tid; x < E; x += blockDim.x) {
-    pa.counts[x] = base[x];
-    kept[x] = pa.cap < 0 ? base[x] : min(base[x], pa.cap);
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const int tot = wave_exclusive_scan256(kept, off, E);
-    if (tid == 0) off[E] = tot;
-  }
-  __syncthreads();
-  for (int x = tid; x <= E; x += blockDim.x) pa.offsets[x] = off[x];
-  if (pa.items) write_tile_map(kept, off, E, pa.bm, pa.items, pa.n_items, tmp);
-  // phase B: ranks and placement
-  for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;
-  __syncthreads();
-  for (int p0 = 0; p0 < n; p0 += blockDim.x) {
-    const int i = p0 + tid;
-    const int e = i < n ? (int)sel[i] : 0xFFFF;
-    const bool valid = e < E;
-    const int r = rank_pass(e, valid, wcnt, base, E);
-    if (i < n) place_pair(pa, i, e, valid, r, off);
   }
 }
 
@@ -807,13 +697,6 @@ hipError_t launch_route_small(const float* part, int KS, const RouteArgs& ra, co
   const int grid = do_route ? (ra.T + tpb - 1) / tpb : 1;
   auto kern = ra.E <= 64 ? route_small_kernel<1> : (ra.E <= 128 ? route_small_kernel<2> : route_small_kernel<4>);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, part, KS, tpb, ra, idx_in, pa, do_route, do_perm, arrived);
-  return hipGetLastError();
-}
-
-hipError_t launch_route_permute_single(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
-                                       const PermArgs& pa, int do_route, int do_perm, hipStream_t s) {
-  hipLaunchKernelGGL(route_permute_single_kernel, dim3(1), dim3(1024), 0, s, part, KS, ra, idx_in, pa, do_route,
-                     do_perm);
   return hipGetLastError();
 }
 
