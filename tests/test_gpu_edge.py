@@ -72,6 +72,40 @@ def test_partly_filled_items_skip_idle_row_tiles(mid, T):
     assert len(active) >= 3, active
 
 
+@pytest.mark.parametrize("T", [64, 2100])
+def test_token_permutation_permutes_outputs_bitwise(mid, T):
+    """Dropless, every token's routing and FFN are its own: permuting the token
+    order permutes idx, gates and out, bit for bit (streaming and tiled paths,
+    including the partly filled items whose rows then change places)."""
+    sp, lay, ml = mid
+    x = S.make_tokens(sp, T, device="cuda", seed=T + 7)
+    perm = torch.randperm(T, generator=torch.Generator().manual_seed(T)).to("cuda")
+    a = ml.forward(x)
+    b = ml.forward(x[perm].contiguous())
+    torch.cuda.synchronize()
+    for u, v, what in zip(a[:3], b[:3], ("out", "idx", "gates")):
+        u = u[perm]
+        assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v), what
+
+
+def test_combine_is_linear_in_the_gates(mid):
+    """Scaling every gate by a power of two scales the combined output by it
+    exactly (fp32 accumulation, one rounding); zero gates give exact zeros."""
+    sp, lay, ml = mid
+    x = S.make_tokens(sp, 300, device="cuda", seed=5)
+    idx, gates, _ = ml.route(x, want_scores=False)
+    _, offsets, row_token, slot_row, _ = ml.permute(idx)
+    y_rows, y_sh = ml.expert_ffn(x, offsets, row_token)
+    base = ml.combine(y_rows, slot_row, gates, y_sh).float()
+    twice = ml.combine(y_rows, slot_row, gates * 2, y_sh).float()
+    zero = ml.combine(y_rows, slot_row, gates * 0, y_sh).float()
+    torch.cuda.synchronize()
+    assert base.abs().max() > 0
+    assert torch.equal(twice, base * 2)
+    assert torch.equal(zero, torch.zeros_like(zero))
+
+
 def test_dense_limit_matches_textbook_swiglu():
     """E = 1, k = 1: the gate is softmax of one logit = 1, so the layer is a dense
     SwiGLU FFN.  Checked against the formula written out with scipy's expit."""
