@@ -43,7 +43,7 @@ struct Plan {
   int64_t R;
   bool single;
   int KS, kchunk;
-  int rt, n_rt;
+  int rt, n_rt, rpb, n_rb;
   int mode, bm;
   bool wstream;  // tiled kernels stream the weights non-temporally
   bool rowskip_gu, rowskip_dn;  // tiled kernels skip the idle row tiles of partly filled items
@@ -129,6 +129,12 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   }
   q.rt = (q.E > 128 && q.act == MOE_BF16) ? 32 : 16;
   q.n_rt = (q.T + q.rt - 1) / q.rt;
+  // at most kMaxRouteBlocks router (and permute) blocks, each over rpb consecutive router tiles:
+  // every permute block sums the histograms of the blocks before it, so that work grows with the
+  // square of the block count (1024 blocks: at most 1 MB of reads per block at E = 256)
+  q.rpb = (q.n_rt + kMaxRouteBlocks - 1) / kMaxRouteBlocks;
+  if (q.rpb < 1) q.rpb = 1;
+  q.n_rb = (q.n_rt + q.rpb - 1) / q.rpb;
   q.mode = (q.act == MOE_F32 || q.T <= kStreamMaxT) ? 0 : 1;
   // streaming kernels take items of 16 rows (T <= 16: an expert gets each token at most once; or
   // at most 8 pairs per expert on average, where splitting a hot expert costs less than the
@@ -163,7 +169,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   };
   q.o_part = take(q.single ? (size_t)q.KS * q.T * q.E * 4 : 0);
   q.o_arrived = take(4);
-  q.o_hist = take(q.single ? 0 : (size_t)q.n_rt * q.E * 4);
+  q.o_hist = take(q.single ? 0 : (size_t)q.n_rb * q.E * 4);
   q.o_counts = take((size_t)q.E * 4);
   q.o_off = take((size_t)(q.E + 1) * 4);
   q.o_rowtok = take((size_t)q.R * 4);
@@ -210,6 +216,7 @@ RouteArgs route_args(const Plan& p, const float* lb, const float* sb, int32_t* i
   r.idx = idx;
   r.gates = gates;
   r.scores = scores;
+  r.tiles_per_block = p.rpb;
   return r;
 }
 
@@ -228,7 +235,7 @@ PermArgs perm_args(const Plan& p, void* ws, int32_t* counts, int32_t* offsets, i
   a.items = at<int4>(ws, p.o_items);
   a.n_items = at<int32_t>(ws, p.o_nitems);
   a.bm = p.bm;
-  a.rt = p.rt;
+  a.rt = p.rt * p.rpb;  // tokens per permute block
   return a;
 }
 
@@ -371,7 +378,7 @@ moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* cou
     return hip_ok(launch_route_small(nullptr, 0, ra, topk_idx, pa, 0, 1, nullptr, s), "permute");
   }
   int32_t* hist = at<int32_t>(ws, p.o_hist);
-  if ((st = hip_ok(launch_tile_hist(topk_idx, p.T, p.k, p.E, p.rt, hist, s), "histogram"))) return st;
+  if ((st = hip_ok(launch_tile_hist(topk_idx, p.T, p.k, p.E, p.rt * p.rpb, hist, s), "histogram"))) return st;
   return hip_ok(launch_permute_multi(topk_idx, hist, pa, s), "permute");
 }
 

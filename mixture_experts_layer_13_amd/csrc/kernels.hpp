@@ -16,6 +16,7 @@ inline int route_small_tpb(int T) { return T <= 32 ? 1 : 4; }
 // partial logits one small-T route block sums (K chunks x experts x its tokens)
 constexpr int kSmallPartials = 8192;
 constexpr int kPrefillRows = 128;       // rows per item in the tiled (large-M) expert kernels
+constexpr int kMaxRouteBlocks = 1024;   // large T: router / permute blocks at most (each over several tiles)
 
 struct RouteArgs {
   int T, d, E, k;
@@ -27,6 +28,7 @@ struct RouteArgs {
   int32_t* idx;              // [T][k]
   float* gates;              // [T][k]
   float* scores;             // [T][E] or null
+  int tiles_per_block;       // large-T router: consecutive 16/32-token tiles per block (>= 1)
 };
 
 struct PermArgs {
@@ -40,7 +42,7 @@ struct PermArgs {
   int4* items;               // tile map {expert, first row, rows, 0} (null: not built)
   int32_t* n_items;
   int bm;                    // rows per tile-map item
-  int rt;                    // tokens per router tile / tile-histogram row (large T)
+  int rt;                    // tokens per router block / tile-histogram row (large T)
 };
 
 struct FfnArgs {

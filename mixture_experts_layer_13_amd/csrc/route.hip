@@ -473,10 +473,11 @@ __global__ __launch_bounds__(256) void route_small_kernel(const float* __restric
 }
 
 // ------------------------------------------------------------------ fused router (large T)
-// One block per tile of 16 * MT tokens computes all E logits with MFMA: the
-// four waves split K into quarters and their partial sums are added in LDS in
-// fixed wave order.  Then each token is scored and selected (a wave per token)
-// and the block writes the tile's expert histogram.  NB = experts / 16 held
+// A block takes ra.tiles_per_block consecutive tiles of 16 * MT tokens.  For
+// each tile it computes all E logits with MFMA (the four waves split K into
+// quarters, and their partial sums are added in LDS in fixed wave order), then
+// scores and selects each token (a wave per token) and adds the tile's picks to
+// the block's expert histogram, which it writes once at the end.  NB = experts / 16 held
 // per wave (compile-time bound, E <= 16 * NB).
 template <typename TIN, int MT, int NB>
 __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict__ x, const TIN* __restrict__ wr,
@@ -492,70 +493,74 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict
   __shared__ int base[256];
   const int tid = threadIdx.x, lane = lane_id(), w = tid / 64, g = lane >> 4, c = lane & 15;
   const int T = ra.T, E = ra.E, d = ra.d, k = ra.k;
-  const int t0 = blockIdx.x * TM;
   const int nblk = (E + 15) / 16;
-  f32x4 acc[MT][NB];
+  for (int xx = tid; xx < 256; xx += blockDim.x) base[xx] = 0;  // ordered before use by the barriers below
+  for (int tt = 0; tt < ra.tiles_per_block; ++tt) {
+    const int t0 = (blockIdx.x * ra.tiles_per_block + tt) * TM;
+    if (t0 >= T) break;  // block-uniform
+    f32x4 acc[MT][NB];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const TIN* pa[MT];
+      for (int b = 0; b < NB; ++b) acc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const TIN* pa[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) pa[m] = x + (size_t)min(t0 + 16 * m + c, T - 1) * d + g * EPC;
-  const TIN* pb = wr + (size_t)min(c, E - 1) * d + g * EPC;   // expert block b adds 16 * b rows
-  const int nsteps = d / KSTEP;
-  const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
-  for (int st = s0; st < s1; st += U) {
-    u32x4 av[U][MT], bv[U][NB];
+    for (int m = 0; m < MT; ++m) pa[m] = x + (size_t)min(t0 + 16 * m + c, T - 1) * d + g * EPC;
+    const TIN* pb = wr + (size_t)min(c, E - 1) * d + g * EPC;   // expert block b adds 16 * b rows
+    const int nsteps = d / KSTEP;
+    const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
+    for (int st = s0; st < s1; st += U) {
+      u32x4 av[U][MT], bv[U][NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (st + u < s1) {
-        const int kk = (st + u) * KSTEP;
+      for (int u = 0; u < U; ++u) {
+        if (st + u < s1) {
+          const int kk = (st + u) * KSTEP;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) av[u][m] = ld16(pa[m] + kk);
+          for (int m = 0; m < MT; ++m) av[u][m] = ld16(pa[m] + kk);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const int row = min(16 * b + c, E - 1) - min(c, E - 1);
-          if (b < nblk) bv[u][b] = ld16(pb + (size_t)row * d + kk);
+          for (int b = 0; b < NB; ++b) {
+            const int row = min(16 * b + c, E - 1) - min(c, E - 1);
+            if (b < nblk) bv[u][b] = ld16(pb + (size_t)row * d + kk);
+          }
         }
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (st + u < s1)
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            if (b < nblk)
+#pragma unroll
+              for (int m = 0; m < MT; ++m) acc[m][b] = Chunk<TIN>::mma(av[u][m], bv[u][b], acc[m][b]);
     }
+    // sum the four K quarters in wave order
+    for (int ww = 0; ww < 4; ++ww) {
+      if (w == ww) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (st + u < s1)
+        for (int b = 0; b < NB; ++b) {
+          if (b >= nblk) continue;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          if (b < nblk)
+          for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m][b] = Chunk<TIN>::mma(av[u][m], bv[u][b], acc[m][b]);
-  }
-  // sum the four K quarters in wave order
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b >= nblk) continue;
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float* p = &slog[(16 * m + 4 * g + i) * LD + 16 * b + c];
-            *p = ww == 0 ? acc[m][b][i] : *p + acc[m][b][i];
-          }
+            for (int i = 0; i < 4; ++i) {
+              float* p = &slog[(16 * m + 4 * g + i) * LD + 16 * b + c];
+              *p = ww == 0 ? acc[m][b][i] : *p + acc[m][b][i];
+            }
+        }
       }
+      __syncthreads();
     }
+    const int nt = min(TM, T - t0);
+    route_rows<(16 * NB + 63) / 64>(slog, LD, nt, t0, ra, ra.logit_bias, sel, w, 4);
+    // the tile's pairs into the block histogram (sel[] is complete only after this barrier; the
+    // next tile overwrites slog and sel only after the barriers inside the rank passes)
     __syncthreads();
-  }
-  const int nt = min(TM, T - t0);
-  route_rows<(16 * NB + 63) / 64>(slog, LD, nt, t0, ra, ra.logit_bias, sel, w, 4);
-  // tile histogram over the tile's pairs (sel[] is complete only after this barrier)
-  __syncthreads();
-  for (int xx = tid; xx < 256; xx += blockDim.x) base[xx] = 0;
-  const int np = nt * k;
-  for (int p0 = 0; p0 < np; p0 += blockDim.x) {
-    const int i = p0 + tid;
-    const int e = i < np ? (int)sel[i] : 0xFFFF;
-    rank_pass(e, e < E, wcnt, base, E);
+    const int np = nt * k;
+    for (int p0 = 0; p0 < np; p0 += blockDim.x) {
+      const int i = p0 + tid;
+      const int e = i < np ? (int)sel[i] : 0xFFFF;
+      rank_pass(e, e < E, wcnt, base, E);
+    }
   }
   __syncthreads();
   for (int xx = tid; xx < E; xx += blockDim.x) hist[(size_t)blockIdx.x * E + xx] = base[xx];
@@ -702,7 +707,8 @@ hipError_t launch_route_small(const float* part, int KS, const RouteArgs& ra, co
 
 hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int rt, int32_t* hist,
                                hipStream_t s) {
-  dim3 grid((ra.T + rt - 1) / rt);
+  const int span = rt * ra.tiles_per_block;
+  dim3 grid((ra.T + span - 1) / span);
   const int nb = (ra.E + 15) / 16;
   if (act == kF32) {
     hipLaunchKernelGGL((router_fused_kernel<float, 1, 16>), grid, dim3(256), 0, s, (const float*)x, (const float*)wr,

@@ -106,6 +106,63 @@ def test_combine_is_linear_in_the_gates(mid):
     assert torch.equal(zero, torch.zeros_like(zero))
 
 
+def test_several_router_tiles_per_block(mid):
+    """Above 1024 router tiles each router and permute block takes several
+    consecutive tiles (T=20000: 1250 tiles of 16 tokens, 2 per block)."""
+    sp, lay, ml = mid
+    x = S.make_tokens(sp, 20000, device="cuda", seed=11)
+    run_and_check(sp, lay, ml, x, nsamp=300)
+
+
+# the largest token count the library accepts, on a small layer
+MAXT = S.SPECS["olmoe"].replace(name="maxt", cfg_id=12, d=128, E=64, k=8, ffn=128, rms_norm_x=False)
+
+
+def _check_permutation(idx: np.ndarray, counts, offsets, row_token, slot_row, drop):
+    """Dropless permutation by its definition: pairs walked token-major fill each
+    expert's rows in order, and every row maps back to its token."""
+    T, k = idx.shape
+    E = counts.shape[0]
+    flat = idx.reshape(-1).astype(np.int64)
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
+    assert not drop.any()
+    order = np.argsort(flat, kind="stable")  # expert-major, token-major inside an expert
+    expect = np.empty(T * k, np.int64)
+    expect[order] = np.arange(T * k)
+    assert np.array_equal(slot_row.reshape(-1), expect)
+    assert np.array_equal(row_token[expect], np.repeat(np.arange(T), k))
+
+
+def test_largest_token_count():
+    """T = 2^20 (the API's limit): 65536 router tiles, 64 per block.  The GPU's own
+    routing must be a valid top-k that agrees with the oracle on sampled tokens
+    (dropless routing is per token), its permutation must follow the definition
+    exactly, and sampled outputs must match the oracle."""
+    from mixture_experts_layer_13_amd import binding as B
+    sp = MAXT
+    T = 1 << 20
+    lay = S.make_layer(sp, device="cuda")
+    ml = layer_of(sp, lay)
+    x = S.make_tokens(sp, T, device="cuda", seed=3)
+    out, idx, gates, drop = ml.forward(x)
+    counts, offsets, row_token, slot_row, drop2 = ml.permute(idx)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    _check_permutation(gi, counts.cpu().numpy(), offsets.cpu().numpy(), row_token.cpu().numpy(),
+                       slot_row.cpu().numpy(), drop2.cpu().numpy())
+    assert not drop.cpu().numpy().any()
+    rows = np.sort(np.random.default_rng(2).choice(T, 256, replace=False))
+    ref = oracle_run(sp, lay, x[torch.from_numpy(rows).to("cuda")])
+    rep = compare_routes(gi[rows], ref, sp.k)
+    assert rep.set_mismatch_strict == 0 and rep.order_mismatch == 0
+    ok = rep.matched
+    rel = row_rel_err(out[torch.from_numpy(rows).to("cuda")].float().cpu().numpy().astype(np.float64)[ok],
+                      ref["out"][ok])
+    assert rel.max(initial=0) <= tol_of(sp), rel.max()
+    assert B.forward_launches(ml.cfg_for(T)) == 5
+
+
 def test_dense_limit_matches_textbook_swiglu():
     """E = 1, k = 1: the gate is softmax of one logit = 1, so the layer is a dense
     SwiGLU FFN.  Checked against the formula written out with scipy's expit."""
