@@ -151,11 +151,16 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   // slab and can turn their L2 hits into misses; measured, skipping pays with INT4 weights (a
   // quarter of the bytes; Qwen3 INT4 T=4096 gate/up 288 -> 261 us) and with bf16 weights when
   // experts average at least two items and the slab's K is at most 4096 (OLMoE T=4096 gate/up
-  // 315 -> 305 us), and costs 3% on DeepSeek-V3 (K = 7168, or T=4096 at 128 rows per expert)
+  // 315 -> 305 us), and costs 3% on DeepSeek-V3 (K = 7168, or T=4096 at 128 rows per expert).
+  // With streamed weights (one row tile per expert) there is no reuse to lose (OLMoE T=256
+  // 223 -> 208 us), unless shared experts follow: their full tiles, cut into the last XCD chunks
+  // at the weight of the cheap routed ones, then finish last (DeepSeek-V2-Lite T=256 gate/up
+  // 137 -> 152 us)
   {
     const bool many = (int64_t)q.T * q.k >= 2 * (int64_t)kPrefillRows * q.E;
-    q.rowskip_gu = q.wdt == MOE_INT4_G128 || (many && q.d <= 4096);
-    q.rowskip_dn = q.wdt == MOE_INT4_G128 || (many && q.F <= 4096);
+    const bool lone = q.wstream && q.S == 0;
+    q.rowskip_gu = q.wdt == MOE_INT4_G128 || lone || (many && q.d <= 4096);
+    q.rowskip_dn = q.wdt == MOE_INT4_G128 || lone || (many && q.F <= 4096);
   }
   q.items_max = q.R / q.bm + (q.R < q.E ? q.R : q.E);
   q.sh_items = q.S > 0 ? (q.T + q.bm - 1) / q.bm : 0;

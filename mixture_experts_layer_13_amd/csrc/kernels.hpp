@@ -9,7 +9,8 @@ namespace moe {
 enum { kF32 = 0, kBF16 = 1, kINT4 = 2 };
 enum { kScoreSoftmax = 0, kScoreSigmoid = 1 };
 
-constexpr int kSmallMaxPairs = 2048;    // T*k handled by the many-block route with a one-wave permute
+constexpr int kSmallMaxPairs = 2048;    // T*k handled by the many-block route and its one-block permutation
+constexpr int kOneWaveMaxPairs = 256;   // up to here the small route's permutation runs on one wave
 // tokens per block of the small-T route launch: one block for a single token
 // (no hand-off), else a block per token up to 32 tokens, then 4 per block
 inline int route_small_tpb(int T) { return T <= 32 ? 1 : 4; }

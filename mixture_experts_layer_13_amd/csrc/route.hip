@@ -390,6 +390,46 @@ __device__ void permute_one_wave(const PermArgs& p, const int32_t* idx, const ui
   }
 }
 
+// The same permutation by a whole block, for many pairs: passes of blockDim.x
+// pairs in token-major order through rank_pass (which keeps each expert's
+// running count in base[], so ranks stay stable in t across passes), then the
+// capacity rule, the scan, the tile map (write_tile_map) and the placement, with
+// barriers between the phases.  Every thread of the block must call it.
+// LDS: base [256], off [257], tmp [512], wcnt [nwaves][256], pr [kSmallMaxPairs].
+__device__ void permute_block(const PermArgs& p, const int32_t* idx, const uint16_t* sel, int* base, int* off,
+                              int* tmp, int* wcnt, int* pr) {
+  const int tid = threadIdx.x, n = p.T * p.k, E = p.E;
+  for (int x = tid; x < 256; x += blockDim.x) base[x] = 0;  // ordered by the barriers inside rank_pass
+  for (int p0 = 0; p0 < n; p0 += blockDim.x) {
+    const int i = p0 + tid;
+    const int raw = i < n ? (idx ? idx[i] : (int)sel[i]) : -1;
+    const bool valid = raw >= 0 && raw < E;
+    const int e = valid ? raw : 0;
+    const int r = rank_pass(e, valid, wcnt, base, E);
+    if (i < n) pr[i] = valid ? r * 256 + e : -1;
+  }
+  __syncthreads();
+  for (int x = tid; x < E; x += blockDim.x) {
+    p.counts[x] = base[x];
+    tmp[x] = p.cap < 0 ? base[x] : min(base[x], p.cap);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int total = wave_exclusive_scan256(tmp, off, E);
+    if (tid == 0) off[E] = total;
+  }
+  __syncthreads();
+  for (int x = tid; x <= E; x += blockDim.x) p.offsets[x] = off[x];
+  if (p.items) {
+    for (int x = tid; x < E; x += blockDim.x) base[x] = tmp[x];  // kept per expert
+    write_tile_map(base, off, E, p.bm, p.items, p.n_items, tmp);
+  }
+  for (int i = tid; i < n; i += blockDim.x) {
+    const int v = pr[i];
+    place_pair(p, i, v & 255, v >= 0, v >> 8, off);
+  }
+}
+
 // For T*k <= kSmallMaxPairs (decode), E <= 64 EPL: block b takes tokens tpb*b .. +tpb-1.
 // Its threads add the KS K-chunk partial logits of those tokens (each output's
 // chunks in order by one lane, or split over KG lanes and added in a fixed
@@ -408,6 +448,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(const float* __restric
   __shared__ float sbias[256], ssel[256];
   __shared__ uint16_t sel[kSmallMaxPairs];
   __shared__ int base[256], off[257], tmp[512], pr[kSmallMaxPairs];
+  __shared__ int wcnt[4 * 256];
   __shared__ int last;
   const int tid = threadIdx.x, w = tid >> 6;
   const int T = ra.T, E = ra.E;
@@ -469,7 +510,8 @@ __global__ __launch_bounds__(256) void route_small_kernel(const float* __restric
       pidx = ra.idx;
     }
   }
-  if (w == 0) permute_one_wave(pa, pidx, psel, base, off, tmp, pr);
+  if (pa.T * pa.k > kOneWaveMaxPairs) permute_block(pa, pidx, psel, base, off, tmp, wcnt, pr);
+  else if (w == 0) permute_one_wave(pa, pidx, psel, base, off, tmp, pr);
 }
 
 // ------------------------------------------------------------------ fused router (large T)

@@ -260,7 +260,7 @@ def test_extreme_skew_single_hot_set():
         assert (out.float() == out[0:1].float()).all()
 
 
-@pytest.mark.parametrize("T", [40, 600])
+@pytest.mark.parametrize("T", [40, 100, 600])
 def test_permute_treats_invalid_indices_as_dropped(mid, T):
     sp, lay, ml = mid
     r = np.random.default_rng(T)
