@@ -32,7 +32,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 }
 
 constexpr int kSingleMaxT = 256;   // T up to which routing runs as split router + route_small
-static_assert(kSingleMaxT * kMaxK <= kSmallMaxPairs, "every small-T forward must fit the one-wave permutation");
+static_assert(kSingleMaxT * kMaxK <= kSmallMaxPairs, "every small-T forward must fit the small route's pair buffers");
 constexpr int kStreamMaxT = 64;    // T up to which the expert GEMMs use the streaming kernels
 constexpr int64_t kMaxT = 1 << 20;
 

@@ -430,7 +430,7 @@ __device__ void permute_block(const PermArgs& p, const int32_t* idx, const uint1
   }
 }
 
-// For T*k <= kSmallMaxPairs (decode), E <= 64 EPL: block b takes tokens tpb*b .. +tpb-1.
+// For T*k <= kSmallMaxPairs (T <= 256), E <= 64 EPL: block b takes tokens tpb*b .. +tpb-1.
 // Its threads add the KS K-chunk partial logits of those tokens (each output's
 // chunks in order by one lane, or split over KG lanes and added in a fixed
 // butterfly); the biases are fetched at entry, so the selection does not wait
@@ -438,8 +438,9 @@ __device__ void permute_block(const PermArgs& p, const int32_t* idx, const uint1
 // the picks stay in LDS and wave 0 ranks them.  Several blocks: each block
 // publishes its topk_idx rows (release fence, then one device-scope increment
 // of `arrived`, which the router launch zeroed), and the block that arrives
-// last ranks all pairs with one wave after an acquire fence.  do_route = 0:
-// one block permutes idx_in.
+// last ranks all pairs after an acquire fence: with one wave up to
+// kOneWaveMaxPairs pairs, else with the whole block.  do_route = 0: one block
+// permutes idx_in the same way.
 template <int EPL>
 __global__ __launch_bounds__(256) void route_small_kernel(const float* __restrict__ part, int KS, int tpb,
                                                           RouteArgs ra, const int32_t* idx_in, PermArgs pa,
