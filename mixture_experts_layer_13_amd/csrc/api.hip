@@ -127,11 +127,14 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     q.KS = 0;
     q.kchunk = q.d;
   }
-  q.rt = (q.E > 128 && q.act == MOE_BF16) ? 32 : 16;
+  // 16-token router tiles at every E: at E = 256 a 32-token tile needs 390 registers (one wave per
+  // SIMD) and was slower despite reading the router weight half as often (DeepSeek-V3 T=4096
+  // router 422 -> 163 us with 16-token tiles)
+  q.rt = 16;
   q.n_rt = (q.T + q.rt - 1) / q.rt;
   // at most kMaxRouteBlocks router (and permute) blocks, each over rpb consecutive router tiles:
   // every permute block sums the histograms of the blocks before it, so that work grows with the
-  // square of the block count (1024 blocks: at most 1 MB of reads per block at E = 256)
+  // square of the block count (512 blocks: at most 512 KB of reads per block at E = 256)
   q.rpb = (q.n_rt + kMaxRouteBlocks - 1) / kMaxRouteBlocks;
   if (q.rpb < 1) q.rpb = 1;
   q.n_rb = (q.n_rt + q.rpb - 1) / q.rpb;

@@ -17,7 +17,7 @@ inline int route_small_tpb(int T) { return T <= 32 ? 1 : 4; }
 // partial logits one small-T route block sums (K chunks x experts x its tokens)
 constexpr int kSmallPartials = 8192;
 constexpr int kPrefillRows = 128;       // rows per item in the tiled (large-M) expert kernels
-constexpr int kMaxRouteBlocks = 1024;   // large T: router / permute blocks at most (each over several tiles)
+constexpr int kMaxRouteBlocks = 512;    // large T: router / permute blocks at most (each over several tiles)
 
 struct RouteArgs {
   int T, d, E, k;

@@ -769,9 +769,6 @@ hipError_t launch_router_fused(int act, const void* x, const void* wr, const Rou
   if (act == kF32) {
     hipLaunchKernelGGL((router_fused_kernel<float, 1, 16>), grid, dim3(256), 0, s, (const float*)x, (const float*)wr,
                        ra, hist);
-  } else if (rt == 32) {
-    hipLaunchKernelGGL((router_fused_kernel<bf16, 2, 16>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
-                       hist);
   } else if (nb <= 4) {
     hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 4>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
                        hist);

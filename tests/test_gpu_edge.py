@@ -110,8 +110,8 @@ def test_combine_is_linear_in_the_gates(mid):
 
 
 def test_several_router_tiles_per_block(mid):
-    """Above 1024 router tiles each router and permute block takes several
-    consecutive tiles (T=20000: 1250 tiles of 16 tokens, 2 per block)."""
+    """Above 512 router tiles each router and permute block takes several
+    consecutive tiles (T=20000: 1250 tiles of 16 tokens, 3 per block)."""
     sp, lay, ml = mid
     x = S.make_tokens(sp, 20000, device="cuda", seed=11)
     run_and_check(sp, lay, ml, x, nsamp=300)
@@ -138,7 +138,7 @@ def _check_permutation(idx: np.ndarray, counts, offsets, row_token, slot_row, dr
 
 
 def test_largest_token_count():
-    """T = 2^20 (the API's limit): 65536 router tiles, 64 per block.  The GPU's own
+    """T = 2^20 (the API's limit): 65536 router tiles, 128 per block.  The GPU's own
     routing must be a valid top-k that agrees with the oracle on sampled tokens
     (dropless routing is per token), its permutation must follow the definition
     exactly, and sampled outputs must match the oracle."""
