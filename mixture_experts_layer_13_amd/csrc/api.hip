@@ -127,10 +127,11 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     q.KS = 0;
     q.kchunk = q.d;
   }
-  // 16-token router tiles at every E: at E = 256 a 32-token tile needs 390 registers (one wave per
-  // SIMD) and was slower despite reading the router weight half as often (DeepSeek-V3 T=4096
-  // router 422 -> 163 us with 16-token tiles)
-  q.rt = 16;
+  // router tokens per tile: 16 (router_fused_kernel), or 64 for bf16 with more than 128 experts
+  // from T = 8192 on (router_wide_kernel: the waves split the experts, so the 3.7 MB DeepSeek-V3
+  // router weight is read once per 64 tokens; measured there, T=16384 646 -> 219 us, T=8192
+  // 325 -> 206 us, but with fewer than 128 blocks it loses: T=4096 164 -> 200 us)
+  q.rt = (q.E > 128 && q.act == MOE_BF16 && q.T >= 8192) ? 64 : 16;
   q.n_rt = (q.T + q.rt - 1) / q.rt;
   // at most kMaxRouteBlocks router (and permute) blocks, each over rpb consecutive router tiles:
   // every permute block sums the histograms of the blocks before it, so that work grows with the

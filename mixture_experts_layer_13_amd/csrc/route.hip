@@ -622,6 +622,117 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict
   for (int xx = tid; xx < E; xx += blockDim.x) hist[(size_t)blockIdx.x * E + xx] = base[xx];
 }
 
+// Wide router for large E (bf16, 128 < E <= 256): a block takes 64-token tiles
+// (ra.tiles_per_block of them) and its four waves split the experts, wave w
+// computing experts 64 w .. 64 w + 63 over the whole K, so the router weight
+// (3.7 MB at DeepSeek-V3 size) is read once per 64 tokens instead of once per
+// 16.  The tile's token rows go through double-buffered LDS (64 K at a time,
+// shared by the four waves); each wave's router rows go straight from memory
+// into MFMA operands one stage ahead.  The logits then take the staging
+// space, and scoring, top-k and the block histogram follow as in
+// router_fused_kernel.
+__global__ __launch_bounds__(256, 2) void router_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ wr,
+                                                             RouteArgs ra, int32_t* __restrict__ hist) {
+  constexpr int TM = 64, KS = 128, LDX = KS + 8, LDL = 256 + 4;
+  constexpr int XCH = TM * KS / 8 / 256;  // 16-byte token-row chunks a thread stages per step
+  constexpr int SMEM = TM * LDL > TM * LDX ? TM * LDL : TM * LDX;  // floats: logits, or two bf16 staging buffers
+  __shared__ float smem[SMEM];
+  __shared__ uint16_t sel[TM * kMaxK];
+  __shared__ int wcnt[4 * 256];
+  __shared__ int base[256];
+  bf16* const xs = reinterpret_cast<bf16*>(smem);  // [2][TM][LDX] during the K loop
+  float* const slog = smem;                        // [TM][LDL] afterwards
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / 64, g = lane >> 4, c = lane & 15;
+  const int T = ra.T, E = ra.E, d = ra.d, k = ra.k;
+  const int nst = d / KS;
+  // this lane's router rows (B operand): experts 64 w + 16 nb + c, K offset 8 g of each 32-K slice
+  const bf16* pb[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) pb[nb] = wr + (size_t)min(64 * w + 16 * nb + c, E - 1) * d + 8 * g;
+  for (int xx = tid; xx < 256; xx += blockDim.x) base[xx] = 0;  // ordered before use by the barriers below
+  for (int tt = 0; tt < ra.tiles_per_block; ++tt) {
+    const int t0 = (blockIdx.x * ra.tiles_per_block + tt) * TM;
+    if (t0 >= T) break;  // block-uniform
+    // token-row chunks this thread stages: rows (tid + 256 q) / 16, 16-byte chunk tid % 16
+    const bf16* px[XCH];
+#pragma unroll
+    for (int q = 0; q < XCH; ++q) px[q] = x + (size_t)min(t0 + (tid + 256 * q) / 16, T - 1) * d + 8 * (tid % 16);
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 xr[XCH], b0[4][4], b1[4][4];
+    auto load_x = [&](int st) {
+#pragma unroll
+      for (int q = 0; q < XCH; ++q) xr[q] = ld16(px[q] + st * KS);
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+      for (int q = 0; q < XCH; ++q)
+        *reinterpret_cast<u32x4*>(&xs[(buf * TM + (tid + 256 * q) / 16) * LDX + 8 * (tid % 16)]) = xr[q];
+    };
+    auto load_w = [&](u32x4 (&bq)[4][4], int st) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) bq[sl][nb] = ld16(pb[nb] + st * KS + 32 * sl);
+    };
+    auto compute = [&](int buf, const u32x4 (&bq)[4][4]) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        u32x4 af[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          af[mt] = *reinterpret_cast<const u32x4*>(&xs[(buf * TM + 16 * mt + c) * LDX + 32 * sl + 8 * g]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) acc[mt][nb] = mma_bf16(af[mt], bq[sl][nb], acc[mt][nb]);
+      }
+    };
+    // two-step ping-pong, one step (128 K) ahead
+    load_w(b0, 0);
+    load_x(0);
+    store_x(0);
+    __syncthreads();
+    int st = 0;
+    for (; st + 2 <= nst; st += 2) {
+      load_x(min(st + 1, nst - 1));
+      load_w(b1, min(st + 1, nst - 1));
+      compute(0, b0);
+      store_x(1);
+      __syncthreads();
+      load_x(min(st + 2, nst - 1));
+      load_w(b0, min(st + 2, nst - 1));
+      compute(1, b1);
+      store_x(0);
+      __syncthreads();
+    }
+    if (st < nst) compute(0, b0);
+    __syncthreads();  // every wave is past its last read of the staging space
+    // logits into LDS
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slog[(16 * mt + 4 * g + i) * LDL + 64 * w + 16 * nb + c] = acc[mt][nb][i];
+    __syncthreads();
+    const int nt = min(TM, T - t0);
+    route_rows<4>(slog, LDL, nt, t0, ra, ra.logit_bias, sel, w, 4);
+    __syncthreads();  // sel[] complete; slog free for the next tile after the rank passes' barriers
+    const int np = nt * k;
+    for (int p0 = 0; p0 < np; p0 += blockDim.x) {
+      const int i = p0 + tid;
+      const int e = i < np ? (int)sel[i] : 0xFFFF;
+      rank_pass(e, e < E, wcnt, base, E);
+    }
+  }
+  __syncthreads();
+  for (int xx = tid; xx < E; xx += blockDim.x) hist[(size_t)blockIdx.x * E + xx] = base[xx];
+}
+
 // Tile histogram of given indices (for the standalone permute on large T).
 __global__ __launch_bounds__(512) void tile_hist_kernel(const int32_t* __restrict__ idx, int T, int k, int E, int rt,
                                                         int32_t* __restrict__ hist) {
@@ -769,6 +880,8 @@ hipError_t launch_router_fused(int act, const void* x, const void* wr, const Rou
   if (act == kF32) {
     hipLaunchKernelGGL((router_fused_kernel<float, 1, 16>), grid, dim3(256), 0, s, (const float*)x, (const float*)wr,
                        ra, hist);
+  } else if (rt == 64) {
+    hipLaunchKernelGGL(router_wide_kernel, grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra, hist);
   } else if (nb <= 4) {
     hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 4>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
                        hist);

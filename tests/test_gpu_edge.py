@@ -166,6 +166,28 @@ def test_largest_token_count():
     assert B.forward_launches(ml.cfg_for(T)) == 5
 
 
+# DeepSeek-V3 routing (sigmoid, selection bias, 2.5 x renormalised gates, a shared expert)
+# with more than 128 experts, where from T = 8192 on the router takes 64-token tiles and splits
+# the experts over its waves (T = 8492: a ragged last tile); E = 160 leaves one wave half and
+# one wave wholly past E; T = 1000 stays on 16-token tiles
+WIDE = S.SPECS["dsv3"].replace(name="wide_router", cfg_id=13, d=512, E=256, ffn=256, ffn_shared=256)
+
+
+@pytest.mark.parametrize("E,T,cap", [(256, 1000, None), (256, 8492, None), (160, 9000, None), (256, 8492, (5, 4))])
+def test_wide_router_many_experts(E, T, cap):
+    sp = WIDE.replace(E=E, capacity=cap)
+    lay = S.make_layer(sp, device="cuda")
+    ml = layer_of(sp, lay)
+    x = S.make_tokens(sp, T, device="cuda", seed=E + T)
+    out, idx, gates, drop, ref = run_and_check(sp, lay, ml, x, nsamp=300)
+    if cap is None:
+        assert not drop.cpu().numpy().any()
+    else:
+        # drops follow every earlier token's routing: compared when the routing agrees everywhere
+        if np.array_equal(idx.cpu().numpy(), ref["idx"]):
+            assert np.array_equal(drop.cpu().numpy().astype(bool), ref["drop"].astype(bool))
+
+
 def test_dense_limit_matches_textbook_swiglu():
     """E = 1, k = 1: the gate is softmax of one logit = 1, so the layer is a dense
     SwiGLU FFN.  Checked against the formula written out with scipy's expit."""
