@@ -337,6 +337,47 @@ __device__ __forceinline__ void place_pair(const PermArgs& p, int i, int e, bool
   }
 }
 
+// The permutation of one token's top-k picks (one wave, no barriers): the k
+// experts are distinct, so every count is 0 or 1 and the rows go to the picked
+// experts in expert order.  A pick's row is the number of kept picks with a
+// lower expert index (ballots over the lanes, lane = expert mod 64), each kept
+// expert gets one single-row item, and capacity only matters as cap = 0.
+__device__ void permute_single_token(const PermArgs& p, const uint16_t* sel, int* off) {
+  const int lane = lane_id(), E = p.E, k = p.k;
+  const bool keep = p.cap != 0;
+  int run = 0;
+  for (int j = 0; j * 64 < E; ++j) {
+    const int e = 64 * j + lane;
+    bool picked = false;
+    for (int i = 0; i < k; ++i) picked |= (int)sel[i] == e;
+    const uint64_t m = __ballot(picked && e < E);
+    const int o = run + (keep ? __popcll(m & lanemask_lt()) : 0);
+    if (e < E) {
+      p.counts[e] = picked ? 1 : 0;
+      p.offsets[e] = o;
+      off[e] = o;
+      if (p.items && keep && picked) p.items[o] = make_int4(e, o, 1, 0);
+    }
+    run += keep ? __popcll(m) : 0;
+  }
+  if (lane == 0) {
+    p.offsets[E] = run;
+    if (p.items) *p.n_items = run;
+  }
+  if (lane < k) {
+    const int e = sel[lane];
+    if (keep) {
+      const int row = off[e];
+      p.slot_row[lane] = row;
+      p.drop[lane] = 0;
+      p.row_token[row] = 0;
+    } else {
+      p.slot_row[lane] = -1;
+      p.drop[lane] = 1;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ small-T route + permute
 // Ranks every pair with one wave (no barriers): pair i = 64 j + lane.  One
 // pass in token-major order gives each pair its stable rank inside its expert
@@ -524,7 +565,9 @@ __global__ __launch_bounds__(256) void route_small_kernel(const float* __restric
       pidx = ra.idx;
     }
   }
-  if (pa.T * pa.k > kOneWaveMaxPairs) permute_block(pa, pidx, psel, base, off, tmp, wcnt, pr);
+  if (psel && pa.T == 1) {  // the picks of one token, from this kernel's own top-k
+    if (w == 0) permute_single_token(pa, psel, off);
+  } else if (pa.T * pa.k > kOneWaveMaxPairs) permute_block(pa, pidx, psel, base, off, tmp, wcnt, pr);
   else if (w == 0) permute_one_wave(pa, pidx, psel, base, off, tmp, pr);
 }
 

@@ -247,10 +247,10 @@ def test_capacity_zero_leaves_shared_experts():
 
 
 def test_capacity_zero_at_decode_sizes():
-    """Decode sizes fuse the combine into the down launch.  C = 0 drops every
-    routed pair: with a shared expert the output is the shared FFN (checked
-    against the oracle); with none, no down block is live and the output must
-    still be written, as exact zeros."""
+    """Decode sizes (T = 1 takes the single-token permutation): C = 0 drops every
+    routed pair.  With a shared expert the output is the shared FFN (checked
+    against the oracle); with none, no expert block is live and the combine
+    must still write the output, as exact zeros."""
     sp = S.SPECS["dsv2_lite"].replace(name="capzero_dec", cfg_id=18, d=512, E=16, ffn=256, ffn_shared=256,
                                       capacity=(0, 1))
     lay = S.make_layer(sp, device="cuda")
