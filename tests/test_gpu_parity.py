@@ -53,7 +53,7 @@ def check_capacity_rule(idx, drop, E, cap):
 
 
 CASES = [("tiny_f32", 64), ("olmoe", 1), ("olmoe", 8), ("olmoe", 32), ("olmoe", 64), ("olmoe", 4096),
-         ("dsv2_lite", 8192), ("dsv2_lite_cap", 8192), ("qwen3_int4", 32), ("qwen3_int4", 4096),
+         ("dsv2_lite", 8192), ("dsv2_lite_cap", 8192), ("qwen3_int4", 1), ("qwen3_int4", 32), ("qwen3_int4", 4096),
          ("dsv3", 1), ("dsv3", 16), ("dsv3", 256), ("dsv3", 4096), ("dsv3", 16384)]
 
 
@@ -101,9 +101,9 @@ def test_forward_matches_oracle(name, T):
     assert rel.max(initial=0) <= tol_of(sp)
 
 
-@pytest.mark.parametrize("name,T", [("tiny_f32", 64), ("olmoe", 8), ("olmoe", 300), ("olmoe", 20000),
+@pytest.mark.parametrize("name,T", [("tiny_f32", 64), ("olmoe", 1), ("olmoe", 8), ("olmoe", 300), ("olmoe", 20000),
                                     ("dsv2_lite_cap", 8192),
-                                    ("qwen3_int4", 32)])
+                                    ("qwen3_int4", 1), ("qwen3_int4", 32), ("dsv3", 1)])
 def test_split_path_reproduces_forward_bitwise(name, T):
     """Replaying the layer's own routes through route -> permute -> expert_ffn ->
     combine returns the fused forward's output exactly (the route-replay control)."""
