@@ -24,8 +24,9 @@ Sources (the pages this follows):
   [MoE-inf]  "MoE at the inference level ..." -- Workarounds (int4 expert
              weights, auxiliary-loss-free bias term).
   [MoE-res]  "MoE Research", section 2 (shared always-on experts;
-             loss-free balancing bias used for selection) and section 7A
-             (experts-touched formula E*(1-(1-k/E)^B)).
+             loss-free balancing bias used for selection; node-limited
+             routing: a token's experts come from at most M nodes) and
+             section 7A (experts-touched formula E*(1-(1-k/E)^B)).
 Readings where the pages are silent (the SwiGLU definition, gate
 renormalisation, capacity priority, INT4 format, ...) are listed in the
 repository's design notes and restated at each function below.
@@ -128,6 +129,31 @@ def select_topk(key: np.ndarray, k: int):
     return idx, margin
 
 
+def limit_groups(key: np.ndarray, n_groups: int, topk_groups: int):
+    """Group-limited selection ([MoE-res] section 2, node-limited routing; [MoE-inf]
+    workarounds, device-limited routing with M = 4): a token's k experts must come
+    from at most M = topk_groups of the n_groups groups.
+
+    Reading (the pages name the constraint, not the rule that picks the groups):
+    the experts form n_groups equal groups of consecutive indices (group of e is
+    e // (E / n_groups)); a group's score is the largest selection key in it; the
+    M groups with the largest scores are kept (equal scores: the lower group
+    first); every expert outside them gets key -inf, so the top-k that follows
+    picks only inside them.  Returns (masked key, group margin [T] = M-th group
+    score minus the (M+1)-th, +inf when M == n_groups)."""
+    key = np.asarray(key, np.float64) + 0.0
+    T, E = key.shape
+    if E % n_groups or not 1 <= topk_groups <= n_groups:
+        raise ValueError((E, n_groups, topk_groups))
+    gsz = E // n_groups
+    gscore = key.reshape(T, n_groups, gsz).max(axis=2)
+    keep, gmargin = select_topk(gscore, topk_groups)
+    allowed = np.zeros((T, n_groups), bool)
+    np.put_along_axis(allowed, keep.astype(np.int64), True, axis=1)
+    masked = np.where(np.repeat(allowed, gsz, axis=1), key, -np.inf)
+    return masked, gmargin
+
+
 def gate_weights(scores: np.ndarray, idx: np.ndarray, renorm: bool, scale: float) -> np.ndarray:
     """g[t, j] = scale * score[t, idx[t, j]] (/ sum_j' score[t, idx[t, j']] when renorm).
 
@@ -219,11 +245,13 @@ def moe_layer(x: np.ndarray, w_router: np.ndarray, experts: ExpertFn, E: int, k:
               score: str = "softmax", renorm: bool = False, gate_scale: float = 1.0,
               logit_bias: Optional[np.ndarray] = None, select_bias: Optional[np.ndarray] = None,
               capacity: Optional[tuple] = None, shared: Optional[ExpertFn] = None, n_shared: int = 0,
-              ffn_rows: Optional[np.ndarray] = None, routes: Optional[tuple] = None) -> dict:
+              ffn_rows: Optional[np.ndarray] = None, routes: Optional[tuple] = None,
+              groups: Optional[tuple] = None) -> dict:
     """The whole layer, step by step.
 
     1. logits = x W_r (+ skew bias); 2. scores (softmax, or sigmoid);
     3. selection key = score (+ selection-only bias for sigmoid scoring);
+    3b. groups = (n_groups, M): keys outside the token's M best groups -> -inf;
     4. top-k with lowest-index ties; 5. gates; 6. capacity / assignment;
     7. every kept (t, j): y = FFN_{idx[t,j]}(x_t); 8. out_t = sum over kept j of
     g[t,j] * y + sum over shared experts of FFN_s(x_t) (weight 1, never dropped).
@@ -245,6 +273,9 @@ def moe_layer(x: np.ndarray, w_router: np.ndarray, experts: ExpertFn, E: int, k:
         key = scores if select_bias is None else scores + np.asarray(select_bias, np.float64)[None, :]
     else:
         raise ValueError(score)
+    group_margin = np.full(T, np.inf)
+    if groups is not None:
+        key, group_margin = limit_groups(key, groups[0], groups[1])
     idx, margin = select_topk(key, k)
     gates = gate_weights(scores, idx, renorm, gate_scale)
     if routes is not None:
@@ -272,7 +303,7 @@ def moe_layer(x: np.ndarray, w_router: np.ndarray, experts: ExpertFn, E: int, k:
         wg, wu, wd = shared(s)
         out[rows] += swiglu_ffn(x[rows], wg, wu, wd)
     return dict(out=out, logits=logits, scores=scores, key=key, idx=idx, gates=gates,
-                margin=margin, cap=cap, **asg)
+                margin=margin, group_margin=group_margin, cap=cap, **asg)
 
 
 def experts_touched_expected(E: int, k: int, B: int) -> float:

@@ -110,6 +110,90 @@ def test_topk_matches_brute_force_full_sort_with_ties(E, k):
             assert margin[t] == np.inf
 
 
+# ---------------------------------------------------------------- group-limited selection
+def test_group_limit_worked_example():
+    """E = 8 in 4 groups of 2, M = 2, k = 3, worked by hand.  Group maxima are
+    0.30, 0.22, 0.25, 0.05, so groups 0 and 2 stay and the picks are 0, 4, 5;
+    plain top-3 is 0, 4, 2.  Scoring groups by their sum (0.31, 0.43, 0.27, 0.05)
+    would keep groups 1 and 0 (picks 0, 2, 3), and interleaved groups (e mod 4)
+    would allow {0, 2, 4, 6} (picks 0, 4, 2): both fail here."""
+    key = np.array([[0.30, 0.01, 0.22, 0.21, 0.25, 0.02, 0.05, 0.00]])
+    masked, gm = O.limit_groups(key, 4, 2)
+    assert np.isneginf(masked[0, [2, 3, 6, 7]]).all()
+    assert (masked[0, [0, 1, 4, 5]] == key[0, [0, 1, 4, 5]]).all()
+    assert O.select_topk(masked, 3)[0][0].tolist() == [0, 4, 5]
+    assert O.select_topk(key, 3)[0][0].tolist() == [0, 4, 2]
+    assert gm[0] == pytest.approx(0.25 - 0.22)  # 2nd and 3rd group maxima
+    # equal group maxima: the lower group stays
+    tie = np.array([[0.5, 0.1, 0.2, 0.5, 0.4, 0.5]])
+    m2, gm2 = O.limit_groups(tie, 3, 2)
+    assert np.isneginf(m2[0, 4:]).all() and np.isfinite(m2[0, :4]).all() and gm2[0] == 0.0
+
+
+@pytest.mark.parametrize("E,G,M", [(8, 4, 2), (12, 3, 1), (16, 8, 3), (6, 6, 4)])
+def test_group_limit_brute_force(E, G, M):
+    """Every kept group's maximum is >= every dropped group's (on equal maxima the
+    kept group has the lower index); keys inside kept groups are untouched, all
+    others -inf; at most M groups carry a pick, and the overall best expert is
+    always picked."""
+    key = rng.integers(0, 6, size=(200, E)).astype(np.float64)  # many exact ties
+    masked, gm = O.limit_groups(key, G, M)
+    gsz = E // G
+    for t in range(key.shape[0]):
+        gmax = [max(key[t, g * gsz:(g + 1) * gsz]) for g in range(G)]
+        kept = [g for g in range(G) if np.isfinite(masked[t, g * gsz])]
+        assert len(kept) == M
+        for g in range(G):
+            inside = masked[t, g * gsz:(g + 1) * gsz]
+            if g in kept:
+                assert (inside == key[t, g * gsz:(g + 1) * gsz]).all()
+            else:
+                assert np.isneginf(inside).all()
+                for h in kept:
+                    assert gmax[h] > gmax[g] or (gmax[h] == gmax[g] and h < g)
+        srt = sorted(gmax, reverse=True)
+        assert gm[t] == (srt[M - 1] - srt[M] if M < G else np.inf)
+        for k in range(1, M * gsz + 1):
+            picks = O.select_topk(masked[t:t + 1], k)[0][0]
+            assert len({int(e) // gsz for e in picks}) <= M
+            assert int(picks[0]) == _brute_topk(key[t].tolist(), 1)[0]
+
+
+def test_group_limit_special_cases():
+    """M = n_groups and n_groups = 1 change nothing; groups of one expert with
+    M = k reduce to the plain top-k."""
+    key = rng.normal(size=(50, 16))
+    assert (O.limit_groups(key, 4, 4)[0] == key).all()
+    assert (O.limit_groups(key, 1, 1)[0] == key).all()
+    for k in (1, 3, 8):
+        assert (O.select_topk(O.limit_groups(key, 16, k)[0], k)[0] == O.select_topk(key, k)[0]).all()
+    with pytest.raises(ValueError):
+        O.limit_groups(key, 5, 2)
+    with pytest.raises(ValueError):
+        O.limit_groups(key, 4, 5)
+
+
+def test_group_limited_layer():
+    """Through the whole layer: M = n_groups gives the ungrouped result; M < n_groups
+    keeps each token's picks inside M groups, and its gates still follow the
+    unbiased scores of the picks."""
+    E, d, k = 16, 8, 4
+    x = rng.normal(size=(40, d))
+    wr = rng.normal(size=(E, d))
+    ex = _experts_fn(_rand_experts(E, d, 5))
+    sb = rng.normal(size=E) * 0.1
+    base = O.moe_layer(x, wr, ex, E, k, score="sigmoid", select_bias=sb, renorm=True, gate_scale=2.5)
+    same = O.moe_layer(x, wr, ex, E, k, score="sigmoid", select_bias=sb, renorm=True, gate_scale=2.5,
+                       groups=(4, 4))
+    assert (same["idx"] == base["idx"]).all() and np.array_equal(same["out"], base["out"])
+    lim = O.moe_layer(x, wr, ex, E, k, score="sigmoid", select_bias=sb, renorm=True, gate_scale=2.5,
+                      groups=(4, 1))
+    assert all(len(set((lim["idx"][t] // 4).tolist())) == 1 for t in range(40))
+    assert (lim["idx"] != base["idx"]).any()
+    g = np.take_along_axis(lim["scores"], lim["idx"].astype(np.int64), axis=1)
+    assert np.allclose(lim["gates"], 2.5 * g / g.sum(axis=1, keepdims=True))
+
+
 def test_zero_router_gives_lowest_indices():
     """W_r = 0 and no bias: every key ties, so every token selects experts 0..k-1."""
     x = rng.normal(size=(10, 6))
