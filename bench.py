@@ -115,7 +115,7 @@ def moe_layer(sp, lay, layout):
     from mixture_experts_layer_13_amd.layer import MoeLayer
     cfg = B.make_cfg(1, sp.d, sp.E, sp.k, sp.ffn, sp.n_shared, sp.ffn_shared, act=sp.act, expert=sp.expert,
                      score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale, capacity=sp.capacity,
-                     layout=layout)
+                     layout=layout, groups=sp.groups)
     mats = [lay.w_gate, lay.w_up, lay.w_down, lay.sh_gate, lay.sh_up, lay.sh_down]
     if layout == "tiled":
         mats = [None if m is None else B.pack_tiled(m, sp.expert) for m in mats]

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -70,7 +70,13 @@ typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
  * 1 <= k <= min(E, 8), d, ffn, ffn_shared multiples of 128, 0 <= n_shared <= 8,
  * act_dtype MOE_F32 or MOE_BF16 (x, w_router, y_rows, y_shared, out),
  * expert_dtype equal to act_dtype, or MOE_INT4_G128 with act_dtype MOE_BF16,
- * and every expert matrix (ffn x d, ffn_shared x d) under 2 GiB. */
+ * and every expert matrix (ffn x d, ffn_shared x d) under 2 GiB.
+ * Group-limited selection ("MoE Research", section 2, node-limited routing;
+ * "MoE at the inference level", workarounds, device-limited routing): with
+ * n_groups = G > 0 the experts form G equal groups of consecutive indices
+ * (E % G == 0, G <= 64), a group scores the largest selection key in it, and a
+ * token picks its k experts only inside its topk_groups = M best groups (equal
+ * group scores: the lower group), 1 <= M <= G, k <= M * E / G.  0 / 0: none. */
 typedef struct moe_cfg {
   int32_t T;            /* tokens                                              */
   int32_t d;            /* hidden size                                         */
@@ -87,6 +93,8 @@ typedef struct moe_cfg {
   int32_t cap_num;      /* capacity factor C = cap_num / cap_den;              */
   int32_t cap_den;      /*   0 / 0 = dropless; cap_num = 0 drops every pair    */
   int32_t weight_layout; /* moe_layout of the routed and shared expert weights  */
+  int32_t n_groups;     /* expert groups for group-limited selection (0: none) */
+  int32_t topk_groups;  /* groups a token may pick from (0: none)              */
 } moe_cfg;
 
 /* Expert weights (device pointers, layout above).  s_* are the INT4 scales

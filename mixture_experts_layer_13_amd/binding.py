@@ -33,12 +33,16 @@ class MoeError(RuntimeError):
         self.status = status
 
 
+ABI_VERSION = 3  # MOE_ABI_VERSION of include/moe.h
+
+
 class MoeCfg(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("ffn", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("ffn_shared", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("gate_scale", ctypes.c_float), ("cap_num", ctypes.c_int32),
-                ("cap_den", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
+                ("cap_den", ctypes.c_int32), ("weight_layout", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32)]
 
 
 class MoeExperts(ctypes.Structure):
@@ -74,6 +78,9 @@ def _load() -> ctypes.CDLL:
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = res, args
+    if lib.moe_abi_version() != ABI_VERSION:  # MoeCfg above mirrors that version's moe_cfg
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.moe_abi_version()}, the binding expects {ABI_VERSION}: "
+                          "rebuild it")
     return lib
 
 
@@ -83,10 +90,12 @@ lib = _load()
 # ---------------------------------------------------------------- config helpers
 def make_cfg(T: int, d: int, E: int, k: int, ffn: int, n_shared: int = 0, ffn_shared: int = 0,
              act: str = "bf16", expert: str = "bf16", score: str = "softmax", renorm: bool = False,
-             gate_scale: float = 1.0, capacity: Optional[tuple] = None, layout: str = "rows") -> MoeCfg:
+             gate_scale: float = 1.0, capacity: Optional[tuple] = None, layout: str = "rows",
+             groups: Optional[tuple] = None) -> MoeCfg:
     cn, cd = capacity if capacity is not None else (0, 0)
+    gn, gm = groups if groups is not None else (0, 0)
     return MoeCfg(T, d, E, k, ffn, n_shared, ffn_shared, _DTYPES[act], _DTYPES[expert], _SCORES[score],
-                  int(bool(renorm)), float(gate_scale), cn, cd, _LAYOUTS[layout])
+                  int(bool(renorm)), float(gate_scale), cn, cd, _LAYOUTS[layout], gn, gm)
 
 
 def cfg_with_T(cfg: MoeCfg, T: int) -> MoeCfg:

@@ -38,6 +38,7 @@ constexpr int64_t kMaxT = 1 << 20;
 
 struct Plan {
   int T, d, E, k, F, S, FS, act, wdt, score, renorm, tiled;
+  int G, GM;  // expert groups, groups a token may pick from (0: no group limit)
   float gscale;
   int64_t cap;  // -1: dropless
   int64_t R;
@@ -84,6 +85,13 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     if (bytes >= ((int64_t)1 << 31))
       return fail(MOE_ERR_UNSUPPORTED, "an expert matrix of %lld bytes exceeds 2 GiB", (long long)bytes);
   }
+  if (!(c->n_groups == 0 && c->topk_groups == 0)) {
+    if (c->n_groups < 1 || c->n_groups > 64 || c->E % c->n_groups)
+      return fail(MOE_ERR_UNSUPPORTED, "n_groups=%d: need 0, or 1..64 dividing E=%d", c->n_groups, c->E);
+    if (c->topk_groups < 1 || c->topk_groups > c->n_groups || c->k > c->topk_groups * (c->E / c->n_groups))
+      return fail(MOE_ERR_INVALID_ARG, "topk_groups=%d: need 1..n_groups with k <= topk_groups * E / n_groups",
+                  c->topk_groups);
+  }
   const bool dropless = c->cap_num == 0 && c->cap_den == 0;
   if (!dropless && (c->cap_den <= 0 || c->cap_num < 0))
     return fail(MOE_ERR_INVALID_ARG, "capacity %d/%d: need 0/0 or num >= 0, den > 0", c->cap_num, c->cap_den);
@@ -98,6 +106,8 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   q.FS = c->n_shared ? c->ffn_shared : 0;
   q.act = c->act_dtype;
   q.wdt = c->expert_dtype;
+  q.G = c->n_groups;
+  q.GM = c->topk_groups;
   q.score = c->score;
   q.renorm = c->renorm;
   q.gscale = c->gate_scale;
@@ -226,6 +236,8 @@ RouteArgs route_args(const Plan& p, const float* lb, const float* sb, int32_t* i
   r.gates = gates;
   r.scores = scores;
   r.tiles_per_block = p.rpb;
+  r.n_groups = p.G;
+  r.topk_groups = p.GM;
   return r;
 }
 

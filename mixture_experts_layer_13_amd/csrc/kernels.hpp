@@ -29,7 +29,8 @@ struct RouteArgs {
   int32_t* idx;              // [T][k]
   float* gates;              // [T][k]
   float* scores;             // [T][E] or null
-  int tiles_per_block;       // large-T router: consecutive 16/32-token tiles per block (>= 1)
+  int tiles_per_block;       // large-T router: consecutive 16/64-token tiles per block (>= 1)
+  int n_groups, topk_groups; // group-limited selection (topk_groups < n_groups), else 0 / 0
 };
 
 struct PermArgs {

@@ -40,10 +40,13 @@ template <> struct Chunk<float> {
 // k rounds; each takes the wave-wide maximum of the fp32 keys in a monotone
 // 32-bit encoding, then, among the entries holding that maximum, the lowest
 // expert index (ballots over the lanes' best entries), so equal keys select
-// the lower index and slots come out in descending key order.  Gates: the
+// the lower index and slots come out in descending key order.  Group-limited
+// selection first zeroes the keys outside the token's topk_groups best groups
+// (group score: its largest key; equal scores keep the lower group).  Gates: the
 // selected unbiased scores (renormalised over the k picks when asked), times
 // gate_scale.  Tokens i >= nvalid are computed but not written.
-template <int NT, int EPL>
+// GRP: the group-limited step is compiled in (kernels without it keep their registers).
+template <int NT, int EPL, bool GRP = false>
 __device__ __forceinline__ void route_tokens(float (&logit)[NT][EPL], const RouteArgs& a, int t0, int nvalid,
                                              uint16_t* sel) {
   const int lane = lane_id();
@@ -103,6 +106,52 @@ __device__ __forceinline__ void route_tokens(float (&logit)[NT][EPL], const Rout
     if (lane + 64 * j >= E)
 #pragma unroll
       for (int i = 0; i < NT; ++i) key[i][j] = 0u;
+  if (GRP) {
+    const int G = a.n_groups, gsz = E / G;
+    int grp[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) grp[j] = (lane + 64 * j) / gsz;  // >= G past E (keys 0 there)
+    uint32_t gk[NT];  // lane g < G: the score of group g
+#pragma unroll
+    for (int i = 0; i < NT; ++i) gk[i] = 0u;
+    for (int gi = 0; gi < G; ++gi) {
+      uint32_t m[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        m[i] = 0u;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (grp[j] == gi) m[i] = max(m[i], key[i][j]);
+      }
+      wave_max_u32_n<NT>(m);
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        if (lane == gi) gk[i] = m[i];
+    }
+    uint64_t keep[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) keep[i] = 0ull;
+    for (int r = 0; r < a.topk_groups; ++r) {
+      uint32_t b[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) b[i] = (lane < G && !((keep[i] >> lane) & 1ull)) ? gk[i] : 0u;
+      uint32_t top[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) top[i] = b[i];
+      wave_max_u32_n<NT>(top);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        // lowest group among the not yet kept ones holding the maximum
+        const uint64_t bl = __ballot(lane < G && !((keep[i] >> lane) & 1ull) && b[i] == top[i]);
+        keep[i] |= 1ull << (__ffsll((unsigned long long)bl) - 1);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (grp[j] >= G || !((keep[i] >> grp[j]) & 1ull)) key[i][j] = 0u;
+  }
   float gsum[NT], sel_s[NT];
   int sel_e[NT];
 #pragma unroll
@@ -181,7 +230,7 @@ __device__ __forceinline__ void load_logits(float (&logit)[NT][EPL], const float
 }
 
 // Routes tokens [0, nt) whose logits sit in LDS rows (wave w takes groups of 4).
-template <int EPL>
+template <int EPL, bool GRP>
 __device__ void route_rows(const float* slog, int ld, int nt, int t0, const RouteArgs& ra, const float* bias,
                            uint16_t* sel, int w, int nw) {
   const int k = ra.k;
@@ -189,12 +238,12 @@ __device__ void route_rows(const float* slog, int ld, int nt, int t0, const Rout
     if (nt - t4 >= 4) {
       float logit[4][EPL];
       load_logits<4, EPL>(logit, slog + t4 * ld, ld, ra.E, bias);
-      route_tokens<4, EPL>(logit, ra, t0 + t4, 4, sel + t4 * k);
+      route_tokens<4, EPL, GRP>(logit, ra, t0 + t4, 4, sel + t4 * k);
     } else {
       for (int i = t4; i < nt; ++i) {
         float logit[1][EPL];
         load_logits<1, EPL>(logit, slog + i * ld, ld, ra.E, bias);
-        route_tokens<1, EPL>(logit, ra, t0 + i, 1, sel + i * k);
+        route_tokens<1, EPL, GRP>(logit, ra, t0 + i, 1, sel + i * k);
       }
     }
   }
@@ -495,7 +544,7 @@ __device__ void permute_block(const PermArgs& p, const int32_t* idx, const uint1
 // last ranks all pairs after an acquire fence: with one wave up to
 // kOneWaveMaxPairs pairs, else with the whole block.  do_route = 0: one block
 // permutes idx_in the same way.
-template <int EPL>
+template <int EPL, bool GRP>
 __global__ __launch_bounds__(256) void route_small_kernel(const float* __restrict__ part, int KS, int tpb,
                                                           RouteArgs ra, const int32_t* idx_in, PermArgs pa,
                                                           int do_route, int do_perm, int32_t* arrived) {
@@ -547,7 +596,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(const float* __restric
     if (w < nt) {
       float lg[1][EPL];
       load_logits<1, EPL>(lg, slog + w * E, E, E, bias);
-      route_tokens<1, EPL>(lg, rl, t0 + w, 1, one ? sel + w * ra.k : nullptr);
+      route_tokens<1, EPL, GRP>(lg, rl, t0 + w, 1, one ? sel + w * ra.k : nullptr);
     }
     if (!do_perm) return;
     if (one) {
@@ -578,7 +627,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(const float* __restric
 // scores and selects each token (a wave per token) and adds the tile's picks to
 // the block's expert histogram, which it writes once at the end.  NB = experts / 16 held
 // per wave (compile-time bound, E <= 16 * NB).
-template <typename TIN, int MT, int NB>
+template <typename TIN, int MT, int NB, bool GRP>
 __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict__ x, const TIN* __restrict__ wr,
                                                            RouteArgs ra, int32_t* __restrict__ hist) {
   constexpr int EPC = Chunk<TIN>::EPC;
@@ -650,7 +699,7 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict
       __syncthreads();
     }
     const int nt = min(TM, T - t0);
-    route_rows<(16 * NB + 63) / 64>(slog, LD, nt, t0, ra, ra.logit_bias, sel, w, 4);
+    route_rows<(16 * NB + 63) / 64, GRP>(slog, LD, nt, t0, ra, ra.logit_bias, sel, w, 4);
     // the tile's pairs into the block histogram (sel[] is complete only after this barrier; the
     // next tile overwrites slog and sel only after the barriers inside the rank passes)
     __syncthreads();
@@ -674,6 +723,7 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const TIN* __restrict
 // into MFMA operands one stage ahead.  The logits then take the staging
 // space, and scoring, top-k and the block histogram follow as in
 // router_fused_kernel.
+template <bool GRP>
 __global__ __launch_bounds__(256, 2) void router_wide_kernel(const bf16* __restrict__ x, const bf16* __restrict__ wr,
                                                              RouteArgs ra, int32_t* __restrict__ hist) {
   constexpr int TM = 64, KS = 128, LDX = KS + 8, LDL = 256 + 4;
@@ -763,7 +813,7 @@ __global__ __launch_bounds__(256, 2) void router_wide_kernel(const bf16* __restr
         for (int i = 0; i < 4; ++i) slog[(16 * mt + 4 * g + i) * LDL + 64 * w + 16 * nb + c] = acc[mt][nb][i];
     __syncthreads();
     const int nt = min(TM, T - t0);
-    route_rows<4>(slog, LDL, nt, t0, ra, ra.logit_bias, sel, w, 4);
+    route_rows<4, GRP>(slog, LDL, nt, t0, ra, ra.logit_bias, sel, w, 4);
     __syncthreads();  // sel[] complete; slog free for the next tile after the rank passes' barriers
     const int np = nt * k;
     for (int p0 = 0; p0 < np; p0 += blockDim.x) {
@@ -906,35 +956,47 @@ hipError_t launch_router_partial(int act, const void* x, const void* wr, int T, 
   return hipGetLastError();
 }
 
+// the group-limited step is needed (fewer groups kept than there are)
+static bool route_groups(const RouteArgs& ra) { return ra.topk_groups > 0 && ra.topk_groups < ra.n_groups; }
+
 hipError_t launch_route_small(const float* part, int KS, const RouteArgs& ra, const int32_t* idx_in,
                               const PermArgs& pa, int do_route, int do_perm, int32_t* arrived, hipStream_t s) {
   const int tpb = route_small_tpb(ra.T);
   const int grid = do_route ? (ra.T + tpb - 1) / tpb : 1;
-  auto kern = ra.E <= 64 ? route_small_kernel<1> : (ra.E <= 128 ? route_small_kernel<2> : route_small_kernel<4>);
+  auto kern = route_groups(ra)
+                  ? (ra.E <= 64 ? route_small_kernel<1, true>
+                                : (ra.E <= 128 ? route_small_kernel<2, true> : route_small_kernel<4, true>))
+                  : (ra.E <= 64 ? route_small_kernel<1, false>
+                                : (ra.E <= 128 ? route_small_kernel<2, false> : route_small_kernel<4, false>));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, part, KS, tpb, ra, idx_in, pa, do_route, do_perm, arrived);
   return hipGetLastError();
 }
 
-hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int rt, int32_t* hist,
-                               hipStream_t s) {
+template <bool GRP>
+void launch_router_fused_t(int act, const void* x, const void* wr, const RouteArgs& ra, int rt, int32_t* hist,
+                           hipStream_t s) {
   const int span = rt * ra.tiles_per_block;
   dim3 grid((ra.T + span - 1) / span);
   const int nb = (ra.E + 15) / 16;
+  const bf16 *xb = (const bf16*)x, *wb = (const bf16*)wr;
   if (act == kF32) {
-    hipLaunchKernelGGL((router_fused_kernel<float, 1, 16>), grid, dim3(256), 0, s, (const float*)x, (const float*)wr,
-                       ra, hist);
+    hipLaunchKernelGGL((router_fused_kernel<float, 1, 16, GRP>), grid, dim3(256), 0, s, (const float*)x,
+                       (const float*)wr, ra, hist);
   } else if (rt == 64) {
-    hipLaunchKernelGGL(router_wide_kernel, grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra, hist);
+    hipLaunchKernelGGL(router_wide_kernel<GRP>, grid, dim3(256), 0, s, xb, wb, ra, hist);
   } else if (nb <= 4) {
-    hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 4>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
-                       hist);
+    hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 4, GRP>), grid, dim3(256), 0, s, xb, wb, ra, hist);
   } else if (nb <= 8) {
-    hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 8>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
-                       hist);
+    hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 8, GRP>), grid, dim3(256), 0, s, xb, wb, ra, hist);
   } else {
-    hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 16>), grid, dim3(256), 0, s, (const bf16*)x, (const bf16*)wr, ra,
-                       hist);
+    hipLaunchKernelGGL((router_fused_kernel<bf16, 1, 16, GRP>), grid, dim3(256), 0, s, xb, wb, ra, hist);
   }
+}
+
+hipError_t launch_router_fused(int act, const void* x, const void* wr, const RouteArgs& ra, int rt, int32_t* hist,
+                               hipStream_t s) {
+  if (route_groups(ra)) launch_router_fused_t<true>(act, x, wr, ra, rt, hist, s);
+  else launch_router_fused_t<false>(act, x, wr, ra, rt, hist, s);
   return hipGetLastError();
 }
 

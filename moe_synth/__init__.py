@@ -58,6 +58,7 @@ class LayerSpec:
     rms_norm_x: bool
     tokens: tuple         # token counts the layer is exercised at
     capacity: Optional[tuple] = None  # (num, den) for C = num/den, None = dropless
+    groups: Optional[tuple] = None    # (n_groups, topk_groups) for group-limited selection, None = none
 
     def replace(self, **kw) -> "LayerSpec":
         return dataclasses.replace(self, **kw)

@@ -25,7 +25,7 @@ def _B():
 def cfg_of(sp: S.LayerSpec, T: int, layout: str = "rows"):
     return _B().make_cfg(T, sp.d, sp.E, sp.k, sp.ffn, sp.n_shared, sp.ffn_shared, act=sp.act, expert=sp.expert,
                          score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale, capacity=sp.capacity,
-                         layout=layout)
+                         layout=layout, groups=sp.groups)
 
 
 def layer_of(sp: S.LayerSpec, lay: S.Layer, layout: str = "rows"):
@@ -77,7 +77,7 @@ def oracle_run(sp: S.LayerSpec, lay: S.Layer, x: torch.Tensor, ffn_rows=None, ro
                        renorm=sp.renorm, gate_scale=sp.gate_scale, logit_bias=to_f64(lay.logit_bias),
                        select_bias=to_f64(lay.select_bias), capacity=sp.capacity,
                        shared=ExpertSource(sp, lay, shared=True) if sp.n_shared else None, n_shared=sp.n_shared,
-                       ffn_rows=ffn_rows, routes=routes)
+                       ffn_rows=ffn_rows, routes=routes, groups=sp.groups)
 
 
 def min_gap(key: np.ndarray, k: int) -> np.ndarray:
@@ -100,7 +100,8 @@ class RouteReport:
 
 
 def compare_routes(gpu_idx: np.ndarray, ref: dict, k: int) -> RouteReport:
-    margin = ref["margin"]
+    # a near-tie between the last kept and the first dropped group is a near-tie of the route too
+    margin = np.minimum(ref["margin"], ref.get("group_margin", np.inf))
     same_set = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(gpu_idx, ref["idx"])])
     same_order = (gpu_idx == ref["idx"]).all(1)
     gaps = min_gap(ref["key"], k)

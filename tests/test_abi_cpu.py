@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     lib.moe_abi_version.restype = ctypes.c_int32
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 @pytest.fixture(scope="module")
@@ -65,6 +65,16 @@ def test_validation_errors(B):
     assert B.validate(B.make_cfg(4, 32768, 8, 2, 16384)) == B.MOE_OK               # 1 GiB
     assert B.validate(B.make_cfg(4, 32768, 8, 2, 16384, act="f32", expert="f32")) == B.MOE_ERR_UNSUPPORTED
     assert B.validate(B.make_cfg(4, 1024, 8, 2, 512, 1, 1 << 20)) != B.MOE_OK
+    # group-limited selection: G divides E, G <= 64, 1 <= M <= G, k <= M * E / G; 0 / 0 = none
+    g = lambda grp, E=256, k=8: B.validate(B.make_cfg(16, 1024, E, k, 512, score="sigmoid", groups=grp))
+    assert g((8, 4)) == B.MOE_OK and g((8, 8)) == B.MOE_OK and g((0, 0)) == B.MOE_OK
+    assert g((64, 8), E=64) == B.MOE_OK and g((8, 1), E=64) == B.MOE_OK
+    assert g((8, 1), E=64, k=8) == B.MOE_OK          # k = 8 fills the one group of 8
+    assert g((16, 1), E=64, k=8) == B.MOE_ERR_INVALID_ARG  # 4 experts left for k = 8
+    assert g((7, 4)) == B.MOE_ERR_UNSUPPORTED        # 7 does not divide 256
+    assert g((128, 8)) == B.MOE_ERR_UNSUPPORTED      # more than 64 groups
+    assert g((8, 9)) == B.MOE_ERR_INVALID_ARG and g((8, 0)) == B.MOE_ERR_INVALID_ARG
+    assert g((0, 4)) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_rows_capacity_and_workspace(B):

@@ -188,6 +188,50 @@ def test_wide_router_many_experts(E, T, cap):
             assert np.array_equal(drop.cpu().numpy().astype(bool), ref["drop"].astype(bool))
 
 
+# Group-limited selection ("MoE Research", section 2, node-limited routing; "MoE at the
+# inference level", workarounds, device-limited routing with M = 4): DeepSeek-V3 routing with
+# 256 experts in 8 groups, 4 kept, through every router path (the one-launch small-T route at
+# T = 1, 16, 300; 16-token tiles at T = 1000; 64-token tiles at T = 8492); 160 experts in
+# groups of 20 that straddle the waves' 64-expert blocks; softmax over 64 experts in 8 groups
+# with 2 kept (k = 8 of the 16 experts left) on the small route and on 16-token tiles.
+GROUPED = WIDE.replace(name="grouped", cfg_id=14, groups=(8, 4))
+GROUPED_SM = S.SPECS["olmoe"].replace(name="grouped_softmax", cfg_id=15, d=512, ffn=256, groups=(8, 2))
+
+
+@pytest.mark.parametrize("which,E,G,M,T", [("sig", 256, 8, 4, 1), ("sig", 256, 8, 4, 16), ("sig", 256, 8, 4, 300),
+                                           ("sig", 256, 8, 4, 1000), ("sig", 256, 8, 4, 8492),
+                                           ("sig", 160, 8, 3, 9000), ("sm", 64, 8, 2, 1), ("sm", 64, 8, 2, 64),
+                                           ("sm", 64, 8, 2, 5000)])
+def test_group_limited_selection(which, E, G, M, T):
+    sp = (GROUPED if which == "sig" else GROUPED_SM).replace(E=E, groups=(G, M))
+    lay = S.make_layer(sp, device="cuda")
+    ml = layer_of(sp, lay)
+    x = S.make_tokens(sp, T, device="cuda", seed=E + T)
+    out, idx, gates, drop, ref = run_and_check(sp, lay, ml, x, nsamp=300)
+    gi = idx.cpu().numpy()
+    gsz = E // G
+    # every token, whatever its margins: its picks come from at most M groups
+    assert max(len(set((row // gsz).tolist())) for row in gi) <= M
+    if T >= 64:
+        # the limit binds: plain top-k would spread some tokens over more groups
+        free = oracle_run(sp.replace(groups=None), lay, x, ffn_rows=np.arange(0))["idx"]
+        assert max(len(set((row // gsz).tolist())) for row in free) > M
+
+
+def test_groups_of_one_expert_keep_plain_topk():
+    """Groups of one expert with M = k select exactly the plain top-k: bitwise the
+    same indices, gates and outputs as the layer without a group limit."""
+    sp = GROUPED_SM.replace(groups=(64, 8))
+    lay = S.make_layer(sp, device="cuda")
+    a, b = layer_of(sp, lay), layer_of(sp.replace(groups=None), lay)
+    for T in (1, 300, 5000):
+        x = S.make_tokens(sp, T, device="cuda", seed=T)
+        ra, rb = a.forward(x), b.forward(x)
+        torch.cuda.synchronize()
+        for u, v in zip(ra, rb):
+            assert torch.equal(u, v)
+
+
 def test_dense_limit_matches_textbook_swiglu():
     """E = 1, k = 1: the gate is softmax of one logit = 1, so the layer is a dense
     SwiGLU FFN.  Checked against the formula written out with scipy's expit."""
