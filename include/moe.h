@@ -179,6 +179,20 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router,
                        float* topk_w, uint8_t* drop_mask,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Route replay (the launch-bound study's Sub-study 2: the routes of one
+ * model replayed through a layer's expert weights; replaying the layer's own
+ * routes must return its baseline exactly).  The layer from given routes:
+ * permute, gate/up SwiGLU GEMM, down GEMM, combine, with no router.
+ *   x [T][d]; topk_idx [T][k] int32 (a value outside [0, E) is dropped, as
+ *   in moe_permute; indices of one token should be distinct, as top-k makes
+ *   them); topk_w [T][k] fp32 gates, used as given.  Capacity applies to the
+ *   given routes in (t, j) order.  Out: out [T][d], drop_mask [T][k].
+ *   Bit for bit what moe_forward returns when topk_idx / topk_w are its own
+ *   routes (and what moe_permute -> moe_expert_ffn -> moe_combine return). */
+moe_status moe_forward_with_routes(const moe_cfg* cfg, const void* x, const int32_t* topk_idx,
+                                   const float* topk_w, const moe_experts* w, void* out,
+                                   uint8_t* drop_mask, void* ws, size_t ws_bytes, void* stream);
+
 /* Repacks weight rows from MOE_LAYOUT_ROWS into MOE_LAYOUT_TILED (out of
  * place; a pure byte permutation, so results do not change, bit for bit).
  * Not from the pages: an MI355X data-layout choice.  A 16-byte load per lane

@@ -69,6 +69,8 @@ def _load() -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [C, P, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [C, P, P, P, P, ctypes.POINTER(MoeExperts), P, P, P, P, P,
                                        ctypes.c_size_t, P]),
+        "moe_forward_with_routes": (ctypes.c_int, [C, P, P, P, ctypes.POINTER(MoeExperts), P, P, P,
+                                                   ctypes.c_size_t, P]),
         "moe_pack_weights": (ctypes.c_int, [ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int32, P]),
         "moe_set_timing_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -185,6 +187,11 @@ def moe_expert_ffn(cfg, x, offsets, row_token, w: MoeExperts, y_rows, y_shared, 
 def moe_combine(cfg, y_rows, slot_row, topk_w, y_shared, out, stream=None):
     _check(lib.moe_combine(ctypes.byref(cfg), _p(y_rows), _p(slot_row), _p(topk_w), _p(y_shared), _p(out),
                            _stream(stream)))
+
+
+def moe_forward_with_routes(cfg, x, topk_idx, topk_w, w: MoeExperts, out, drop_mask, ws, stream=None):
+    _check(lib.moe_forward_with_routes(ctypes.byref(cfg), _p(x), _p(topk_idx), _p(topk_w), ctypes.byref(w), _p(out),
+                                       _p(drop_mask), _p(ws), ws.numel(), _stream(stream)))
 
 
 def moe_forward(cfg, x, w_router, logit_bias, select_bias, w: MoeExperts, out, topk_idx, topk_w, drop_mask, ws,

@@ -487,6 +487,40 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   return st;
 }
 
+moe_status moe_forward_with_routes(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, const float* topk_w,
+                                   const moe_experts* w, void* out, uint8_t* drop_mask, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  Plan p;
+  moe_status st;
+  if ((st = make_plan(cfg, &p))) return st;
+  if (p.T == 0) return MOE_OK;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if ((st = check_experts(p, w))) return st;
+  if (!x || !topk_idx || !topk_w || !out || !drop_mask)
+    return fail(MOE_ERR_INVALID_ARG, "NULL x, topk_idx, topk_w, out or drop_mask");
+  if (!al16(x) || !al16(out)) return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+  if (!al4(topk_idx) || !al4(topk_w)) return fail(MOE_ERR_INVALID_ARG, "topk_idx and topk_w must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* slot = at<int32_t>(ws, p.o_slot);
+  int32_t* rowtok = at<int32_t>(ws, p.o_rowtok);
+  PermArgs pa = perm_args(p, ws, at<int32_t>(ws, p.o_counts), at<int32_t>(ws, p.o_off), rowtok, slot, drop_mask);
+  // the same permutation launches as moe_permute (and so as moe_forward, whose route
+  // launch ranks the pairs with the same code)
+  if (p.single) {
+    RouteArgs ra = route_args(p, nullptr, nullptr, nullptr, nullptr, nullptr);
+    if ((st = hip_ok(launch_route_small(nullptr, 0, ra, topk_idx, pa, 0, 1, nullptr, s), "permute"))) return st;
+  } else {
+    int32_t* hist = at<int32_t>(ws, p.o_hist);
+    if ((st = hip_ok(launch_tile_hist(topk_idx, p.T, p.k, p.E, p.rt * p.rpb, hist, s), "histogram"))) return st;
+    if ((st = hip_ok(launch_permute_multi(topk_idx, hist, pa, s), "permute"))) return st;
+  }
+  void* ysh = p.S ? at<void>(ws, p.o_ysh) : nullptr;
+  FfnArgs a = ffn_args(p, ws, x, rowtok, w, at<void>(ws, p.o_y), ysh);
+  if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
+  if ((st = hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM"))) return st;
+  return hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
+}
+
 moe_status moe_pack_weights(int32_t dtype, const void* src, void* dst, int64_t rows, int32_t K, void* stream) {
   if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_INT4_G128)
     return fail(MOE_ERR_INVALID_ARG, "dtype=%d is not a moe_dtype", dtype);

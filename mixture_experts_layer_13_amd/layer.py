@@ -51,6 +51,18 @@ class MoeLayer:
                       drop_mask, self.workspace(c), stream)
         return out, topk_idx, topk_w, drop_mask
 
+    def forward_with_routes(self, x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor, out=None,
+                            drop_mask=None, stream=None):
+        """Route replay: the layer from the given [T, k] indices and gates (no router)."""
+        c = self.cfg_for(x.shape[0])
+        dev = self.device
+        assert topk_idx.shape == (c.T, c.k) and topk_idx.dtype == torch.int32 and topk_idx.is_contiguous()
+        assert topk_w.shape == (c.T, c.k) and topk_w.dtype == torch.float32 and topk_w.is_contiguous()
+        out = torch.empty((c.T, c.d), dtype=self.act_dtype, device=dev) if out is None else out
+        drop_mask = torch.empty((c.T, c.k), dtype=torch.uint8, device=dev) if drop_mask is None else drop_mask
+        B.moe_forward_with_routes(c, x, topk_idx, topk_w, self.experts, out, drop_mask, self.workspace(c), stream)
+        return out, drop_mask
+
     # ------------------------------------------------------------ split path
     def route(self, x: torch.Tensor, want_scores: bool = True, stream=None):
         c = self.cfg_for(x.shape[0])

@@ -116,6 +116,17 @@ def test_entry_points_reject_bad_arguments_before_launch(B):
     assert st == B.MOE_ERR_INVALID_ARG          # y_shared given without shared experts
     st = B.lib.moe_permute(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, 16, None)
     assert st == B.MOE_ERR_WORKSPACE
+    st = B.lib.moe_forward_with_routes(ctypes.byref(c), fake, fake, fake, ctypes.byref(w), fake, fake, fake,
+                                       1 << 30, None)
+    assert st == B.MOE_ERR_INVALID_ARG          # null expert weights
+    ew = B.MoeExperts()
+    ew.w_gate = ew.w_up = ew.w_down = 0x10000
+    st = B.lib.moe_forward_with_routes(ctypes.byref(c), fake, None, fake, ctypes.byref(ew), fake, fake, fake,
+                                       1 << 30, None)
+    assert st == B.MOE_ERR_INVALID_ARG          # null topk_idx
+    st = B.lib.moe_forward_with_routes(ctypes.byref(c), fake, fake, fake, ctypes.byref(ew), fake, fake, fake, 16,
+                                       None)
+    assert st == B.MOE_ERR_WORKSPACE
     assert B.lib.moe_status_str(B.MOE_ERR_HIP) == b"HIP error"
 
 
