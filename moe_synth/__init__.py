@@ -49,7 +49,7 @@ class LayerSpec:
     n_shared: int
     ffn_shared: int
     act: str              # 'f32' | 'bf16'  (x, router weight, outputs)
-    expert: str           # 'f32' | 'bf16' | 'int4'
+    expert: str           # 'f32' | 'bf16' | 'int4' | 'fp8'
     score: str            # 'softmax' | 'sigmoid'
     renorm: bool          # gates /= sum over the selected k
     gate_scale: float     # multiplies routed gates (2.5 for DeepSeek-V3)
@@ -137,6 +137,18 @@ def _quantise_int4(w: torch.Tensor):
     return packed, s
 
 
+def _quantise_fp8(w: torch.Tensor):
+    """Per-output-channel FP8 (OCP E4M3, the "fn" variant) quantiser.
+
+    Data generation only: s = absmax over the channel's K values / 448 (fp32), codes =
+    torch's round-to-nearest-even conversion of w / s to float8_e4m3fn, stored as bytes;
+    s == 0 -> codes 0."""
+    s = w.abs().amax(dim=-1) / 448.0
+    sf = torch.where(s > 0, s, torch.ones_like(s)).unsqueeze(-1)
+    codes = (w / sf).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, s.to(torch.float32)
+
+
 @dataclasses.dataclass
 class Layer:
     """All weights of one synthetic MoE layer (tokens are drawn separately)."""
@@ -173,6 +185,15 @@ def _expert_mats(sp: LayerSpec, n: int, ffn: int, ids, seed, device, chunk):
                 packed[e0:e1], scales[e0:e1] = _quantise_int4(w)
                 del w
             out.append((packed, scales))
+        elif sp.expert == "fp8":
+            codes = torch.empty((n,) + shape_tail, dtype=torch.uint8, device=device)
+            scales = torch.empty((n, shape_tail[0]), dtype=torch.float32, device=device)
+            for e0 in range(0, n, chunk):
+                e1 = min(n, e0 + chunk)
+                w = _normal((e1 - e0,) + shape_tail, std, g, device)
+                codes[e0:e1], scales[e0:e1] = _quantise_fp8(w)
+                del w
+            out.append((codes, scales))
         else:
             t = torch.empty((n,) + shape_tail, dtype=_dt(sp.expert), device=device)
             for e0 in range(0, n, chunk):

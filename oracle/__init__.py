@@ -6,6 +6,7 @@ Every function is pinned by the CPU test suite (no function here is
 "parity unpinned")."""
 from .moe_oracle import *  # noqa: F401,F403
 from .moe_oracle import (INT4_GROUP, assign_rows, bf16_to_f64, capacity_rows,  # noqa: F401
-                         experts_touched_expected, f32_to_f64, gate_weights, int4_dequant,
+                         experts_touched_expected, f32_to_f64, fp8_dequant, fp8_e4m3_to_f64,
+                         gate_weights, int4_dequant, limit_groups,
                          int4_unpack, moe_layer, router_logits, select_topk, sigmoid_scores,
                          silu, softmax_scores, swaps_per_token, swiglu_ffn)

@@ -80,6 +80,25 @@ def int4_dequant(packed: np.ndarray, scale_bits: np.ndarray, group: int = INT4_G
     return q * np.repeat(s, group, axis=-1)
 
 
+def fp8_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 bytes (the OCP 8-bit floating-point format, "fn" variant: sign,
+    4 exponent bits with bias 7, 3 mantissa bits, no infinities) to float64,
+    exactly ([MoE-inf] workarounds: fp8 expert weights).  Exponent field 0 is
+    subnormal, m/8 * 2^-6; field 15 with mantissa 7 is NaN; every other code is
+    (1 + m/8) * 2^(e - 7), so the largest finite value is 448."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def fp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """w[n, k] = fp8(code[n, k]) * s[n] with one fp32 scale per output channel, exactly."""
+    return fp8_e4m3_to_f64(codes) * np.asarray(scales, np.float64)[..., None]
+
+
 # --------------------------------------------------------------------------
 # router: logits, scores, selection, gates
 # --------------------------------------------------------------------------

@@ -69,6 +69,9 @@ class ExpertSource:
             for q, s in ((L.w_gate, L.s_gate), (L.w_up, L.s_up), (L.w_down, L.s_down)):
                 out.append(O.int4_dequant(q[e].cpu().numpy(), s[e].cpu().view(torch.int16).numpy()))
             return out
+        if self.sp.expert == "fp8":
+            return [O.fp8_dequant(q[e].cpu().numpy(), s[e].cpu().numpy())
+                    for q, s in ((L.w_gate, L.s_gate), (L.w_up, L.s_up), (L.w_down, L.s_down))]
         return [to_f64(L.w_gate[e]), to_f64(L.w_up[e]), to_f64(L.w_down[e])]
 
 
@@ -125,4 +128,4 @@ def row_rel_err(y: np.ndarray, ref: np.ndarray) -> np.ndarray:
 
 
 def tol_of(sp: S.LayerSpec) -> float:
-    return {"f32": F32_TOL, "bf16": BF16_TOL, "int4": INT4_TOL}[sp.expert]
+    return {"f32": F32_TOL, "bf16": BF16_TOL, "int4": INT4_TOL, "fp8": BF16_TOL}[sp.expert]

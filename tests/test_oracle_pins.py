@@ -35,6 +35,25 @@ def test_int4_unpack_bit_by_bit():
                 assert q[r, 2 * i + half] == val
 
 
+def test_fp8_decoding_matches_library_and_closed_forms():
+    """Every one of the 256 E4M3 codes against torch's own float8_e4m3fn decoding (a
+    library routine), plus closed forms: 0x38 = 1, 0x7E = 448 (largest), 0x08 = 2^-6
+    (smallest normal), 0x01 = 2^-9 (smallest subnormal), 0x80 = -0, 0x7F / 0xFF NaN."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.fp8_e4m3_to_f64(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(lib)) and np.isnan(got).sum() == 2
+    ok = ~np.isnan(lib)
+    assert np.array_equal(got[ok], lib[ok])
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9
+    assert got[0x80] == 0.0 and np.signbit(got[0x80]) and got[0xB8] == -1.0
+    assert np.nanmax(got) == 448.0 and np.nanmin(got) == -448.0
+    # per-channel scales multiply whole rows
+    c = np.array([[0x38, 0x40], [0x30, 0xB8]], np.uint8)
+    assert np.array_equal(O.fp8_dequant(c, np.array([0.5, 3.0])), np.array([[0.5, 1.0], [1.5, -3.0]]))
+
+
 def test_int4_one_hot_selects_exactly_one_weight():
     """A single non-zero nibble at a known (n, k) selects exactly q * s of its group:
     pins nibble order (low nibble = even k) and the group index k // 128."""
