@@ -126,7 +126,11 @@ def moe_layer(sp, lay, layout):
 
 def expert_bytes(sp):
     n = 3 * sp.d * sp.ffn
-    return n // 2 + (3 * sp.d * sp.ffn // 128) * 2 if sp.expert == "int4" else n * (4 if sp.expert == "f32" else 2)
+    if sp.expert == "int4":
+        return n // 2 + (3 * sp.d * sp.ffn // 128) * 2
+    if sp.expert == "fp8":  # one byte per weight and an fp32 scale per output channel
+        return n + (2 * sp.ffn + sp.d) * 4
+    return n * (4 if sp.expert == "f32" else 2)
 
 
 def alg_work(sp, T, idx, drop):
@@ -304,12 +308,13 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name
 def decode_other(layout):
     """The other decode-sized layers the HBM target covers: Qwen3 INT4 at T=32 (4
     copies of its 0.31 GB of expert weights) and DeepSeek-V3 at T=1 and 16 (2 copies:
-    one token already touches 0.8 GB), plus DeepSeek-V3 T=256 from its token sweep."""
+    one token already touches 0.8 GB), plus DeepSeek-V3 T=256 from its token sweep,
+    and the OLMoE-shaped layer with FP8 experts (half the bf16 bytes) at T=1..64."""
     import torch
 
     import moe_synth as S
     out = {}
-    for name, Ts, copies in (("qwen3_int4", (32,), 4), ("dsv3", (1, 16, 256), 2)):
+    for name, Ts, copies in (("qwen3_int4", (32,), 4), ("dsv3", (1, 16, 256), 2), ("olmoe_fp8", (1, 8, 32, 64), 4)):
         sp = S.SPECS[name]
         lay = S.make_layer(sp, device="cuda")
         out[name] = decode_sweep(sp, lay, layout, Ts=Ts, replays=100, copies=copies, name=name)

@@ -62,7 +62,7 @@ typedef enum {
   MOE_ERR_HIP = -4           /* a HIP launch failed                           */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2, MOE_FP8_E4M3 = 3 } moe_dtype;
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
 
@@ -70,7 +70,13 @@ typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
  * 1 <= k <= min(E, 8), d, ffn, ffn_shared multiples of 128, 0 <= n_shared <= 8,
  * act_dtype MOE_F32 or MOE_BF16 (x, w_router, y_rows, y_shared, out),
  * expert_dtype equal to act_dtype, or MOE_INT4_G128 with act_dtype MOE_BF16,
+ * or MOE_FP8_E4M3 with act_dtype MOE_BF16, T <= 64 and n_shared == 0,
  * and every expert matrix (ffn x d, ffn_shared x d) under 2 GiB.
+ * FP8 experts ("MoE at the inference level", workarounds: fp8 expert weights
+ * halve the bytes): one byte per weight in the OCP E4M3 format ("fn":
+ * exponent bias 7, no infinities, largest value 448), w = fp8 * s with one
+ * fp32 scale per output channel, s_gate / s_up [E][ffn], s_down [E][d]; the
+ * decode kernels convert each byte to bf16 exactly.
  * Group-limited selection ("MoE Research", section 2, node-limited routing;
  * "MoE at the inference level", workarounds, device-limited routing): with
  * n_groups = G > 0 the experts form G equal groups of consecutive indices
@@ -97,9 +103,9 @@ typedef struct moe_cfg {
   int32_t topk_groups;  /* groups a token may pick from (0: none)              */
 } moe_cfg;
 
-/* Expert weights (device pointers, layout above).  s_* are the INT4 scales
- * (NULL unless expert_dtype == MOE_INT4_G128); sh_* / shs_* the shared experts
- * (NULL when n_shared == 0). */
+/* Expert weights (device pointers, layout above).  s_* are the INT4 or FP8
+ * scales (NULL unless expert_dtype is MOE_INT4_G128 or MOE_FP8_E4M3); sh_* /
+ * shs_* the shared experts (NULL when n_shared == 0). */
 typedef struct moe_experts {
   const void *w_gate, *w_up, *w_down;
   const void *s_gate, *s_up, *s_down;

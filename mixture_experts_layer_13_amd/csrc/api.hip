@@ -68,10 +68,14 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     return fail(MOE_ERR_UNSUPPORTED, "ffn_shared=%d is not a multiple of 128 in [128, 65536]", c->ffn_shared);
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "act_dtype=%d is not MOE_F32 or MOE_BF16", c->act_dtype);
-  if (c->expert_dtype != MOE_F32 && c->expert_dtype != MOE_BF16 && c->expert_dtype != MOE_INT4_G128)
+  if (c->expert_dtype != MOE_F32 && c->expert_dtype != MOE_BF16 && c->expert_dtype != MOE_INT4_G128 &&
+      c->expert_dtype != MOE_FP8_E4M3)
     return fail(MOE_ERR_INVALID_ARG, "expert_dtype=%d is not a moe_dtype", c->expert_dtype);
-  if (!(c->expert_dtype == c->act_dtype || (c->expert_dtype == MOE_INT4_G128 && c->act_dtype == MOE_BF16)))
+  const bool quant = c->expert_dtype == MOE_INT4_G128 || c->expert_dtype == MOE_FP8_E4M3;
+  if (!(c->expert_dtype == c->act_dtype || (quant && c->act_dtype == MOE_BF16)))
     return fail(MOE_ERR_UNSUPPORTED, "expert_dtype=%d with act_dtype=%d", c->expert_dtype, c->act_dtype);
+  if (c->expert_dtype == MOE_FP8_E4M3 && (c->T > kStreamMaxT || c->n_shared > 0))
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 experts: decode sizes only (T <= %d) and no shared experts", kStreamMaxT);
   if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID)
     return fail(MOE_ERR_INVALID_ARG, "score=%d is not a moe_score", c->score);
   if (c->renorm != 0 && c->renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm=%d is not 0 or 1", c->renorm);
@@ -265,8 +269,10 @@ moe_status check_experts(const Plan& p, const moe_experts* w) {
   if (!w->w_gate || !w->w_up || !w->w_down) return fail(MOE_ERR_INVALID_ARG, "routed expert weight pointer is NULL");
   if (!al16(w->w_gate) || !al16(w->w_up) || !al16(w->w_down))
     return fail(MOE_ERR_INVALID_ARG, "routed expert weights must be 16-byte aligned");
-  if (p.wdt == MOE_INT4_G128 && (!w->s_gate || !w->s_up || !w->s_down))
-    return fail(MOE_ERR_INVALID_ARG, "INT4 experts need s_gate, s_up and s_down");
+  if ((p.wdt == MOE_INT4_G128 || p.wdt == MOE_FP8_E4M3) && (!w->s_gate || !w->s_up || !w->s_down))
+    return fail(MOE_ERR_INVALID_ARG, "INT4 and FP8 experts need s_gate, s_up and s_down");
+  if (p.wdt == MOE_FP8_E4M3 && (!al4(w->s_gate) || !al4(w->s_up) || !al4(w->s_down)))
+    return fail(MOE_ERR_INVALID_ARG, "FP8 scales must be 4-byte aligned");
   if (p.S > 0) {
     if (!w->sh_gate || !w->sh_up || !w->sh_down) return fail(MOE_ERR_INVALID_ARG, "shared expert weight pointer is NULL");
     if (!al16(w->sh_gate) || !al16(w->sh_up) || !al16(w->sh_down))
@@ -522,10 +528,12 @@ moe_status moe_forward_with_routes(const moe_cfg* cfg, const void* x, const int3
 }
 
 moe_status moe_pack_weights(int32_t dtype, const void* src, void* dst, int64_t rows, int32_t K, void* stream) {
-  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_INT4_G128)
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_INT4_G128 && dtype != MOE_FP8_E4M3)
     return fail(MOE_ERR_INVALID_ARG, "dtype=%d is not a moe_dtype", dtype);
   if (rows < 0 || rows % 16) return fail(MOE_ERR_INVALID_ARG, "rows=%lld is not a non-negative multiple of 16", (long long)rows);
-  const int64_t rb = dtype == MOE_INT4_G128 ? (int64_t)K / 2 : (int64_t)K * (dtype == MOE_F32 ? 4 : 2);
+  const int64_t rb = dtype == MOE_INT4_G128 ? (int64_t)K / 2
+                     : dtype == MOE_FP8_E4M3  ? (int64_t)K
+                                              : (int64_t)K * (dtype == MOE_F32 ? 4 : 2);
   if (K <= 0 || (dtype == MOE_INT4_G128 && K % kInt4Group) || rb % 64)
     return fail(MOE_ERR_INVALID_ARG, "K=%d: a row must be a positive multiple of 64 bytes (INT4: K multiple of 128)", K);
   if (rows == 0) return MOE_OK;

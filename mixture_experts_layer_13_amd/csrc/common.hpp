@@ -21,6 +21,9 @@ constexpr int kInt4Group = 128;
 struct F32 {};
 struct BF16 {};
 struct INT4 {};
+struct FP8 {  // one OCP E4M3 byte per weight, one fp32 scale per output channel
+  uint8_t bits;
+};
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);

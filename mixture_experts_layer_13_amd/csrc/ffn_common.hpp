@@ -69,8 +69,16 @@ template <> __device__ __forceinline__ const void* expert_mat<bf16>(const void* 
 template <> __device__ __forceinline__ const void* expert_mat<INT4>(const void* b, int e, int N, int K) {
   return (const uint8_t*)b + (size_t)e * N * (K / 2);
 }
+template <> __device__ __forceinline__ const void* expert_mat<FP8>(const void* b, int e, int N, int K) {
+  return (const uint8_t*)b + (size_t)e * N * K;
+}
 __device__ __forceinline__ const void* expert_scales(const void* b, int e, int N, int K) {
   return b ? (const void*)((const uint16_t*)b + (size_t)e * N * (K / kInt4Group)) : nullptr;
+}
+// scales of expert e by weight type: INT4 one bf16 per (channel, 128-K group), FP8 one fp32 per channel
+template <typename TW> __device__ __forceinline__ const void* expert_scales_of(const void* b, int e, int N, int K) {
+  if constexpr (std::is_same<TW, FP8>::value) return b ? (const void*)((const float*)b + (size_t)e * N) : nullptr;
+  else return expert_scales(b, e, N, K);
 }
 
 __device__ __forceinline__ f32x16 mma32_bf16(u32x4 a, u32x4 b, f32x16 c) {

@@ -21,6 +21,10 @@ template <> struct Dec<INT4> {
   using TA = bf16;
   static constexpr int KSTEP = 128, AL = 4, U = 2;
 };
+template <> struct Dec<FP8> {
+  using TA = bf16;
+  static constexpr int KSTEP = 64, AL = 2, U = 8;
+};
 
 // Weight bytes of one output channel n (row n of an [N][K] matrix, Kb bytes
 // per row) as one lane sees them: the row is read in 64-byte chunks, the lane
@@ -52,17 +56,20 @@ struct WRow {
 // One weight row of a [N][K] matrix as seen by one lane; a step of KSTEP K
 // values is one 64-byte chunk of the row.  Lane K order inside a step:
 // bf16 k = kb + 8g + i; f32 k = kb + 4g + i; INT4 k = kb + 32g + 8s + i
-// (s = dword of the 16-byte load).
+// (s = dword of the 16-byte load); FP8 k = kb + 16g + i (byte i of the load).
 template <typename TW> struct BRow {
   WRow w;
   const uint16_t* s;  // INT4 scales of the row (bf16, one per 128-K group)
+  float cs;           // FP8: the channel's scale
   __device__ BRow() {}
   __device__ BRow(const void* m, int n, int K, int g, const void* sc, int tiled)
       : w(m, n, row_bytes<TW>(K), g, tiled),
-        s(std::is_same<TW, INT4>::value ? (const uint16_t*)sc + (size_t)n * (K / kInt4Group) : nullptr) {}
+        s(std::is_same<TW, INT4>::value ? (const uint16_t*)sc + (size_t)n * (K / kInt4Group) : nullptr),
+        cs(std::is_same<TW, FP8>::value ? ((const float*)sc)[n] : 1.f) {}
   __device__ u32x4 load(int kb) const { return w.chunk(kb / Dec<TW>::KSTEP); }
   __device__ float scale(int kb) const {
     if constexpr (std::is_same<TW, INT4>::value) return bf16_bits_to_f32(s[kb / kInt4Group]);
+    else if constexpr (std::is_same<TW, FP8>::value) return cs;
     else return 1.f;
   }
 };
@@ -88,6 +95,26 @@ __device__ __forceinline__ f32x4 dstep_int4(const u32x4 (&av)[4], u32x4 b, float
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[i], acc[i]);
   return acc;
 }
+// FP8: sixteen E4M3 bytes (K = 16g + i) become two bf16 operands (bytes 0-7 and
+// 8-15; every E4M3 value is exact in bf16) by the chip's conversion, two bytes
+// per instruction; the products of one step are summed from zero and the
+// channel scale is applied once per step.
+template <bool HI> __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ f32x4 dstep_fp8(const u32x4 (&av)[2], u32x4 b, float sc, f32x4 acc) {
+  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 bb = {fp8x2_to_bf16x2<false>(b[2 * h]), fp8x2_to_bf16x2<true>(b[2 * h]),
+                      fp8x2_to_bf16x2<false>(b[2 * h + 1]), fp8x2_to_bf16x2<true>(b[2 * h + 1])};
+    t = mma_bf16(av[h], bb, t);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[i], acc[i]);
+  return acc;
+}
+
 // -136 times the sum over the group of each activation row, in the MFMA
 // output layout (an all-ones weight operand: every column holds the row sum).
 __device__ __forceinline__ f32x4 int4_group_offset(const u32x4 (&av)[4]) {
@@ -103,6 +130,7 @@ __device__ __forceinline__ f32x4 int4_group_offset(const u32x4 (&av)[4]) {
 // 16-channel tiles per wave of the streaming kernels (channels per block:
 // gate/up 16 NT, down 64 NT; the host grid uses the same numbers)
 template <typename TW> constexpr int stream_tiles() { return std::is_same<TW, INT4>::value ? 2 : 1; }
+static_assert(Dec<FP8>::AL == 2 && Dec<FP8>::KSTEP == 64, "FP8 steps: 16 bytes per lane, two bf16 operands");
 int stream_channels_per_block(bool gateup, int wdt) { return (gateup ? 16 : 64) * (wdt == kINT4 ? 2 : 1); }
 
 // GATEUP: h[row][n] = silu(A Wg^T) * (A Wu^T); else y[row][n] = A Wd^T.
@@ -126,7 +154,9 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   // MFMAs can start while later steps land).  Measured on decode layers: INT4 gate/up 1 (its
   // small register footprint keeps 5 blocks per CU), INT4 down 2, bf16 16 / 8 / 4 for items of
   // 16 / 32 / 64 rows
-  constexpr int U = std::is_same<TW, INT4>::value ? (GATEUP ? 1 : 2) : (MT == 1 ? 16 : (MT == 2 ? 8 : 4));
+  constexpr int U = std::is_same<TW, INT4>::value  ? (GATEUP ? 1 : 2)
+                    : std::is_same<TW, FP8>::value ? (MT == 1 ? 8 : (MT == 2 ? 4 : 2))
+                                                   : (MT == 1 ? 16 : (MT == 2 ? 8 : 4));
   constexpr int AL = D::AL, KSTEP = D::KSTEP;
   __shared__ f32x4 red[KSPLIT > 1 ? 3 : 1][NM][NT][MT][64];
   const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
@@ -161,10 +191,10 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   // weight rows first: their loads do not wait for the activation row lookup
   const void* m0 = GATEUP ? (shared ? a.shg : expert_mat<TW>(a.wg, e, a.F, a.d))
                           : (shared ? a.shd : expert_mat<TW>(a.wd, e, a.d, K));
-  const void* s0 = GATEUP ? (shared ? a.shsg : expert_scales(a.sg, e, a.F, a.d))
-                          : (shared ? a.shsd : expert_scales(a.sd, e, a.d, K));
+  const void* s0 = GATEUP ? (shared ? a.shsg : expert_scales_of<TW>(a.sg, e, a.F, a.d))
+                          : (shared ? a.shsd : expert_scales_of<TW>(a.sd, e, a.d, K));
   const void* m1 = GATEUP ? (shared ? a.shu : expert_mat<TW>(a.wu, e, a.F, a.d)) : m0;
-  const void* s1p = GATEUP ? (shared ? a.shsu : expert_scales(a.su, e, a.F, a.d)) : s0;
+  const void* s1p = GATEUP ? (shared ? a.shsu : expert_scales_of<TW>(a.su, e, a.F, a.d)) : s0;
   BRow<TW> b0[NT], b1[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -200,7 +230,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
       for (int j = 0; j < NT; ++j)
         b0[j] = b1[j] = BRow<TW>(expert_mat<TW>(a.shd, seg, a.d, K), n0 + 16 * j, K, g,
-                                 expert_scales(a.shsd, seg, a.d, K), a.wtiled);
+                                 expert_scales_of<TW>(a.shsd, seg, a.d, K), a.wtiled);
     }
     const int aoff = seg * K;
     const int nsteps = K / KSTEP;
@@ -228,7 +258,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
             if (mt < nmt)
 #pragma unroll
               for (int q = 0; q < AL; ++q)
-                av[mt][u][q] = ld16(arow[mt] + aoff + kb + (AL == 1 ? (KSTEP / 4) * g : 32 * g + 8 * q));
+                av[mt][u][q] = ld16(arow[mt] + aoff + kb + (KSTEP / 4) * g + 8 * q);
         }
       }
 #pragma unroll
@@ -245,6 +275,14 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
                   for (int j = 0; j < NT; ++j)
                     acc[m][j][mt] = dstep_int4(av[mt][u], bq[m][j][u], sc[m][j][u], xn, acc[m][j][mt]);
               }
+          } else if constexpr (std::is_same<TW, FP8>::value) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                  if (mt < nmt) acc[m][j][mt] = dstep_fp8(av[mt][u], bq[m][j][u], sc[m][j][u], acc[m][j][mt]);
           } else {
 #pragma unroll
             for (int m = 0; m < NM; ++m)
@@ -311,6 +349,8 @@ static void launch_stream(int wdt, const FfnArgs& a, int grid, hipStream_t s) {
     hipLaunchKernelGGL((ffn_stream_kernel<float, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
   else if (wdt == kBF16)
     hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+  else if (wdt == kFP8)
+    hipLaunchKernelGGL((ffn_stream_kernel<FP8, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((ffn_stream_kernel<INT4, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
 }

@@ -6,7 +6,7 @@
 
 namespace moe {
 
-enum { kF32 = 0, kBF16 = 1, kINT4 = 2 };
+enum { kF32 = 0, kBF16 = 1, kINT4 = 2, kFP8 = 3 };
 enum { kScoreSoftmax = 0, kScoreSigmoid = 1 };
 
 constexpr int kSmallMaxPairs = 2048;    // T*k handled by the many-block route and its one-block permutation

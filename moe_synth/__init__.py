@@ -88,6 +88,8 @@ SPECS = {
 }
 # DeepSeek-V2-Lite is also run with a fixed capacity C = 1.25.
 SPECS["dsv2_lite_cap"] = SPECS["dsv2_lite"].replace(name="dsv2_lite_cap", capacity=(5, 4))
+# the OLMoE-shaped layer with FP8 (E4M3) expert weights and per-channel scales (decode sizes)
+SPECS["olmoe_fp8"] = SPECS["olmoe"].replace(name="olmoe_fp8", cfg_id=5, expert="fp8", tokens=(1, 8, 32, 64))
 
 
 def spec(name: str) -> LayerSpec:

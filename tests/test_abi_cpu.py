@@ -65,6 +65,11 @@ def test_validation_errors(B):
     assert B.validate(B.make_cfg(4, 32768, 8, 2, 16384)) == B.MOE_OK               # 1 GiB
     assert B.validate(B.make_cfg(4, 32768, 8, 2, 16384, act="f32", expert="f32")) == B.MOE_ERR_UNSUPPORTED
     assert B.validate(B.make_cfg(4, 1024, 8, 2, 512, 1, 1 << 20)) != B.MOE_OK
+    # FP8 experts: bf16 activations, decode sizes (T <= 64), no shared experts
+    assert B.validate(B.make_cfg(64, 2048, 64, 8, 1024, expert="fp8")) == B.MOE_OK
+    assert B.validate(B.make_cfg(65, 2048, 64, 8, 1024, expert="fp8")) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(B.make_cfg(8, 2048, 64, 8, 1024, act="f32", expert="fp8")) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(B.make_cfg(8, 2048, 64, 8, 1024, 1, 1024, expert="fp8")) == B.MOE_ERR_UNSUPPORTED
     # group-limited selection: G divides E, G <= 64, 1 <= M <= G, k <= M * E / G; 0 / 0 = none
     g = lambda grp, E=256, k=8: B.validate(B.make_cfg(16, 1024, E, k, 512, score="sigmoid", groups=grp))
     assert g((8, 4)) == B.MOE_OK and g((8, 8)) == B.MOE_OK and g((0, 0)) == B.MOE_OK
