@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   // small register footprint keeps 5 blocks per CU), INT4 down 2, bf16 16 / 8 / 4 for items of
   // 16 / 32 / 64 rows
   constexpr int U = std::is_same<TW, INT4>::value  ? (GATEUP ? 1 : 2)
-                    : std::is_same<TW, FP8>::value ? (MT == 1 ? 8 : (MT == 2 ? 4 : 2))
+                    : std::is_same<TW, FP8>::value ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
                                                    : (MT == 1 ? 16 : (MT == 2 ? 8 : 4));
   constexpr int AL = D::AL, KSTEP = D::KSTEP;
   __shared__ f32x4 red[KSPLIT > 1 ? 3 : 1][NM][NT][MT][64];
