@@ -52,7 +52,7 @@ class MoeExperts(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+        raise ImportError(f"{LIB_PATH} is not built: run `python mixture_experts_layer_13_amd/build.py` "
                           "from the repository root (hipcc --offload-arch=gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p

@@ -1,6 +1,6 @@
 """Builds libmoe.so in-tree with hipcc for gfx950.
 
-Usage: python mixture_experts_layer_13_amd/build.py  (or __graft_entry__.build()).
+Usage: python mixture_experts_layer_13_amd/build.py
 """
 import os
 import subprocess
