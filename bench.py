@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/gateup_tiled_olmoe_T4096_traffic.json from four rocprofv3 --pmc csv "
                          "directories (FETCH_SIZE and WRITE_SIZE of this bench, then of --copy-probe) and exit")
+    ap.add_argument("--profile-layer", metavar="SPEC",
+                    help="run --warmup + --steps eager forwards of the named synthetic layer at --T tokens "
+                         "(for counter passes on one layer's kernels), print the mean ms and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device-to-device copy three times (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -417,6 +420,14 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.profile_layer:
+        psp = S.SPECS[args.profile_layer]
+        play = S.make_layer(psp, device="cuda")
+        ml = moe_layer(psp, play, args.layout)
+        x = S.make_tokens(psp, args.T, device="cuda")
+        ms = time_layer(ml, x, args.steps, args.warmup)[0]
+        print(json.dumps({"layer": args.profile_layer, "T": args.T, "ms_per_forward": round(ms, 4)}), flush=True)
         return
     sp = S.SPECS["olmoe"]
     T = args.T
