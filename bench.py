@@ -1,19 +1,23 @@
 """Benchmark of the MoE layer forward on one MI355X.
 
-Default workload: the OLMoE-1B-7B-shaped layer (d=2048, E=64, k=8, SwiGLU
-ffn=1024, bf16, softmax top-k without renorm, router skew bias std 0.5) at
-T=4096 tokens, seeded synthetic inputs resident in HBM.  A step is one
-moe_forward: router + top-k, permutation, gate/up GEMM, down GEMM, combine.
+Headline workload: the DeepSeek-V3-shaped layer (d=7168, 256 routed experts,
+k=8, one shared expert, SwiGLU ffn=2048, bf16, sigmoid scoring with a
+selection-only bias, gates 2.5 x renormalised) at T=16384 tokens, the largest
+configuration and the one the prefill MFMA target is set on.  Seeded synthetic
+inputs and random-init weights of that shape are resident in HBM.  A step is
+one moe_forward: router + top-k, permutation, gate/up GEMM, down GEMM, combine.
 
 Prints one JSON line.  `roofline` is for the dominant kernel (the grouped
 gate/up SwiGLU GEMM, MFMA-bound), timed with HIP events recorded by the
 library around that launch on its own stream during the timed steps.
-`cpu_baseline` is the FP64 oracle on a bounded token sample of the same
-workload.  `decode` adds the same layer at decode sizes (hipGraph replays,
-weights rotated over several copies so the Infinity Cache does not serve
-them), reported against HBM bandwidth.
+`cpu_baseline` is the FP64 oracle: routing over every token plus the whole
+layer on a seeded 1024-token subset, extrapolated to the workload.  Sub-keys:
+the OLMoE-shaped layer at T=4096 (`olmoe_T4096`), decode sizes as hipGraph
+replays with weights rotated over several copies so the Infinity Cache does
+not serve them (`decode`, `decode_other`, against HBM bandwidth), the other
+prefill layers (`prefill`), and routing near-ties and INT4 drift (`routing`).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-prefill]
 """
 import argparse
 import ctypes
@@ -36,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--T", type=int, default=4096)
+    ap.add_argument("--T", type=int, default=16384, help="tokens of the headline (or --profile-layer) workload")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -44,8 +48,10 @@ def parse():
                     help="expert weight layout (tiled: repacked once before timing)")
     ap.add_argument("--decode-only", action="store_true", help="run only the decode sweep and print it")
     ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="write profiles/gateup_tiled_olmoe_T4096_traffic.json from four rocprofv3 --pmc csv "
-                         "directories (FETCH_SIZE and WRITE_SIZE of this bench, then of --copy-probe) and exit")
+                    help="write the gate/up traffic record of --traffic-workload under profiles/ from four "
+                         "rocprofv3 --pmc csv directories (FETCH_SIZE and WRITE_SIZE of --profile-layer runs, then "
+                         "of --copy-probe) and exit")
+    ap.add_argument("--traffic-workload", choices=sorted(TRAFFIC_WORKLOADS), default="dsv3_T16384")
     ap.add_argument("--profile-layer", metavar="SPEC",
                     help="run --warmup + --steps eager forwards of the named synthetic layer at --T tokens "
                          "(for counter passes on one layer's kernels), print the mean ms and exit")
@@ -151,10 +157,17 @@ def alg_work(sp, T, idx, drop):
     return dict(bytes=byts, flops=flops, gateup_flops=gateup, touched=touched, kept=n_kept)
 
 
-TRAFFIC_PATH = os.path.join(ROOT, "profiles", "gateup_tiled_olmoe_T4096_traffic.json")
+# gate/up traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE of the bf16 tiled gate/up kernel),
+# one per workload: (spec, T, file under profiles/)
+TRAFFIC_WORKLOADS = {"dsv3_T16384": ("dsv3", 16384), "olmoe_T4096": ("olmoe", 4096)}
+GATEUP_KERNEL = ("ffn_tiled32_kernel<true", "ffn_tiled32_kernelILb1E")  # demangled or mangled name
 # the sources the dominant (bf16 tiled gate/up) kernel is compiled from
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", f)
                   for f in ("ffn_tiled.hip", "ffn_common.hpp", "common.hpp", "kernels.hpp")]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"gateup_tiled_{workload}_traffic.json")
 
 
 def kernel_sha():
@@ -164,12 +177,13 @@ def kernel_sha():
     return h.hexdigest()
 
 
-def traffic_record():
-    """HBM bytes of the dominant kernel from the committed rocprofv3 counter summary,
-    valid only while the kernel's sources are the ones the counters were taken on."""
-    if not os.path.exists(TRAFFIC_PATH):
+def traffic_record(workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary, valid only while the kernel's sources are the ones the counters were taken on."""
+    path = traffic_path(workload)
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(TRAFFIC_PATH))
+    rec = json.load(open(path))
     if rec.get("source_sha256") != kernel_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -193,59 +207,110 @@ def _pmc_mean_kib(csv_dir, counter, kernel_substr, largest=None):
     return sum(vals) / len(vals)
 
 
-def write_traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+def write_traffic_record(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
     """Writes the traffic record of the gate/up kernel from four rocprofv3 --pmc runs:
-    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the bench, and of the copy probe,
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the workload, and of the copy probe,
     whose known 1 GiB read + 1 GiB write calibrates each counter."""
-    gu = ("ffn_tiled32_kernel<true", "ffn_tiled32_kernelILb1E")  # demangled or mangled name
     copy = ("copyBuffer",)  # the runtime's device-to-device copy kernel behind the probe's Tensor.copy_
-    f_k = _pmc_mean_kib(fetch_dir, "FETCH_SIZE", gu)
-    w_k = _pmc_mean_kib(write_dir, "WRITE_SIZE", gu)
+    f_k = _pmc_mean_kib(fetch_dir, "FETCH_SIZE", GATEUP_KERNEL)
+    w_k = _pmc_mean_kib(write_dir, "WRITE_SIZE", GATEUP_KERNEL)
     cf = _pmc_mean_kib(copy_fetch_dir, "FETCH_SIZE", copy, largest=3)
     cw = _pmc_mean_kib(copy_write_dir, "WRITE_SIZE", copy, largest=3)
     nbytes = 1 << 30
     fs, ws = nbytes / (cf * 1024), nbytes / (cw * 1024)
-    rec = {"kernel": "ffn_tiled32_kernel<gate/up + SwiGLU, tiled weights>", "workload": "olmoe_1b7b_layer_T4096",
+    rec = {"kernel": "ffn_tiled32_kernel<gate/up + SwiGLU, tiled weights>", "workload": workload,
            "fetch_size_kib_per_launch": round(f_k, 1), "write_size_kib_per_launch": round(w_k, 1),
            "copy_probe": {"bytes_read": nbytes, "bytes_written": nbytes, "fetch_size_kib": round(cf, 1),
                           "write_size_kib": round(cw, 1), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
            "hbm_bytes_per_launch": int(f_k * 1024 * fs + w_k * 1024 * ws),
            "commands": commands, "source_files": [os.path.relpath(f, ROOT) for f in KERNEL_SOURCES],
            "source_sha256": kernel_sha()}
-    with open(TRAFFIC_PATH, "w") as fh:
+    with open(traffic_path(workload), "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
     print(json.dumps(rec))
 
 
-def cpu_baseline(sp, lay, x, n_tokens, min_s=10.0):
+def gateup_alg_bytes(sp, T, w):
+    """Algorithmic HBM bytes of one gate/up launch: the touched experts' gate and up
+    weights, the shared experts' gate and up weights, each token row of x once, h written."""
+    es = 2
+    wbytes = (w["touched"] * 2 * sp.d * sp.ffn + sp.n_shared * 2 * sp.d * sp.ffn_shared) * es
+    return int(wbytes + T * sp.d * es + (w["kept"] * sp.ffn + T * sp.n_shared * sp.ffn_shared) * es)
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
+def cpu_baseline(sp, lay, x, n_ffn=None, seed=0, min_s=10.0):
+    """The FP64 oracle on the host cores, timed on a bounded sample of the workload.
+
+    n_ffn None: the whole layer over every token, repeated to at least `min_s` s.
+    n_ffn = n: routing (router product, scores, top-k, gates, assignment) over every
+    token once, and the whole layer once on a seeded subset of n tokens (dropless
+    routing is per token, so the subset's routes are those of the full run); the
+    workload's time is extrapolated as t_route + t_subset * T / n."""
+    import numpy as np
+
     import oracle as O
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_harness import ExpertSource, to_f64
-    xs = x[:n_tokens]
-    xf, wr, lb = to_f64(xs), to_f64(lay.w_router), to_f64(lay.logit_bias)
+    T = x.shape[0]
+    xf, wr, lb, sb = to_f64(x), to_f64(lay.w_router), to_f64(lay.logit_bias), to_f64(lay.select_bias)
 
-    class HostWeights:  # expert weights copied to host memory before timing (inputs resident)
-        w_gate = [t.cpu() for t in lay.w_gate]
-        w_up = [t.cpu() for t in lay.w_up]
-        w_down = [t.cpu() for t in lay.w_down]
-
+    class HostWeights:  # every weight copied to host memory before timing (inputs resident)
+        pass
+    for f in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up", "sh_down"):
+        t = getattr(lay, f)
+        setattr(HostWeights, f, None if t is None else [m.cpu() for m in t])
+    kw = dict(score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale, logit_bias=lb, select_bias=sb,
+              capacity=sp.capacity, shared=ExpertSource(sp, HostWeights, shared=True) if sp.n_shared else None,
+              n_shared=sp.n_shared, groups=sp.groups)
     host = ExpertSource(sp, HostWeights)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    # whole runs of the sample until at least `min_s` seconds of host time (at most 20 runs)
-    runs, t0 = 0, time.perf_counter()
-    while runs < 20 and (runs == 0 or time.perf_counter() - t0 < min_s):
-        O.moe_layer(xf, wr, host, sp.E, sp.k, score=sp.score, renorm=sp.renorm, gate_scale=sp.gate_scale,
-                    logit_bias=lb, capacity=sp.capacity)
-        runs += 1
-    dt = time.perf_counter() - t0
-    return {"value": runs * n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_tokens} of the {x.shape[0]} tokens (full FP64 layer on the sample: routing, "
-                      f"all selected expert FFNs from bf16 bit patterns, combine), {runs} runs in {dt:.1f} s"}
+    base = {"unit": "tokens/s", "cores": _threads(), "blas_threads": _threads(), "host_cpus": os.cpu_count(),
+            "kind": "oracle"}
+    if n_ffn is None:
+        runs, t0 = 0, time.perf_counter()
+        while runs < 20 and (runs == 0 or time.perf_counter() - t0 < min_s):
+            O.moe_layer(xf, wr, host, sp.E, sp.k, **kw)
+            runs += 1
+        dt = time.perf_counter() - t0
+        return dict(base, value=runs * T / dt,
+                    sample=f"all {T} tokens (full FP64 layer: routing, every selected expert FFN from the stored "
+                           f"bit patterns, combine), {runs} runs in {dt:.1f} s")
+    assert sp.capacity is None, "the subset extrapolation needs per-token (dropless) routing"
+    t0 = time.perf_counter()
+    O.moe_layer(xf, wr, host, sp.E, sp.k, ffn_rows=np.arange(0), **kw)
+    t_route = time.perf_counter() - t0
+    sub = np.sort(np.random.default_rng(seed).choice(T, size=n_ffn, replace=False))
+    t0 = time.perf_counter()
+    O.moe_layer(xf[sub], wr, host, sp.E, sp.k, **kw)
+    t_sub = time.perf_counter() - t0
+    est = t_route + t_sub * T / n_ffn
+    return dict(base, value=T / est,
+                sample=f"routing over all {T} tokens ({t_route:.1f} s) + the whole FP64 layer (routing, every "
+                       f"selected expert FFN from the stored bf16 bit patterns, shared expert, combine) on a seeded "
+                       f"{n_ffn}-token subset ({t_sub:.1f} s, seed {seed}); value = T / (t_route + t_subset * T / "
+                       f"{n_ffn}), i.e. {est:.1f} s for the workload")
+
+
+def routing_report(ml, sp, x):
+    """Near-ties of the route on the GPU's own fp32 selection keys (tokens whose k-th
+    and (k+1)-th keys differ by at most 1e-3 / 1e-5), from moe_route's scores."""
+    import torch
+    _, _, scores = ml.route(x)
+    key = scores if ml.select_bias is None else scores + ml.select_bias[None, :]
+    if sp.k >= sp.E:
+        return {"tokens": x.shape[0], "near_ties_1e-3": 0, "near_ties_1e-5": 0}
+    top = torch.topk(key, sp.k + 1, dim=1).values
+    margin = top[:, sp.k - 1] - top[:, sp.k]
+    return {"tokens": x.shape[0], "near_ties_1e-3": int((margin <= 1e-3).sum()),
+            "near_ties_1e-5": int((margin <= 1e-5).sum())}
 
 
 def clone_weights(lay):
@@ -302,7 +367,7 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name
         gbs = w["bytes"] / (us * 1e-6) / 1e9
         res[f"T{T}"] = {"us_per_layer": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
                         "alg_bytes": w["bytes"], "touched_experts": w["touched"], "hbm_GBps": round(gbs, 1),
-                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "routing": routing_report(layers[0], sp, x)}
         del graphs
     return {"layer": name, "method": f"hipGraph replay, {copies} weight copies round-robin, {replays} replays",
             "points": res}
@@ -368,44 +433,87 @@ def time_layer(ml, x, steps, warmup):
     return ms_step, per, outs, nl, wall
 
 
+def prefill_point(sp, ml, x, steps, warmup):
+    ms, per, outs, nl, wall = time_layer(ml, x, steps, warmup)
+    T = x.shape[0]
+    w = alg_work(sp, T, outs[1], outs[3])
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "mfma_frac_layer": round(w["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_gateup": round(w["gateup_flops"] / (per["gateup"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "per_launch_us": {n: round(v * 1e3, 2) for n, v in per.items()},
+            "kept_pairs": w["kept"], "pairs": T * sp.k, "routing": routing_report(ml, sp, x)}, (ms, per, outs, nl,
+                                                                                              wall, w)
+
+
+def int4_drift(sp, lay, ml, x, layout):
+    """Routing drift of the INT4 layer against its bf16 twin (the pre-quantisation weights
+    rounded to bf16), in mean experts changed per token out of k.  In the layer itself the
+    router is bf16 and sees the same x, so its picks cannot move; what moves is the
+    residual stream after the layer, x + out, that the next layer's router sees.  That is
+    measured with this layer's router standing in for the next one's."""
+    import torch
+
+    import moe_synth as S
+    wg, wu, wd = S.make_bf16_twin(sp, device="cuda")
+    twin_sp = sp.replace(expert="bf16")
+    twin = moe_layer(twin_sp, S.Layer(twin_sp, lay.w_router, lay.logit_bias, lay.select_bias, wg, wu, wd), layout)
+    out_q, idx_q, _, _ = ml.forward(x)
+    out_b, idx_b, _, _ = twin.forward(x)
+
+    def swaps(a, b):
+        same = (a[:, :, None] == b[:, None, :]).any(2).sum(1)
+        return float((sp.k - same).float().mean())
+
+    nxt_q = ml.route((x.float() + out_q.float()).to(x.dtype), want_scores=False)[0]
+    nxt_b = twin.route((x.float() + out_b.float()).to(x.dtype), want_scores=False)[0]
+    rel = float(((out_q.float() - out_b.float()).norm() / out_b.float().norm()))
+    del twin, wg, wu, wd
+    torch.cuda.empty_cache()
+    return {"tokens": x.shape[0], "k": sp.k, "swaps_per_token_this_layer": swaps(idx_q, idx_b),
+            "swaps_per_token_next_router": swaps(nxt_q, nxt_b), "out_rel_l2_vs_bf16_twin": round(rel, 5)}
+
+
 def prefill_sweep(layout, steps=20, warmup=3):
-    """The prefill layers the MFMA target is set for (T >= 8192), and the INT4
-    layer's prefill: useful-flop MFMA fraction of the whole layer and of its
-    gate/up launch."""
+    """The other prefill layers: DeepSeek-V2-Lite T=8192 (dropless and C=1.25), the
+    DeepSeek-V3 token-sweep step T=4096, the INT4 layer at T=4096 (with its routing drift):
+    useful-flop MFMA fraction of the whole layer and of its gate/up launch."""
     import torch
 
     import moe_synth as S
     res = {}
-    # DeepSeek-V3 also at T=4096, the step of its token sweep below the prefill target
-    for name, Ts in (("dsv2_lite", (8192,)), ("dsv2_lite_cap", (8192,)), ("dsv3", (4096, 16384)),
-                     ("qwen3_int4", (4096,))):
+    for name, Ts in (("dsv2_lite", (8192,)), ("dsv2_lite_cap", (8192,)), ("dsv3", (4096,)), ("qwen3_int4", (4096,))):
         sp = S.SPECS[name]
         lay = S.make_layer(sp, device="cuda")
         ml = moe_layer(sp, lay, layout)
         for T in Ts:
             x = S.make_tokens(sp, T, device="cuda")
-            ms, per, outs, _, _ = time_layer(ml, x, steps, warmup)
-            w = alg_work(sp, T, outs[1], outs[3])
-            res[f"{name}_T{T}"] = {
-                "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
-                "mfma_frac_layer": round(w["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                "mfma_frac_gateup": round(w["gateup_flops"] / (per["gateup"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                "per_launch_us": {n: round(v * 1e3, 2) for n, v in per.items()},
-                "kept_pairs": w["kept"], "pairs": T * sp.k}
-            del x, outs
+            res[f"{name}_T{T}"] = prefill_point(sp, ml, x, steps, warmup)[0]
+            if sp.expert == "int4":
+                res[f"{name}_T{T}"]["drift"] = int4_drift(sp, lay, ml, x, layout)
+            del x
         del ml, lay
         torch.cuda.empty_cache()
     return {"method": f"eager, {steps} timed forwards after {warmup}; useful flops only (dropped pairs and tile "
                       "padding excluded)", "points": res}
 
 
+def roofline_of(sp, T, w, per, workload):
+    t_gu = per["gateup"] * 1e-3
+    achieved = w["gateup_flops"] / t_gu / 1e12
+    return {"bound": "mfma", "kernel": "ffn_tiled32_kernel<gate/up + SwiGLU>", "achieved": round(achieved, 2),
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_record(workload), "alg_bytes_per_launch": gateup_alg_bytes(sp, T, w),
+            "avg_launch_us": round(per["gateup"] * 1e3, 2), "alg_flops_per_launch": w["gateup_flops"]}
+
+
 def main():
     args = parse()
     if args.traffic_record:
+        spec, T = TRAFFIC_WORKLOADS[args.traffic_workload]
         cmds = [f"rocprofv3 --pmc {c} --output-format csv -d <out> -o pmc -- python3 bench.py {a}"
-                for a in ("--steps 5 --warmup 2 --no-cpu --no-decode --no-prefill", "--copy-probe")
+                for a in (f"--profile-layer {spec} --T {T} --steps 3 --warmup 1", "--copy-probe")
                 for c in ("FETCH_SIZE", "WRITE_SIZE")]
-        write_traffic_record(*args.traffic_record, commands=cmds)
+        write_traffic_record(args.traffic_workload, *args.traffic_record, commands=cmds)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -415,7 +523,6 @@ def main():
     import torch
 
     import moe_synth as S
-    from mixture_experts_layer_13_amd import binding as B
 
     torch.cuda.set_device(0)
     if args.copy_probe:
@@ -429,22 +536,24 @@ def main():
         ms = time_layer(ml, x, args.steps, args.warmup)[0]
         print(json.dumps({"layer": args.profile_layer, "T": args.T, "ms_per_forward": round(ms, 4)}), flush=True)
         return
-    sp = S.SPECS["olmoe"]
-    T = args.T
-    lay = S.make_layer(sp, device="cuda")
     if args.decode_only:
+        sp = S.SPECS["olmoe"]
+        lay = S.make_layer(sp, device="cuda")
         print(json.dumps(decode_sweep(sp, lay, args.layout)), flush=True)
+        del lay
+        torch.cuda.empty_cache()
         print(json.dumps(decode_other(args.layout)), flush=True)
         return
+
+    # ---- headline: the DeepSeek-V3-shaped layer at T tokens
+    sp = S.SPECS["dsv3"]
+    T = args.T
+    workload = f"dsv3_T{T}"
+    lay = S.make_layer(sp, device="cuda")
     x = S.make_tokens(sp, T, device="cuda")
     ml = moe_layer(sp, lay, args.layout)
     K = args.steps
-    ms_step, per, outs, nl, wall = time_layer(ml, x, K, args.warmup)
-
-    w = alg_work(sp, T, outs[1], outs[3])
-    t_gu = per["gateup"] * 1e-3
-    achieved = w["gateup_flops"] / t_gu / 1e12
-    traffic = traffic_record()
+    head, (ms_step, per, outs, nl, wall, w) = prefill_point(sp, ml, x, K, args.warmup)
     line = {
         "metric": METRIC,
         "value": round(T / (ms_step * 1e-3), 1),
@@ -458,25 +567,40 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"olmoe_1b7b_layer_T{T}", "T": T, "d": sp.d, "E": sp.E, "k": sp.k,
-                   "ffn": sp.ffn, "launches_per_layer": nl, "weight_layout": args.layout},
-        "roofline": {"bound": "mfma", "kernel": "ffn_tiled32_kernel<gate/up + SwiGLU>", "achieved": round(achieved, 2),
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "avg_launch_us": round(per["gateup"] * 1e3, 2),
-                     "alg_flops_per_launch": w["gateup_flops"]},
-        "layer": {"per_launch_us": {n: round(v * 1e3, 2) for n, v in per.items()},
-                  "alg_flops": w["flops"], "alg_bytes": w["bytes"],
-                  "mfma_frac": round(w["flops"] / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "config": {"workload": f"deepseek_v3_layer_T{T}", "T": T, "d": sp.d, "E": sp.E, "k": sp.k, "ffn": sp.ffn,
+                   "n_shared": sp.n_shared, "ffn_shared": sp.ffn_shared, "launches_per_layer": nl,
+                   "weight_layout": args.layout},
+        "roofline": roofline_of(sp, T, w, per, workload),
+        "layer": {"per_launch_us": head["per_launch_us"], "alg_flops": w["flops"], "alg_bytes": w["bytes"],
+                  "mfma_frac": head["mfma_frac_layer"], "kept_pairs": w["kept"], "touched_experts": w["touched"],
                   "wall_s_timed": round(wall, 3)},
+        "routing": {workload: head["routing"]},
     }
-    if not args.no_decode:
-        line["decode"] = decode_sweep(sp, lay, args.layout)
-        line["decode_other"] = decode_other(args.layout)
+    del ml, outs
+    torch.cuda.empty_cache()
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_tokens=T)  # the whole workload, ~10 s of host time
-    if not args.no_prefill:
-        del ml, lay, x
+        line["cpu_baseline"] = cpu_baseline(sp, lay, x, n_ffn=1024)
+    del lay, x
+    torch.cuda.empty_cache()
+
+    # ---- the OLMoE-shaped layer at T=4096 (a prefill-sized sub-key) and its decode sizes
+    osp = S.SPECS["olmoe"]
+    olay = S.make_layer(osp, device="cuda")
+    ox = S.make_tokens(osp, 4096, device="cuda")
+    oml = moe_layer(osp, olay, args.layout)
+    opt, (oms, oper, oouts, _, _, ow) = prefill_point(osp, oml, ox, K, args.warmup)
+    opt["roofline"] = roofline_of(osp, 4096, ow, oper, "olmoe_T4096")
+    line["olmoe_T4096"] = opt
+    del oml, oouts, ox
+    if not args.no_decode:
+        line["decode"] = decode_sweep(osp, olay, args.layout)
+        del olay
         torch.cuda.empty_cache()
+        line["decode_other"] = decode_other(args.layout)
+    else:
+        del olay
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
         line["prefill"] = prefill_sweep(args.layout)
     print(json.dumps(line), flush=True)
 

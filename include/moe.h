@@ -113,7 +113,13 @@ typedef struct moe_experts {
   const void *shs_gate, *shs_up, *shs_down;
 } moe_experts;
 
-/* Checks a cfg on the host (no device access).  MOE_OK, or the reason. */
+/* Checks a cfg on the host (no device access).  MOE_OK, or the reason.
+ * "MoE: dynamism the compiler cannot remove", batch-1 recipe: every shape a
+ * replayed forward uses is fixed ahead of time, so a cfg is accepted or
+ * rejected once, on the host, and never inside a captured launch sequence.
+ *   cfg: host pointer, read during the call only.  MOE_ERR_INVALID_ARG for a
+ *   NULL cfg or a bad enum / size, MOE_ERR_UNSUPPORTED for a valid layer
+ *   outside the shapes the kernels take; moe_last_error() names the field. */
 moe_status moe_validate(const moe_cfg* cfg);
 
 /* Rows R of the expert-major row buffers (row_token, y_rows): T*k dropless,
@@ -126,7 +132,12 @@ int64_t moe_rows(const moe_cfg* cfg);
 int64_t moe_capacity(const moe_cfg* cfg);
 
 /* Workspace bytes every entry point needs for this cfg (worst case, static).
- * 0 on an invalid cfg.  The workspace needs no initialisation. */
+ * "MoE: dynamism the compiler cannot remove", batch-1 recipe: buffers are
+ * allocated once at fixed addresses and nothing is allocated during a replay;
+ * the size depends on the cfg only (R = T*k rows dropless, E*cap with a
+ * capacity, never on how the tokens route), so one caller-owned buffer of this
+ * size serves every forward of that cfg.  0 on an invalid cfg.  The workspace
+ * needs no initialisation; its contents after a call are unspecified. */
 size_t moe_workspace_bytes(const moe_cfg* cfg);
 
 /* Router: logits, scores, top-k and gates ("MoE: dynamism ...", natural
@@ -169,16 +180,31 @@ moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offs
                           void* y_rows, void* y_shared,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* Weighted combine, fixed order over j, fp32 accumulation, one rounding:
+/* Weighted combine ("MoE: dynamism the compiler cannot remove": the natural
+ * implementation accumulates each selected expert's output into its token's
+ * row, here weighted by the gate; the batch-1 recipe's fixed-shape scatter
+ * becomes a gather by slot_row, so every token writes its row once; "MoE
+ * Research" section 2: shared experts are added with weight 1).  Fixed order
+ * over j, fp32 accumulation, one rounding:
  *   out[t] = sum_{j: slot_row[t,j] in [0, R)} topk_w[t,j] * y_rows[slot_row[t,j]]
- *            + y_shared[t]  (y_shared NULL iff n_shared == 0).  out [T][d]. */
+ *            + y_shared[t]  (y_shared NULL iff n_shared == 0).  out [T][d].
+ *   y_rows [R][d], y_shared [T][d], out [T][d] act dtype, 16-byte aligned;
+ *   slot_row [T][k] int32 and topk_w [T][k] fp32, 4-byte aligned.  A slot_row
+ *   entry outside [0, R) (a dropped pair) contributes nothing. */
 moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* slot_row,
                        const float* topk_w, const void* y_shared, void* out, void* stream);
 
 /* The whole layer in a handful of static-shape launches: route, permute,
- * gate/up SwiGLU GEMM, down GEMM, combine.  Outputs out [T][d], topk_idx,
- * topk_w, drop_mask [T][k].  Same results, bit for bit, as moe_route ->
- * moe_permute -> moe_expert_ffn -> moe_combine on the same inputs. */
+ * gate/up SwiGLU GEMM, down GEMM, combine.  "MoE: dynamism the compiler
+ * cannot remove", batch-1 recipe and its graph-capture answer: fixed shapes,
+ * no host logic and no allocation between launches, so the five launches
+ * capture into one HIP graph per token count; the launch-bound study (picx.dev
+ * summary) is why they are five and not one per expert.
+ *   x [T][d], w_router [E][d] act dtype; logit_bias, select_bias as in
+ *   moe_route; w: expert weights.  Outputs out [T][d] act dtype, topk_idx
+ *   [T][k] int32, topk_w [T][k] fp32, drop_mask [T][k] uint8.  ws: workspace of
+ *   moe_workspace_bytes(cfg) bytes.  Same results, bit for bit, as moe_route ->
+ *   moe_permute -> moe_expert_ffn -> moe_combine on the same inputs. */
 moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router,
                        const float* logit_bias, const float* select_bias,
                        const moe_experts* w, void* out, int32_t* topk_idx,

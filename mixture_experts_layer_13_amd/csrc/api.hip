@@ -211,6 +211,7 @@ template <typename T> T* at(void* ws, size_t off) { return reinterpret_cast<T*>(
 
 bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 bool al4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+bool al2(const void* p) { return ((uintptr_t)p & 1) == 0; }
 
 moe_status check_ws(const Plan& p, void* ws, size_t ws_bytes) {
   if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
@@ -273,12 +274,16 @@ moe_status check_experts(const Plan& p, const moe_experts* w) {
     return fail(MOE_ERR_INVALID_ARG, "INT4 and FP8 experts need s_gate, s_up and s_down");
   if (p.wdt == MOE_FP8_E4M3 && (!al4(w->s_gate) || !al4(w->s_up) || !al4(w->s_down)))
     return fail(MOE_ERR_INVALID_ARG, "FP8 scales must be 4-byte aligned");
+  if (p.wdt == MOE_INT4_G128 && (!al2(w->s_gate) || !al2(w->s_up) || !al2(w->s_down)))
+    return fail(MOE_ERR_INVALID_ARG, "INT4 scales must be 2-byte aligned");
   if (p.S > 0) {
     if (!w->sh_gate || !w->sh_up || !w->sh_down) return fail(MOE_ERR_INVALID_ARG, "shared expert weight pointer is NULL");
     if (!al16(w->sh_gate) || !al16(w->sh_up) || !al16(w->sh_down))
       return fail(MOE_ERR_INVALID_ARG, "shared expert weights must be 16-byte aligned");
     if (p.wdt == MOE_INT4_G128 && (!w->shs_gate || !w->shs_up || !w->shs_down))
       return fail(MOE_ERR_INVALID_ARG, "INT4 shared experts need shs_gate, shs_up and shs_down");
+    if (p.wdt == MOE_INT4_G128 && (!al2(w->shs_gate) || !al2(w->shs_up) || !al2(w->shs_down)))
+      return fail(MOE_ERR_INVALID_ARG, "INT4 shared-expert scales must be 2-byte aligned");
   }
   return MOE_OK;
 }
@@ -441,6 +446,7 @@ moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* sl
   if ((p.S > 0) != (y_shared != nullptr)) return fail(MOE_ERR_INVALID_ARG, "y_shared must be given iff n_shared > 0");
   if (!al16(y_rows) || !al16(out) || (y_shared && !al16(y_shared)))
     return fail(MOE_ERR_INVALID_ARG, "y_rows, y_shared and out must be 16-byte aligned");
+  if (!al4(slot_row) || !al4(topk_w)) return fail(MOE_ERR_INVALID_ARG, "slot_row and topk_w must be 4-byte aligned");
   return hip_ok(launch_combine(p.act, y_rows, slot_row, topk_w, y_shared, out, p.T, p.d, p.k, (int)p.R,
                                (hipStream_t)stream),
                 "combine");

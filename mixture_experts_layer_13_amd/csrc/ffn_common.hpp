@@ -109,6 +109,21 @@ __host__ __device__ inline int tiled_blocks_per_xcd(int64_t routed_tiles_max, in
   const int64_t wmax = routed_tiles_max * wr + shared_tiles * ws;
   return (int)((wmax / 8 + 1 + wmin - 1) / wmin + 2);
 }
+// Routed items of the tile map as the expert kernels read them, clamped so
+// that a corrupted map (a race on the workspace, a stray write into it) gives
+// wrong rows, never an access outside the weights or the row buffers: the item
+// count into [0, items_max], the expert into [0, E), the first row into
+// [0, R), the rows into [1, min(bm, R - first row)]; false for an empty item.
+__device__ __forceinline__ int routed_items(const FfnArgs& a) { return min(max(*a.n_items, 0), a.items_max); }
+__device__ __forceinline__ bool load_item(const FfnArgs& a, int slot, int& e, int& row0, int& mrows) {
+  if (a.R <= 0) return false;
+  const int4 it = a.items[slot];
+  e = min(max(it.x, 0), a.E - 1);
+  row0 = min(max(it.y, 0), a.R - 1);
+  mrows = min(min(it.z, a.bm), a.R - row0);
+  return mrows > 0;
+}
+
 struct TileInfo {
   int e, row0, mrows, n0;
   bool shared;
@@ -117,7 +132,7 @@ __device__ __forceinline__ bool tile_of(const FfnArgs& a, int NT, TileInfo& t) {
   const bool gu = NT == 128;  // gate/up blocks cover 128 channels, down blocks 256 columns
   const int Nr = gu ? a.F : a.d, Ns = gu ? a.S * a.FS : a.d;
   const int nbr = (Nr + NT - 1) / NT, nbs = (Ns + NT - 1) / NT;
-  const int routed_tiles = *a.n_items * nbr;
+  const int routed_tiles = routed_items(a) * nbr;
   const int shared_tiles = a.S > 0 ? a.sh_items * nbs : 0;
   int64_t wr, ws;
   tile_work(gu, a.F, a.S, a.FS, wr, ws);
@@ -148,10 +163,7 @@ __device__ __forceinline__ bool tile_of(const FfnArgs& a, int NT, TileInfo& t) {
   if (!t.shared) {
     const int slot = tile / nbr;
     nb = tile - slot * nbr;
-    const int4 it = a.items[slot];
-    t.e = it.x;
-    t.row0 = it.y;
-    t.mrows = it.z;
+    if (!load_item(a, slot, t.e, t.row0, t.mrows)) return false;
   } else {
     const int sb = tile - routed_tiles;
     const int slot = sb / nbs;

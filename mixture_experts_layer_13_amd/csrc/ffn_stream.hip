@@ -170,11 +170,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   if (!shared) {
     const int slot = bid / nbr;
     nb = bid - slot * nbr;
-    if (slot >= *a.n_items) return;
-    const int4 it = a.items[slot];
-    e = it.x;
-    row0 = it.y;
-    mrows = it.z;
+    if (slot >= routed_items(a) || !load_item(a, slot, e, row0, mrows)) return;
   } else {
     bid -= routed_blocks;
     const int slot = bid / nbs;

@@ -135,6 +135,41 @@ def test_entry_points_reject_bad_arguments_before_launch(B):
     assert B.lib.moe_status_str(B.MOE_ERR_HIP) == b"HIP error"
 
 
+def test_misaligned_index_and_scale_arrays_are_rejected(B):
+    """The combine's slot_row / topk_w must be 4-byte aligned, INT4 scales 2-byte
+    aligned (routed and shared), FP8 scales 4-byte aligned: each misaligned
+    pointer comes back as MOE_ERR_INVALID_ARG before any launch."""
+    P = ctypes.c_void_p
+    fake = P(0x10000)   # never dereferenced: every call below fails validation first
+    c = B.make_cfg(64, 128, 8, 2, 256, act="f32", expert="f32")
+    comb = B.lib.moe_combine
+    assert comb(ctypes.byref(c), fake, P(0x10002), fake, None, fake, None) == B.MOE_ERR_INVALID_ARG   # slot_row
+    assert comb(ctypes.byref(c), fake, fake, P(0x10001), None, fake, None) == B.MOE_ERR_INVALID_ARG   # topk_w
+    assert "4-byte" in B.lib.moe_last_error().decode()
+
+    def ffn(cfg, ew):
+        return B.lib.moe_expert_ffn(ctypes.byref(cfg), fake, fake, fake, ctypes.byref(ew), fake,
+                                    fake if cfg.n_shared else None, fake, 1 << 34, None)
+
+    q = B.make_cfg(64, 256, 8, 2, 256, 1, 256, expert="int4")
+    for field in ("s_gate", "s_up", "s_down", "shs_gate", "shs_up", "shs_down"):
+        ew = B.MoeExperts()
+        for f in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+            setattr(ew, f, 0x10000)
+        for f in ("s_gate", "s_up", "s_down", "shs_gate", "shs_up", "shs_down"):
+            setattr(ew, f, 0x20000)
+        setattr(ew, field, 0x20001)
+        assert ffn(q, ew) == B.MOE_ERR_INVALID_ARG, field
+        assert "2-byte" in B.lib.moe_last_error().decode()
+    f8 = B.make_cfg(16, 256, 8, 2, 256, expert="fp8")
+    for field in ("s_gate", "s_up", "s_down"):
+        ew = B.MoeExperts()
+        ew.w_gate = ew.w_up = ew.w_down = 0x10000
+        ew.s_gate = ew.s_up = ew.s_down = 0x20000
+        setattr(ew, field, 0x20002)
+        assert ffn(f8, ew) == B.MOE_ERR_INVALID_ARG, field
+
+
 def test_pack_rejects_bad_arguments_before_launch(B):
     P = ctypes.c_void_p
     src, dst = P(0x100000), P(0x200000)   # never dereferenced: every call below fails validation first

@@ -63,7 +63,9 @@ def test_forward_matches_oracle(name, T):
     x = S.make_tokens(sp, T, device="cuda")
     out, idx, gates, drop = ml.forward(x)
     torch.cuda.synchronize()
-    nsamp = 4 if sp.d > 4096 else (256 if T > 256 else T)
+    # DeepSeek-V3-shaped layer: 64 sampled tokens at every T (each token's 8 experts
+    # cost the oracle a 7168 x 2048 x 3 FP64 decode apiece); the rest: 256 or all
+    nsamp = min(T, 64) if sp.d > 4096 else (256 if T > 256 else T)
     rows = sample_rows(T, nsamp)
     ref = oracle_run(sp, lay, x, ffn_rows=rows)
     gi, gg, gd = idx.cpu().numpy(), gates.cpu().numpy(), drop.cpu().numpy()
@@ -165,3 +167,66 @@ def test_graph_replay_matches_eager():
                 assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
                                    v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), (T, rep)
         del g
+
+
+@pytest.mark.parametrize("T", [4096, 16384])
+def test_dsv3_busiest_and_shared_expert_rows(T):
+    """Every row of the two busiest experts and of the shared expert of the
+    DeepSeek-V3-shaped layer (K = 7168 gate/up; down over 28 blocks of 256
+    columns; a hot expert split over many 128-row items) through moe_expert_ffn,
+    against the oracle's SwiGLU FFN of the same gathered tokens."""
+    from gpu_harness import ExpertSource, to_f64
+    sp, lay, ml = get_layer("dsv3")
+    x = S.make_tokens(sp, T, device="cuda")
+    idx, gates, _ = ml.route(x, want_scores=False)
+    counts, offsets, row_token, slot_row, drop = ml.permute(idx)
+    y_rows, y_sh = ml.expert_ffn(x, offsets, row_token)
+    torch.cuda.synchronize()
+    cnt, off, rt = counts.cpu().numpy(), offsets.cpu().numpy(), row_token.cpu().numpy()
+    assert cnt.sum() == T * sp.k and off[-1] == T * sp.k
+    xs = to_f64(x)
+    busiest = np.argsort(-cnt, kind="stable")[:2]
+    for e in busiest:
+        lo, hi = int(off[e]), int(off[e + 1])
+        toks = rt[lo:hi]
+        assert hi - lo == cnt[e] and ((toks >= 0) & (toks < T)).all()
+        assert (np.diff(toks) > 0).all()                       # stable t-major rows, one per token
+        assert (idx.cpu().numpy()[toks] == e).any(1).all()      # every row's token picked e
+        ref = O.swiglu_ffn(xs[toks], *ExpertSource(sp, lay)(int(e)))
+        y = y_rows[lo:hi].float().cpu().numpy().astype(np.float64)
+        rel = row_rel_err(y, ref)
+        print(f"\ndsv3 T={T} expert {e}: {hi - lo} rows ({(hi - lo + 127) // 128} items of <= 128), "
+              f"max row rel err {rel.max():.3e}")
+        assert rel.max() <= tol_of(sp)
+    ref = O.swiglu_ffn(xs, *ExpertSource(sp, lay, shared=True)(0))
+    rel = row_rel_err(y_sh.float().cpu().numpy().astype(np.float64), ref)
+    print(f"dsv3 T={T} shared expert: {T} rows, max row rel err {rel.max():.3e}")
+    assert rel.max() <= tol_of(sp)
+
+
+def test_side_stream_forward_after_default_stream_churn():
+    """A forward on a side stream straight after default-stream allocations whose
+    kernels are still queued: MoeLayer allocates its workspace and outputs on the
+    launch stream, so no block freed on the default stream (with writes still
+    pending there) can back them.  Bit for bit the default-stream forward."""
+    sp, lay, ml = get_layer("olmoe")
+    T = 300
+    x = S.make_tokens(sp, T, device="cuda")
+    ref = [t.clone() for t in ml.forward(x)]
+    torch.cuda.synchronize()
+    fresh = layer_of(sp, lay)                       # no workspace yet
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())      # x is ready for s; later default work is not
+    from mixture_experts_layer_13_amd import binding as B
+    nbytes = B.workspace_bytes(fresh.cfg_for(T))
+    junk = torch.empty(nbytes + (1 << 20), dtype=torch.uint8, device="cuda")
+    for _ in range(50):                             # long queue of writes on the default stream
+        junk.fill_(0xA5)
+    del junk                                        # its block returns to the default stream's pool
+    outs = fresh.forward(x, stream=s)
+    more = torch.full((nbytes // 2 + 4096,), 7, dtype=torch.uint8, device="cuda")  # default-stream reuse
+    torch.cuda.synchronize()
+    del more
+    for u, v in zip(ref, outs):
+        assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)

@@ -23,6 +23,34 @@ def test_bf16_decoding_closed_forms():
     assert v[5] == (2 - 2 ** -7) * 2.0 ** 127
 
 
+def _f32_from_fields(bits: int) -> float:
+    """IEEE-754 binary32 decoded field by field (sign, 8-bit biased exponent,
+    23-bit fraction; exponent 0 is subnormal), in exact Python arithmetic."""
+    sign = -1.0 if bits >> 31 else 1.0
+    exp, frac = (bits >> 23) & 0xFF, bits & 0x7FFFFF
+    if exp == 0:
+        return sign * math.ldexp(frac, -149)
+    return sign * math.ldexp((1 << 23) | frac, exp - 150)
+
+
+def test_f32_widening_closed_forms():
+    # 0x3F800000 = 1, 0xC0200000 = -2.5, 0x00000001 = 2^-149 (smallest subnormal),
+    # 0x7F7FFFFF = largest finite, 0x3DCCCCCD = float32(0.1), 0x80000000 = -0
+    bits = np.array([0x3F800000, 0xC0200000, 0x00000001, 0x7F7FFFFF, 0x3DCCCCCD, 0x80000000], np.uint32)
+    v = O.f32_to_f64(bits.view(np.float32))
+    assert v.dtype == np.float64
+    assert v[0] == 1.0 and v[1] == -2.5 and v[2] == 2.0 ** -149
+    assert v[3] == (2 - 2 ** -23) * 2.0 ** 127
+    assert v[4] == 13421773 * 2.0 ** -27 and v[4] != 0.1
+    assert v[5] == 0.0 and math.copysign(1, v[5]) == -1.0
+    # random finite bit patterns, every one against the field-by-field decoding
+    rb = rng.integers(0, 1 << 32, size=2000, dtype=np.uint64).astype(np.uint32)
+    rb = rb[((rb >> 23) & 0xFF) != 0xFF]
+    w = O.f32_to_f64(rb.view(np.float32).reshape(-1, 1))
+    assert w.shape == (len(rb), 1)
+    assert all(w[i, 0] == _f32_from_fields(int(b)) for i, b in enumerate(rb))
+
+
 def test_int4_unpack_bit_by_bit():
     packed = rng.integers(0, 256, size=(3, 5), dtype=np.uint8)
     q = O.int4_unpack(packed)
