@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "moe.h"
@@ -35,6 +36,13 @@ constexpr int kSingleMaxT = 256;   // T up to which routing runs as split router
 static_assert(kSingleMaxT * kMaxK <= kSmallMaxPairs, "every small-T forward must fit the small route's pair buffers");
 constexpr int kStreamMaxT = 64;    // T up to which the expert GEMMs use the streaming kernels
 constexpr int64_t kMaxT = 1 << 20;
+// Experts must average this many rows for the 256-row tiled kernels (ffn_tiled256.hip).  Off by
+// default: measured on the DeepSeek-V3-shaped layer at T=16384 they move half the operand bytes per
+// flop and lift the L2 hit rate from 44% to 74%, but gate/up only went 9.52 -> 9.35 ms and down
+// 4.64 -> 5.29 ms (OLMoE T=4096 gate/up 361 -> 394 us), so the 128-row kernels stay.
+#ifndef MOE_ROWS256_MIN_AVG
+#define MOE_ROWS256_MIN_AVG (1 << 30)
+#endif
 
 struct Plan {
   int T, d, E, k, F, S, FS, act, wdt, score, renorm, tiled;
@@ -159,7 +167,12 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   // registers of 32-row items: measured on OLMoE T=64, 170 -> 161 us) or 32 rows; above 32 a hot
   // expert is split into two items (its weights are read twice), which costs less than the
   // registers (occupancy) of 64-row items
-  q.bm = q.mode == 1 ? kPrefillRows : ((q.T <= 16 || (int64_t)q.T * q.k <= 8 * (int64_t)q.E) ? 16 : 32);
+  // tiled bf16 kernels take 256-row items when experts average at least MOE_ROWS256_MIN_AVG rows
+  // (half the operand bytes per flop of 128-row items, one wave per SIMD); below that the extra
+  // idle rows of each expert's last item and the coarser tail cost more
+  const bool rows256 = q.wdt == MOE_BF16 && (int64_t)q.T * q.k >= (int64_t)MOE_ROWS256_MIN_AVG * q.E;
+  q.bm = q.mode == 1 ? (rows256 ? 2 * kPrefillRows : kPrefillRows)
+                     : ((q.T <= 16 || (int64_t)q.T * q.k <= 8 * (int64_t)q.E) ? 16 : 32);
   // tiled mode with at most 32 rows per expert on average: an expert's weights are read by one
   // row tile (measured: DeepSeek-V3 T=256 2.81 -> 2.61 ms; with several row tiles per expert the
   // L2 reuse they lose costs far more, e.g. OLMoE T=4096 gate/up 313 -> 401 us)

@@ -119,7 +119,8 @@ hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipSt
   } else {
     const int grid = ffn_grid_xcd(a, true, a.F / 128, a.S * a.FS / 128);
     if (grid == 0) return hipSuccess;
-    if (wdt == kBF16) launch_tiled_bf16(true, a, grid, s);
+    if (wdt == kBF16 && a.bm == 256) launch_tiled256_bf16(true, a, grid, s);
+    else if (wdt == kBF16) launch_tiled_bf16(true, a, grid, s);
     else launch_tiled_int4(true, a, grid, s);
   }
   (void)act;
@@ -135,7 +136,8 @@ hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStre
   } else {
     const int grid = ffn_grid_xcd(a, false, (a.d + 255) / 256, (a.d + 255) / 256);
     if (grid == 0) return hipSuccess;
-    if (wdt == kBF16) launch_tiled_bf16(false, a, grid, s);
+    if (wdt == kBF16 && a.bm == 256) launch_tiled256_bf16(false, a, grid, s);
+    else if (wdt == kBF16) launch_tiled_bf16(false, a, grid, s);
     else launch_tiled_int4(false, a, grid, s);
   }
   (void)act;

@@ -1,0 +1,330 @@
+// Tiled (large-M, prefill) bf16 expert FFN kernels for gfx950 with 256-row x
+// 256-weight-row blocks fed through an LDS ring by direct global -> LDS loads.
+//
+// The 128-row kernel (ffn_tiled.hip) keeps one K step of operands in flight per
+// wave in registers; at the chip's measured 1-2 us memory latency under load
+// that leaves its matrix cores waiting about half the time.  Here a block of
+// four waves (one per SIMD) owns 256 rows x 256 weight rows, which halves the
+// operand bytes per flop, and stages both operands in a ring of P = 4 LDS slots
+// of one 32-wide K step each, filled by global_load_lds_dwordx4 (each lane's 16
+// bytes go straight to LDS, no registers held): three K steps stay in flight
+// while one is computed.
+//
+// LDS image of one slot: A (activation rows) then B (weight rows), each 16
+// groups of 16 rows x 64 bytes (32 bf16 of K), 1 KB per group, written by one
+// DMA instruction (lane l's 16 bytes land at byte 16 l of the group).  Weights
+// in the tiled layout keep its unit-major order (16-byte unit 16 q + n holds
+// bytes 16 q .. +15 of row n), so a B group is one contiguous KB of memory.
+// Gathered activation rows use a row-major order (unit 4 n + v holds row n),
+// so each group of four lanes reads one contiguous 64-byte run, with the four
+// units of a row XOR-permuted by (n / 2) % 4.  In both images the MFMA
+// fragment reads (lane l: row l % 32, K half l / 32 of a 16-wide slice) hit
+// distinct banks within every group of eight lanes.
+//
+// Waits.  The compiler tracks LDS written by DMA only coarsely (it drains every
+// outstanding load before the first LDS read of a loop iteration, and a
+// workgroup fence drains them at every barrier), so the DMA instructions are
+// written as inline assembly the compiler does not model, and the kernel waits
+// on the vector-memory counter itself: before the barrier that publishes K step
+// t + 1 each wave waits until only the 8 loads per step it issued for later
+// steps are outstanding; the barrier then also tells every wave that all waves
+// have finished reading the slot that the next DMA overwrites.  The main loop
+// issues no other vector-memory instruction, so those counts are exact.
+//
+// Waves: wave w = 2 i + j owns rows 128 i .. +127 and weight rows of column
+// half j (gate/up: gate channels n0 + 64 j .. +63 and the up rows of the same
+// channels; down: output columns n0 + 128 j .. +127) as 4 x 4 tiles of 32 x 32
+// (v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane).  Every output
+// element sums the same products in the same K order as the 128-row kernel, so
+// the two give identical results, bit for bit.
+#include "ffn_common.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRingP = 4;                // LDS slots
+constexpr int kStepK = 32;               // K elements per slot
+constexpr int kSlotB = 16384;            // bytes of one operand in a slot (16 groups x 1 KB)
+constexpr int kSlot = 2 * kSlotB;        // A then B
+constexpr int kDmaPerStep = 8;           // DMA instructions per wave and K step (4 A + 4 B groups)
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane.  M0 carries
+// the wave-uniform LDS address; it is restored afterwards, so the compiler's own
+// view of M0 stays valid.  One wait state after writing M0 (the LDS-DMA hazard).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(g), "s"(lds)
+      : "memory");
+}
+
+// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// keeps the compiler from moving memory accesses across this point (emits nothing)
+__device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
+// s_barrier with compiler-level ordering on both sides: LDS reads stay on their side of it
+__device__ __forceinline__ void block_barrier() {
+  mem_fence_compiler();
+  __builtin_amdgcn_s_barrier();
+  mem_fence_compiler();
+}
+
+}  // namespace
+
+template <bool GATEUP, bool TILED>
+__global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
+  constexpr int NT = GATEUP ? 128 : 256;  // output channels (gate/up) or columns (down) per block
+  __shared__ __attribute__((aligned(1024))) char smem[kRingP * kSlot];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = w >> 1, wj = w & 1;
+  TileInfo ti;
+  if (!tile_of(a, NT, ti)) return;
+  const int e = ti.e, row0 = ti.row0, mrows = ti.mrows, n0 = ti.n0;
+  const bool shared = ti.shared;
+  const int Kfull = GATEUP ? a.d : (shared ? a.S * a.FS : a.F);
+  const int Kseg = GATEUP ? a.d : (shared ? a.FS : a.F);
+  const int Kb = Kseg * 2;  // bytes per weight row of one K segment
+  const int nkt = Kfull / kStepK;
+
+  // ---- DMA sources: this wave fills A groups and B groups 4 w .. 4 w + 3.
+  // Row-major image (activations, and weights in the row layout): lane l loads row l / 4 of the
+  // group, so every group of four lanes reads one contiguous 64-byte run (rows spread over the
+  // lanes of a quad cost the address and tag units one lookup per lane), and it stores K unit
+  // v = l % 4 of that row's slot, holding logical unit u = v ^ ((row / 2) % 4): the XOR keeps
+  // the fragment reads below (eight lanes, eight rows, one unit) on distinct banks.
+  const int rn = lane >> 2, ru = (lane & 3) ^ ((rn >> 1) & 3);  // row in group, logical 16-byte unit
+  const char* asrc[4];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const int r = min(16 * (4 * w + gi) + rn, mrows - 1);
+    if (GATEUP) {
+      int tok = shared ? row0 + r : a.row_token[row0 + r];
+      tok = min(max(tok, 0), a.T - 1);
+      asrc[gi] = (const char*)a.x + ((size_t)tok * a.d + 8 * ru) * 2;
+    } else {
+      asrc[gi] = (const char*)(shared ? a.hsh : a.h) + ((size_t)(row0 + r) * Kfull + 8 * ru) * 2;
+    }
+  }
+  const char* bmat[2];
+  if (GATEUP) {
+    bmat[0] = (const char*)(shared ? a.shg : expert_mat<bf16>(a.wg, e, a.F, a.d));
+    bmat[1] = (const char*)(shared ? a.shu : expert_mat<bf16>(a.wu, e, a.F, a.d));
+  } else {
+    bmat[0] = bmat[1] = (const char*)(shared ? a.shd : expert_mat<bf16>(a.wd, e, a.d, Kseg));
+  }
+  uint32_t boff[4];
+  const char* bsrc[4];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const int g = 4 * w + gi;  // B group of the block: gate/up 0..7 gate, 8..15 up
+    int row;
+    if (GATEUP) row = n0 + 16 * (g & 7) + rn;
+    else row = min(n0 + 16 * g, a.d - 16) + rn;  // a last block may run past d: re-read, never stored
+    // tiled layout: the group's KB of this K chunk is contiguous and lane l takes its bytes 16 l
+    // (unit-major image); row layout: the row-major image as for the activations
+    boff[gi] = TILED ? (uint32_t)(row & ~15) * Kb + 16 * lane : (uint32_t)row * Kb + 16 * ru;
+    bsrc[gi] = bmat[GATEUP ? (g >> 3) : 0];
+  }
+  constexpr uint32_t cstride = TILED ? 1024u : 64u;  // bytes between consecutive 32-K chunks of a row
+  // byte offset of K step kt inside the weight matrix (shared down: slab kt*32 / Kseg)
+  auto woff = [&](int kt) -> size_t {
+    const int k0 = kt * kStepK;
+    const int slab = (!GATEUP && shared) ? k0 / Kseg : 0;
+    const int kk = k0 - slab * Kseg;
+    return (size_t)slab * a.d * Kb + (size_t)(kk / kStepK) * cstride;
+  };
+  auto issue = [&](int kt) {
+    const uint32_t slot = lds0 + (uint32_t)(kt % kRingP) * kSlot;
+    const size_t wo = woff(kt);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) dma16(asrc[gi] + (size_t)kt * (kStepK * 2), slot + (4 * w + gi) * 1024);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) dma16(bsrc[gi] + wo + boff[gi], slot + kSlotB + (4 * w + gi) * 1024);
+  };
+
+  // ---- fragment reads: lane l takes row n = l % 16 of group 2 m + (l % 32) / 16 of a 32-row tile
+  // and logical unit u = 2 s + l / 32 of slice s: at byte 64 n + 16 (u ^ ((n / 2) % 4)) of the
+  // row-major image, at 256 u + 16 n of the unit-major one.  Slice 1 of the row-major image is
+  // slice 0's offset with bit 5 flipped.
+  const int fn = lane & 15, fh = lane >> 5, fx = (fn >> 1) & 3;
+  const int rofs = ((lane >> 4) & 1) * 1024 + 64 * fn + 16 * ((fx & 2) | (fh ^ (fx & 1)));
+  const int uofs = ((lane >> 4) & 1) * 1024 + 256 * fh + 16 * fn;
+  const int aofs[2] = {rofs, rofs ^ 32};
+  const int bofs[2] = {TILED ? uofs : rofs, TILED ? uofs + 512 : (rofs ^ 32)};
+  int ga[4], gb[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) ga[m] = 8 * wi + 2 * m;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) gb[n] = GATEUP ? ((n >> 1) * 8 + 4 * wj + 2 * (n & 1)) : (8 * wj + 2 * n);
+  const bool active = 128 * wi < mrows;  // a wave whose rows lie past the item's end only moves data
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x16{};
+  u32x4 fa[2][4], fb[2][4];
+  auto rd = [&](int kt, int s, u32x4 (&A)[4], u32x4 (&B)[4]) {
+    const char* slot = smem + (kt % kRingP) * kSlot;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A[m] = *reinterpret_cast<const u32x4*>(slot + aofs[s] + ga[m] * 1024);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) B[n] = *reinterpret_cast<const u32x4*>(slot + kSlotB + bofs[s] + gb[n] * 1024);
+  };
+  auto mma = [&](const u32x4 (&A)[4], const u32x4 (&B)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[m][n] = mma32_bf16(A[m], B[n], acc[m][n]);
+  };
+  // the 8 LDS reads of one slice go out between the first 8 of the 16 MFMAs of the other
+  // (pinned: left alone, the scheduler bunches them)
+  auto pin_slice = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+
+  // Main loop.  ACT: this wave has rows to compute (else it only moves data and meets the barriers).
+  auto run = [&](auto act_tag) {
+    constexpr bool ACT = decltype(act_tag)::value;
+    const int pro = min(kRingP, nkt);
+    for (int kt = 0; kt < pro; ++kt) issue(kt);
+    if (pro >= 4) wait_vm<3 * kDmaPerStep>();  // K step 0 landed; the others stay in flight
+    else if (pro == 3) wait_vm<2 * kDmaPerStep>();
+    else if (pro == 2) wait_vm<kDmaPerStep>();
+    else wait_vm<0>();
+    block_barrier();
+    if (ACT) rd(0, 0, fa[0], fb[0]);
+    int kt = 0;
+    // steady state: K step kt + 1 must have landed at the barrier, kt + 2 and kt + 3 stay in
+    // flight, and K step kt + 4 goes into the slot of kt (every wave has read it by then)
+    for (; kt + kRingP < nkt; ++kt) {
+      if (ACT) {
+        rd(kt, 1, fa[1], fb[1]);
+        mma(fa[0], fb[0]);
+        pin_slice();
+        mem_fence_compiler();
+        wait_lgkm0();
+      }
+      wait_vm<2 * kDmaPerStep>();
+      block_barrier();
+      issue(kt + kRingP);
+      if (ACT) {
+        rd(kt + 1, 0, fa[0], fb[0]);
+        mma(fa[1], fb[1]);
+        pin_slice();
+      }
+    }
+    // the last (at most four) K steps: everything is issued, the waits shrink
+    for (; kt < nkt; ++kt) {
+      if (ACT) {
+        rd(kt, 1, fa[1], fb[1]);
+        mma(fa[0], fb[0]);
+        mem_fence_compiler();
+        wait_lgkm0();
+      }
+      if (kt + 1 < nkt) {
+        const int later = nkt - 2 - kt;  // K steps issued after kt + 1
+        if (later >= 2) wait_vm<2 * kDmaPerStep>();
+        else if (later == 1) wait_vm<kDmaPerStep>();
+        else wait_vm<0>();
+        block_barrier();
+        if (ACT) rd(kt + 1, 0, fa[0], fb[0]);
+      }
+      if (ACT) mma(fa[1], fb[1]);
+    }
+  };
+  if (active) run(std::true_type{});
+  else run(std::false_type{});
+
+  // ---- epilogue through LDS: staged 16-byte row chunks
+  wait_vm<0>();
+  __syncthreads();  // every wave is done with the ring
+  bf16* const stage = reinterpret_cast<bf16*>(smem);
+  bf16* const out = (bf16*)(GATEUP ? (shared ? a.hsh : a.h) : (shared ? a.ysh : a.y));
+  const int ld = GATEUP ? (shared ? a.S * a.FS : a.F) : a.d;
+  const int h = lane >> 5, c = lane & 31;
+  if (GATEUP) {
+    // 256 rows x 128 channels: wave (i, j) writes rows 128 i.., channels 64 j..
+    constexpr int LDH = 128 + 8;
+    if (active) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = 128 * wi + 32 * m + 8 * (i >> 2) + 4 * h + (i & 3);
+            stage[r * LDH + 64 * wj + 32 * n + c] = (bf16)(silu(acc[m][n][i]) * acc[m][n + 2][i]);
+          }
+        mem_fence_compiler();
+      }
+    }
+    __syncthreads();
+    constexpr int CK = 128 / 8;
+#pragma unroll 4
+    for (int q = 0; q < 256 * CK / 256; ++q) {
+      const int idx = tid + 256 * q, r = idx / CK, ck = idx % CK;
+      if (r < mrows) st16(out + (size_t)(row0 + r) * ld + n0 + 8 * ck, *reinterpret_cast<const u32x4*>(&stage[r * LDH + 8 * ck]));
+    }
+  } else {
+    // 256 rows x 256 columns, in two passes of 128 rows (the staging tile would not fit at once)
+    constexpr int LDH = 256 + 8;
+    constexpr int CK = 256 / 8;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (wi == pass && active) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int r = 32 * m + 8 * (i >> 2) + 4 * h + (i & 3);
+              stage[r * LDH + 128 * wj + 32 * n + c] = (bf16)acc[m][n][i];
+            }
+          mem_fence_compiler();  // one row tile at a time keeps the accumulator reads short-lived
+        }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int q = 0; q < 128 * CK / 256; ++q) {
+        const int idx = tid + 256 * q, r = idx / CK, ck = idx % CK, col = n0 + 8 * ck;
+        const int row = 128 * pass + r;
+        if (row < mrows && col < a.d)
+          st16(out + (size_t)(row0 + row) * ld + col, *reinterpret_cast<const u32x4*>(&stage[r * LDH + 8 * ck]));
+      }
+      __syncthreads();
+    }
+  }
+}
+
+void launch_tiled256_bf16(bool gateup, const FfnArgs& a, int grid, hipStream_t s) {
+  if (gateup) {
+    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled256_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((ffn_tiled256_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled256_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((ffn_tiled256_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+  }
+}
+
+}  // namespace moe

@@ -271,13 +271,13 @@ __device__ __forceinline__ int wave_exclusive_scan256(const int* in, int* out, i
 }
 
 // Item i of the n = ceil(kept / bm) items of an expert with `kept` rows from row `first`.
-// For the tiled kernels (bm = 128) the expert's 32-row tiles are spread evenly over its items
+// For the tiled kernels (bm = 128 or 256) the expert's 32-row tiles are spread evenly over its items
 // (their sizes differ by at most 32 rows), so the items that read the same weight slabs run
 // for about as long, instead of n - 1 full items and one short one that runs ahead of them
 // (measured: Qwen3 INT4 T=4096 0.495 -> 0.483 ms, DeepSeek-V2-Lite T=8192 1.324 -> 1.302 ms).
 // Otherwise consecutive bm-row slices.
 __device__ __forceinline__ int4 item_of(int e, int first, int kept, int n, int i, int bm) {
-  if (bm != kPrefillRows) return make_int4(e, first + i * bm, min(bm, kept - i * bm), 0);
+  if (bm < kPrefillRows) return make_int4(e, first + i * bm, min(bm, kept - i * bm), 0);
   const int tiles = (kept + 31) / 32, base = tiles / n, extra = tiles % n;
   const int s = 32 * (i * base + min(i, extra));
   return make_int4(e, first + s, min(32 * (base + (i < extra ? 1 : 0)), kept - s), 0);
