@@ -211,6 +211,27 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router,
                        float* topk_w, uint8_t* drop_mask,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same launches,
+ * with the workspace taken from a built-in device array of
+ * moe_noalloc_scratch_bytes() = 64 MiB per device (held from library load to
+ * process end) instead of a caller buffer.  Nothing is allocated: the array's
+ * address on the current device is looked up once (hipGetSymbolAddress) and
+ * cached.  Enough for every decode-sized forward (e.g. DeepSeek-V3-shaped at
+ * T = 256: 37 MiB); a cfg whose moe_workspace_bytes exceeds it returns
+ * MOE_ERR_WORKSPACE before any launch, with no device access.
+ * The current device must own `stream` and every pointer.  All calls on one
+ * device share its array, which keeps the last call's contents (the layer
+ * needs none of them): two calls that overlap in time on one device race and
+ * must be ordered, e.g. on one stream.  Arguments as moe_forward. */
+moe_status moe_forward_noalloc(const moe_cfg* cfg, const void* x, const void* w_router,
+                               const float* logit_bias, const float* select_bias,
+                               const moe_experts* w, void* out, int32_t* topk_idx,
+                               float* topk_w, uint8_t* drop_mask, void* stream);
+
+/* Bytes of the built-in workspace of moe_forward_noalloc (per device). */
+int64_t moe_noalloc_scratch_bytes(void);
+
 /* Route replay (the launch-bound study's Sub-study 2: the routes of one
  * model replayed through a layer's expert weights; replaying the layer's own
  * routes must return its baseline exactly).  The layer from given routes:

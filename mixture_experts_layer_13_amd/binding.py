@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
                                        ctypes.c_size_t, P]),
         "moe_forward_with_routes": (ctypes.c_int, [C, P, P, P, ctypes.POINTER(MoeExperts), P, P, P,
                                                    ctypes.c_size_t, P]),
+        "moe_forward_noalloc": (ctypes.c_int, [C, P, P, P, P, ctypes.POINTER(MoeExperts), P, P, P, P, P]),
+        "moe_noalloc_scratch_bytes": (ctypes.c_int64, []),
         "moe_pack_weights": (ctypes.c_int, [ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int32, P]),
         "moe_set_timing_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -199,3 +201,11 @@ def moe_forward(cfg, x, w_router, logit_bias, select_bias, w: MoeExperts, out, t
     _check(lib.moe_forward(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_bias), _p(select_bias),
                            ctypes.byref(w), _p(out), _p(topk_idx), _p(topk_w), _p(drop_mask), _p(ws), ws.numel(),
                            _stream(stream)))
+
+
+def moe_forward_noalloc(cfg, x, w_router, logit_bias, select_bias, w: MoeExperts, out, topk_idx, topk_w,
+                        drop_mask, stream=None):
+    """moe_forward with the library's built-in device workspace (no workspace argument)."""
+    _check(lib.moe_forward_noalloc(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_bias), _p(select_bias),
+                                   ctypes.byref(w), _p(out), _p(topk_idx), _p(topk_w), _p(drop_mask),
+                                   _stream(stream)))

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -354,6 +355,33 @@ moe_status enqueue_route(const Plan& p, const void* x, const void* wr, const Rou
   return hip_ok(launch_router_fused(p.act, x, wr, ra, p.rt, at<int32_t>(ws, p.o_hist), s), "router");
 }
 
+// ---- the built-in workspace of moe_forward_noalloc
+// A file-scope device array, so a forward can run with no allocation at all.  Host code
+// never uses the array's name as an address: each device's copy is at its own address,
+// looked up once per device with hipGetSymbolAddress and kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -511,6 +539,25 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   mark(5, nl, s);
   return st;
 }
+
+moe_status moe_forward_noalloc(const moe_cfg* cfg, const void* x, const void* w_router, const float* logit_bias,
+                               const float* select_bias, const moe_experts* w, void* out, int32_t* topk_idx,
+                               float* topk_w, uint8_t* drop_mask, void* stream) {
+  Plan p;
+  moe_status st;
+  if ((st = make_plan(cfg, &p))) return st;
+  if (p.T == 0) return MOE_OK;
+  if (p.total > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "this cfg needs %zu workspace bytes; the built-in scratch holds %zu (use moe_forward with a "
+                "caller-owned workspace)", p.total, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws))) return st;
+  return moe_forward(cfg, x, w_router, logit_bias, select_bias, w, out, topk_idx, topk_w, drop_mask, ws,
+                     kScratchBytes, stream);
+}
+
+int64_t moe_noalloc_scratch_bytes(void) { return (int64_t)kScratchBytes; }
 
 moe_status moe_forward_with_routes(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, const float* topk_w,
                                    const moe_experts* w, void* out, uint8_t* drop_mask, void* ws, size_t ws_bytes,

@@ -185,3 +185,24 @@ def test_pack_rejects_bad_arguments_before_launch(B):
     assert pack(B.MOE_BF16, P(0x100008), dst, 16, 64, None) == B.MOE_ERR_INVALID_ARG  # misaligned
     assert pack(B.MOE_BF16, src, P(0x100400), 16, 64, None) == B.MOE_ERR_INVALID_ARG  # overlapping
     assert pack(B.MOE_BF16, src, src, 16, 64, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_forward_rejects_oversized_cfg_before_device_access(B):
+    """The built-in workspace is 64 MiB; a cfg that needs more fails on the host with
+    MOE_ERR_WORKSPACE (no device is touched: this runs without a GPU)."""
+    assert B.lib.moe_noalloc_scratch_bytes() == 64 << 20
+    P = ctypes.c_void_p
+    fake = P(0x10000)
+    ew = B.MoeExperts()
+    ew.w_gate = ew.w_up = ew.w_down = ew.sh_gate = ew.sh_up = ew.sh_down = 0x10000
+    big = B.make_cfg(16384, 7168, 256, 8, 2048, 1, 2048, score="sigmoid", renorm=True, gate_scale=2.5)
+    assert B.workspace_bytes(big) > 64 << 20
+    st = B.lib.moe_forward_noalloc(ctypes.byref(big), fake, fake, None, None, ctypes.byref(ew), fake, fake, fake,
+                                   fake, None)
+    assert st == B.MOE_ERR_WORKSPACE and "built-in scratch" in B.lib.moe_last_error().decode()
+    zero = B.make_cfg(0, 7168, 256, 8, 2048, 1, 2048)
+    assert B.lib.moe_forward_noalloc(ctypes.byref(zero), None, None, None, None, ctypes.byref(ew), None, None, None,
+                                     None, None) == B.MOE_OK
+    # the decode-sized layers fit: DeepSeek-V3-shaped at T = 256, OLMoE-shaped at T = 64
+    assert B.workspace_bytes(B.make_cfg(256, 7168, 256, 8, 2048, 1, 2048)) <= 64 << 20
+    assert B.workspace_bytes(B.make_cfg(64, 2048, 64, 8, 1024)) <= 64 << 20
