@@ -130,16 +130,27 @@ def moe_layer(sp, lay, layout):
         mats = [None if m is None else B.pack_tiled(m, sp.expert) for m in mats]
     wg, wu, wd, shg, shu, shd = mats
     return MoeLayer(cfg, lay.w_router, wg, wu, wd, logit_bias=lay.logit_bias, select_bias=lay.select_bias,
-                    s_gate=lay.s_gate, s_up=lay.s_up, s_down=lay.s_down, sh_gate=shg, sh_up=shu, sh_down=shd)
+                    s_gate=lay.s_gate, s_up=lay.s_up, s_down=lay.s_down, sh_gate=shg, sh_up=shu, sh_down=shd,
+                    shs_gate=lay.shs_gate, shs_up=lay.shs_up, shs_down=lay.shs_down)
 
 
-def expert_bytes(sp):
-    n = 3 * sp.d * sp.ffn
+def expert_bytes(sp, ffn=None):
+    ffn = sp.ffn if ffn is None else ffn
+    n = 3 * sp.d * ffn
     if sp.expert == "int4":
-        return n // 2 + (3 * sp.d * sp.ffn // 128) * 2
+        return n // 2 + (3 * sp.d * ffn // 128) * 2
     if sp.expert == "fp8":  # one byte per weight and an fp32 scale per output channel
-        return n + (2 * sp.ffn + sp.d) * 4
+        return n + (2 * ffn + sp.d) * 4
     return n * (4 if sp.expert == "f32" else 2)
+
+
+def shared_bytes(sp):
+    """Bytes of the shared experts (INT4 layers keep bf16 shared experts, FP8 layers FP8 ones)."""
+    if not sp.n_shared:
+        return 0
+    if sp.expert == "int4":
+        return sp.n_shared * 3 * sp.d * sp.ffn_shared * 2
+    return sp.n_shared * expert_bytes(sp, sp.ffn_shared)
 
 
 def alg_work(sp, T, idx, drop):
@@ -150,8 +161,7 @@ def alg_work(sp, T, idx, drop):
     touched = int(torch.unique(idx[kept]).numel()) if kept.any() else 0
     n_kept = int(kept.sum().item())
     es = 4 if sp.act == "f32" else 2
-    byts = (touched * expert_bytes(sp) + sp.n_shared * 3 * sp.d * sp.ffn_shared * es + sp.E * sp.d * es
-            + 2 * T * sp.d * es)
+    byts = touched * expert_bytes(sp) + shared_bytes(sp) + sp.E * sp.d * es + 2 * T * sp.d * es
     gateup = 4.0 * sp.d * sp.ffn * n_kept + 4.0 * sp.d * sp.ffn_shared * sp.n_shared * T
     flops = 1.5 * gateup + 2.0 * T * sp.d * sp.E
     return dict(bytes=byts, flops=flops, gateup_flops=gateup, touched=touched, kept=n_kept)
@@ -475,13 +485,16 @@ def int4_drift(sp, lay, ml, x, layout):
 
 def prefill_sweep(layout, steps=20, warmup=3):
     """The other prefill layers: DeepSeek-V2-Lite T=8192 (dropless and C=1.25), the
-    DeepSeek-V3 token-sweep step T=4096, the INT4 layer at T=4096 (with its routing drift):
-    useful-flop MFMA fraction of the whole layer and of its gate/up launch."""
+    DeepSeek-V3 token-sweep step T=4096, the INT4 layer at T=4096 (with its routing drift),
+    and FP8 experts (OLMoE-shaped T=4096, DeepSeek-V2-Lite-shaped T=8192 with FP8 shared
+    experts): useful-flop fraction of the bf16 MFMA peak (every path multiplies in bf16) of
+    the whole layer and of its gate/up launch."""
     import torch
 
     import moe_synth as S
     res = {}
-    for name, Ts in (("dsv2_lite", (8192,)), ("dsv2_lite_cap", (8192,)), ("dsv3", (4096,)), ("qwen3_int4", (4096,))):
+    for name, Ts in (("dsv2_lite", (8192,)), ("dsv2_lite_cap", (8192,)), ("dsv3", (4096,)), ("qwen3_int4", (4096,)),
+                     ("olmoe_fp8", (4096,)), ("dsv2_lite_fp8", (8192,))):
         sp = S.SPECS[name]
         lay = S.make_layer(sp, device="cuda")
         ml = moe_layer(sp, lay, layout)

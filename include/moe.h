@@ -70,13 +70,15 @@ typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
  * 1 <= k <= min(E, 8), d, ffn, ffn_shared multiples of 128, 0 <= n_shared <= 8,
  * act_dtype MOE_F32 or MOE_BF16 (x, w_router, y_rows, y_shared, out),
  * expert_dtype equal to act_dtype, or MOE_INT4_G128 with act_dtype MOE_BF16,
- * or MOE_FP8_E4M3 with act_dtype MOE_BF16, T <= 64 and n_shared == 0,
+ * or MOE_FP8_E4M3 with act_dtype MOE_BF16,
  * and every expert matrix (ffn x d, ffn_shared x d) under 2 GiB.
  * FP8 experts ("MoE at the inference level", workarounds: fp8 expert weights
  * halve the bytes): one byte per weight in the OCP E4M3 format ("fn":
  * exponent bias 7, no infinities, largest value 448), w = fp8 * s with one
- * fp32 scale per output channel, s_gate / s_up [E][ffn], s_down [E][d]; the
- * decode kernels convert each byte to bf16 exactly.
+ * fp32 scale per output channel, s_gate / s_up [E][ffn], s_down [E][d]
+ * (shared experts: shs_gate / shs_up [S][ffn_shared], shs_down [S][d]); the
+ * activations stay bf16.  The decode kernels convert each byte to bf16 exactly
+ * and apply the scale in fp32; the prefill kernels round fp8 * s to bf16 once.
  * Group-limited selection ("MoE Research", section 2, node-limited routing;
  * "MoE at the inference level", workarounds, device-limited routing): with
  * n_groups = G > 0 the experts form G equal groups of consecutive indices

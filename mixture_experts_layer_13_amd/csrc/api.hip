@@ -83,8 +83,6 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   const bool quant = c->expert_dtype == MOE_INT4_G128 || c->expert_dtype == MOE_FP8_E4M3;
   if (!(c->expert_dtype == c->act_dtype || (quant && c->act_dtype == MOE_BF16)))
     return fail(MOE_ERR_UNSUPPORTED, "expert_dtype=%d with act_dtype=%d", c->expert_dtype, c->act_dtype);
-  if (c->expert_dtype == MOE_FP8_E4M3 && (c->T > kStreamMaxT || c->n_shared > 0))
-    return fail(MOE_ERR_UNSUPPORTED, "FP8 experts: decode sizes only (T <= %d) and no shared experts", kStreamMaxT);
   if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID)
     return fail(MOE_ERR_INVALID_ARG, "score=%d is not a moe_score", c->score);
   if (c->renorm != 0 && c->renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm=%d is not 0 or 1", c->renorm);
@@ -298,6 +296,10 @@ moe_status check_experts(const Plan& p, const moe_experts* w) {
       return fail(MOE_ERR_INVALID_ARG, "INT4 shared experts need shs_gate, shs_up and shs_down");
     if (p.wdt == MOE_INT4_G128 && (!al2(w->shs_gate) || !al2(w->shs_up) || !al2(w->shs_down)))
       return fail(MOE_ERR_INVALID_ARG, "INT4 shared-expert scales must be 2-byte aligned");
+    if (p.wdt == MOE_FP8_E4M3 && (!w->shs_gate || !w->shs_up || !w->shs_down))
+      return fail(MOE_ERR_INVALID_ARG, "FP8 shared experts need shs_gate, shs_up and shs_down");
+    if (p.wdt == MOE_FP8_E4M3 && (!al4(w->shs_gate) || !al4(w->shs_up) || !al4(w->shs_down)))
+      return fail(MOE_ERR_INVALID_ARG, "FP8 shared-expert scales must be 4-byte aligned");
   }
   return MOE_OK;
 }

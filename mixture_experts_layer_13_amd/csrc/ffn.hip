@@ -13,8 +13,8 @@
 //    item (<= 64 rows of one expert) and a few output channels and reads its
 //    weight slice once, straight from memory into MFMA operands;
 //  - tiled kernels (large M, prefill; ffn_tiled.hip for bf16,
-//    ffn_tiled_int4.hip for INT4 weights): 128-row x 256-weight-row blocks,
-//    activations through double-buffered LDS.
+//    ffn_tiled_int4.hip for INT4 and ffn_tiled_fp8.hip for FP8 weights):
+//    128-row x 256-weight-row blocks, activations through double-buffered LDS.
 // The gate/up kernels fuse the SwiGLU epilogue silu(x Wg) * (x Wu) and write
 // the bf16 (fp32 for fp32 layers) intermediate h; the down kernels write
 // y_rows.  INT4 weights (two's-complement nibbles, bf16 scale per 128-K group)
@@ -121,6 +121,7 @@ hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipSt
     if (grid == 0) return hipSuccess;
     if (wdt == kBF16 && a.bm == 256) launch_tiled256_bf16(true, a, grid, s);
     else if (wdt == kBF16) launch_tiled_bf16(true, a, grid, s);
+    else if (wdt == kFP8) launch_tiled_fp8(true, a, grid, s);
     else launch_tiled_int4(true, a, grid, s);
   }
   (void)act;
@@ -138,6 +139,7 @@ hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStre
     if (grid == 0) return hipSuccess;
     if (wdt == kBF16 && a.bm == 256) launch_tiled256_bf16(false, a, grid, s);
     else if (wdt == kBF16) launch_tiled_bf16(false, a, grid, s);
+    else if (wdt == kFP8) launch_tiled_fp8(false, a, grid, s);
     else launch_tiled_int4(false, a, grid, s);
   }
   (void)act;

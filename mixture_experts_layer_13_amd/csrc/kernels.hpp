@@ -85,6 +85,7 @@ int stream_channels_per_block(bool gateup, int wdt);
 void launch_tiled_bf16(bool gateup, const FfnArgs& a, int grid, hipStream_t s);
 void launch_tiled256_bf16(bool gateup, const FfnArgs& a, int grid, hipStream_t s);
 void launch_tiled_int4(bool gateup, const FfnArgs& a, int grid, hipStream_t s);
+void launch_tiled_fp8(bool gateup, const FfnArgs& a, int grid, hipStream_t s);
 
 // expert FFN: mode 0 = streaming small-M kernels, 1 = LDS-tiled MFMA kernels
 hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s);

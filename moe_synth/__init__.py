@@ -89,7 +89,9 @@ SPECS = {
 # DeepSeek-V2-Lite is also run with a fixed capacity C = 1.25.
 SPECS["dsv2_lite_cap"] = SPECS["dsv2_lite"].replace(name="dsv2_lite_cap", capacity=(5, 4))
 # the OLMoE-shaped layer with FP8 (E4M3) expert weights and per-channel scales (decode sizes)
-SPECS["olmoe_fp8"] = SPECS["olmoe"].replace(name="olmoe_fp8", cfg_id=5, expert="fp8", tokens=(1, 8, 32, 64))
+SPECS["olmoe_fp8"] = SPECS["olmoe"].replace(name="olmoe_fp8", cfg_id=5, expert="fp8", tokens=(1, 8, 32, 64, 4096))
+# the DeepSeek-V2-Lite-shaped layer with FP8 routed and shared experts (prefill)
+SPECS["dsv2_lite_fp8"] = SPECS["dsv2_lite"].replace(name="dsv2_lite_fp8", cfg_id=6, expert="fp8")
 
 
 def spec(name: str) -> LayerSpec:
@@ -167,6 +169,9 @@ class Layer:
     sh_gate: Optional[torch.Tensor] = None
     sh_up: Optional[torch.Tensor] = None
     sh_down: Optional[torch.Tensor] = None
+    shs_gate: Optional[torch.Tensor] = None   # FP8 shared-expert scales [S][N] (None otherwise)
+    shs_up: Optional[torch.Tensor] = None
+    shs_down: Optional[torch.Tensor] = None
 
 
 def _expert_mats(sp: LayerSpec, n: int, ffn: int, ids, seed, device, chunk):
@@ -221,10 +226,12 @@ def make_layer(sp: LayerSpec, device="cpu", seed: int = 0, chunk: int = 16) -> L
     (wg, sg), (wu, su), (wd, sd) = _expert_mats(sp, sp.E, sp.ffn, (_T_WG, _T_WU, _T_WD), seed, device, chunk)
     lay = Layer(sp, w_router, logit_bias, select_bias, wg, wu, wd, sg, su, sd)
     if sp.n_shared:
-        (a, _), (b, _), (c, _) = _expert_mats(sp.replace(expert="bf16" if sp.expert == "int4" else sp.expert),
-                                              sp.n_shared, sp.ffn_shared, (_T_SG, _T_SU, _T_SD), seed,
-                                              device, chunk)
+        (a, sa), (b, sb), (c, sc) = _expert_mats(sp.replace(expert="bf16" if sp.expert == "int4" else sp.expert),
+                                                 sp.n_shared, sp.ffn_shared, (_T_SG, _T_SU, _T_SD), seed,
+                                                 device, chunk)
         lay.sh_gate, lay.sh_up, lay.sh_down = a, b, c
+        if sp.expert == "fp8":
+            lay.shs_gate, lay.shs_up, lay.shs_down = sa, sb, sc
     return lay
 
 

@@ -38,7 +38,8 @@ def layer_of(sp: S.LayerSpec, lay: S.Layer, layout: str = "rows"):
     wg, wu, wd, shg, shu, shd = mats
     return MoeLayer(cfg_of(sp, 1, layout), lay.w_router, wg, wu, wd, logit_bias=lay.logit_bias,
                     select_bias=lay.select_bias, s_gate=lay.s_gate, s_up=lay.s_up, s_down=lay.s_down,
-                    sh_gate=shg, sh_up=shu, sh_down=shd)
+                    sh_gate=shg, sh_up=shu, sh_down=shd, shs_gate=lay.shs_gate, shs_up=lay.shs_up,
+                    shs_down=lay.shs_down)
 
 
 # ---------------------------------------------------------------- host copies for the oracle
@@ -62,6 +63,9 @@ class ExpertSource:
     def __call__(self, e: int):
         L = self.lay
         if self.shared:
+            if self.sp.expert == "fp8":
+                return [O.fp8_dequant(q[e].cpu().numpy(), s[e].cpu().numpy())
+                        for q, s in ((L.sh_gate, L.shs_gate), (L.sh_up, L.shs_up), (L.sh_down, L.shs_down))]
             mats = (L.sh_gate[e], L.sh_up[e], L.sh_down[e])
             return [to_f64(m) for m in mats]
         if self.sp.expert == "int4":

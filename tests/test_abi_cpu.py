@@ -65,11 +65,11 @@ def test_validation_errors(B):
     assert B.validate(B.make_cfg(4, 32768, 8, 2, 16384)) == B.MOE_OK               # 1 GiB
     assert B.validate(B.make_cfg(4, 32768, 8, 2, 16384, act="f32", expert="f32")) == B.MOE_ERR_UNSUPPORTED
     assert B.validate(B.make_cfg(4, 1024, 8, 2, 512, 1, 1 << 20)) != B.MOE_OK
-    # FP8 experts: bf16 activations, decode sizes (T <= 64), no shared experts
+    # FP8 experts: bf16 activations, every T, shared experts allowed (FP8 too)
     assert B.validate(B.make_cfg(64, 2048, 64, 8, 1024, expert="fp8")) == B.MOE_OK
-    assert B.validate(B.make_cfg(65, 2048, 64, 8, 1024, expert="fp8")) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(B.make_cfg(8192, 2048, 64, 8, 1024, expert="fp8")) == B.MOE_OK
     assert B.validate(B.make_cfg(8, 2048, 64, 8, 1024, act="f32", expert="fp8")) == B.MOE_ERR_UNSUPPORTED
-    assert B.validate(B.make_cfg(8, 2048, 64, 8, 1024, 1, 1024, expert="fp8")) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(B.make_cfg(8192, 2048, 64, 6, 1408, 2, 1408, expert="fp8")) == B.MOE_OK
     # group-limited selection: G divides E, G <= 64, 1 <= M <= G, k <= M * E / G; 0 / 0 = none
     g = lambda grp, E=256, k=8: B.validate(B.make_cfg(16, 1024, E, k, 512, score="sigmoid", groups=grp))
     assert g((8, 4)) == B.MOE_OK and g((8, 8)) == B.MOE_OK and g((0, 0)) == B.MOE_OK
@@ -161,13 +161,15 @@ def test_misaligned_index_and_scale_arrays_are_rejected(B):
         setattr(ew, field, 0x20001)
         assert ffn(q, ew) == B.MOE_ERR_INVALID_ARG, field
         assert "2-byte" in B.lib.moe_last_error().decode()
-    f8 = B.make_cfg(16, 256, 8, 2, 256, expert="fp8")
-    for field in ("s_gate", "s_up", "s_down"):
+    f8 = B.make_cfg(16, 256, 8, 2, 256, 1, 256, expert="fp8")
+    for field in ("s_gate", "s_up", "s_down", "shs_gate", "shs_up", "shs_down"):
         ew = B.MoeExperts()
-        ew.w_gate = ew.w_up = ew.w_down = 0x10000
-        ew.s_gate = ew.s_up = ew.s_down = 0x20000
+        ew.w_gate = ew.w_up = ew.w_down = ew.sh_gate = ew.sh_up = ew.sh_down = 0x10000
+        ew.s_gate = ew.s_up = ew.s_down = ew.shs_gate = ew.shs_up = ew.shs_down = 0x20000
         setattr(ew, field, 0x20002)
         assert ffn(f8, ew) == B.MOE_ERR_INVALID_ARG, field
+        setattr(ew, field, 0)
+        assert ffn(f8, ew) == B.MOE_ERR_INVALID_ARG, field  # every FP8 scale pointer is required
 
 
 def test_pack_rejects_bad_arguments_before_launch(B):

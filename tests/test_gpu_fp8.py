@@ -1,6 +1,6 @@
 """GPU tests of FP8 (OCP E4M3) expert weights with per-channel fp32 scales
 ("MoE at the inference level", workarounds: fp8 expert weights halve the bytes),
-on the decode (streaming) kernels.
+on the decode (streaming) and prefill (tiled) kernels, routed and shared experts.
 
 - Parity against the FP64 oracle, which decodes every byte exactly, on
   OLMoE- and Qwen3-shaped layers at decode sizes, in both weight layouts.
@@ -85,11 +85,14 @@ def _codes_layers(layout):
     return sp, lay8, spb, layb
 
 
+@pytest.mark.parametrize("T", [64, 100])
 @pytest.mark.parametrize("layout", ["rows", "tiled"])
-def test_every_fp8_code_decodes_exactly(layout):
+def test_every_fp8_code_decodes_exactly(layout, T):
+    """T = 64 runs the streaming (decode) kernels, T = 100 the tiled (prefill) ones,
+    with non-temporal weight loads."""
     sp, lay8, spb, layb = _codes_layers(layout)
     m8, mb = layer_of(sp, lay8, layout), layer_of(spb, layb, layout)
-    x = S.make_tokens(sp, 64, device="cuda", seed=5)
+    x = S.make_tokens(sp, T, device="cuda", seed=5)
     o8, ob = m8.forward(x), mb.forward(x)
     torch.cuda.synchronize()
     assert torch.equal(o8[1], ob[1])
@@ -105,3 +108,32 @@ def test_every_fp8_code_decodes_exactly(layout):
         nz = ref != 0
         ratio = y[t, nz] / ref[nz]
         assert np.allclose(ratio, ratio[0], rtol=1e-2), t  # y = const * fp8(code) * scale, to bf16 rounding
+
+
+def _sample(T, n, seed=0):
+    return np.arange(T) if T <= n else np.sort(np.random.default_rng(seed).choice(T, n, replace=False))
+
+
+@pytest.mark.parametrize("layout", ["rows", "tiled"])
+@pytest.mark.parametrize("name,T", [("olmoe_fp8", 4096), ("dsv2_lite_fp8", 3000), ("dsv2_lite_fp8", 40),
+                                    ("olmoe_fp8", 300)])
+def test_fp8_prefill_and_shared_experts_match_oracle(name, T, layout):
+    """The tiled FP8 kernels (T > 64: OLMoE-shaped at T = 4096 and 300, the latter with
+    non-temporal weight loads; DeepSeek-V2-Lite-shaped with two FP8 shared experts at
+    T = 3000) and the streaming ones with FP8 shared experts (T = 40), against the
+    oracle on a token sample."""
+    sp = S.SPECS[name]
+    lay = _layer(sp)
+    ml = layer_of(sp, lay, layout)
+    x = S.make_tokens(sp, T, device="cuda", seed=T)
+    out, idx, gates, drop = ml.forward(x)
+    torch.cuda.synchronize()
+    rows = _sample(T, 128)
+    ref = oracle_run(sp, lay, x, ffn_rows=rows)
+    rep = compare_routes(idx.cpu().numpy(), ref, sp.k)
+    assert rep.set_mismatch_strict == 0 and rep.order_mismatch == 0
+    ok = rows[rep.matched[rows]]
+    assert len(ok) >= 0.9 * len(rows)
+    rel = row_rel_err(out.float().cpu().numpy().astype(np.float64)[ok], ref["out"][ok])
+    print(f"  {name} T={T} {layout}: max row rel err {rel.max(initial=0):.2e} over {len(ok)} tokens")
+    assert rel.max(initial=0) <= tol_of(sp)

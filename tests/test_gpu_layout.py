@@ -28,9 +28,10 @@ def tiled_positions(rows: int, R: int) -> np.ndarray:
 
 
 @pytest.mark.parametrize("expert,rows,K", [("bf16", 16, 32), ("bf16", 48, 2048), ("int4", 32, 128),
-                                           ("int4", 16, 768), ("f32", 32, 16), ("f32", 16, 272)])
+                                           ("int4", 16, 768), ("f32", 32, 16), ("f32", 16, 272), ("fp8", 32, 128),
+                                           ("fp8", 16, 1408)])
 def test_pack_is_the_documented_permutation(expert, rows, K):
-    R = {"bf16": 2 * K, "int4": K // 2, "f32": 4 * K}[expert]
+    R = {"bf16": 2 * K, "int4": K // 2, "f32": 4 * K, "fp8": K}[expert]
     g = torch.Generator().manual_seed(rows * 1000 + K)
     src = torch.randint(0, 256, (rows, R), dtype=torch.uint8, generator=g)
     dst = torch.empty_like(src.cuda())
@@ -51,11 +52,13 @@ ODD = S.SPECS["dsv2_lite"].replace(name="odd_d", cfg_id=21, d=640, E=16, k=4, ff
 MID = S.SPECS["olmoe"].replace(name="mid_l", cfg_id=22, d=1024, E=32, k=4, ffn=512)
 INT4S = S.SPECS["qwen3_int4"].replace(name="int4_s", cfg_id=23, E=32)
 DSV3S = S.SPECS["dsv3"].replace(name="dsv3_s", cfg_id=24, E=32)
+ODD8 = ODD.replace(name="odd_d_fp8", cfg_id=25, expert="fp8")   # FP8 routed and shared experts
 
 CASES = [("tiny_f32", None, 64), ("olmoe", None, 1), ("olmoe", None, 8), ("olmoe", None, 64), ("olmoe", None, 4096),
          ("mid", MID, 33), ("mid", MID, 300), ("odd", ODD, 7), ("odd", ODD, 500), ("dsv2_lite", None, 8192),
          ("dsv2_lite_cap", None, 8192), ("qwen3_int4", None, 32), ("qwen3_int4", None, 4096), ("int4_s", INT4S, 200),
-         ("dsv3_s", DSV3S, 16), ("dsv3_s", DSV3S, 100), ("dsv3_s", DSV3S, 1000)]
+         ("dsv3_s", DSV3S, 16), ("dsv3_s", DSV3S, 100), ("dsv3_s", DSV3S, 1000), ("odd8", ODD8, 7),
+         ("odd8", ODD8, 500), ("olmoe_fp8", None, 4096)]
 
 _LAYERS = {}
 
