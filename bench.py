@@ -15,7 +15,8 @@ layer on a seeded 1024-token subset, extrapolated to the workload.  Sub-keys:
 the OLMoE-shaped layer at T=4096 (`olmoe_T4096`), decode sizes as hipGraph
 replays with weights rotated over several copies so the Infinity Cache does
 not serve them (`decode`, `decode_other`, against HBM bandwidth), the other
-prefill layers (`prefill`), and routing near-ties and INT4 drift (`routing`).
+prefill layers (`prefill`), routing near-ties and INT4 drift (`routing`), and the
+memory-system probe rates the kernels are read against (`memory_probe`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-prefill]
 """
@@ -55,6 +56,8 @@ def parse():
     ap.add_argument("--profile-layer", metavar="SPEC",
                     help="run --warmup + --steps eager forwards of the named synthetic layer at --T tokens "
                          "(for counter passes on one layer's kernels), print the mean ms and exit")
+    ap.add_argument("--memory-probe", action="store_true",
+                    help="print the streaming-read and global->LDS probe rates and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device-to-device copy three times (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -86,6 +89,54 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": a.numel() * 4, "copies": 3, "ms_per_copy": round(ms, 3),
                       "read_plus_write_GBps": round(2 * a.numel() * 4 / (ms * 1e-3) / 1e9, 1),
                       "reduction_read_GBps": round(big.numel() * 4 / (ms_r * 1e-3) / 1e9, 1)}))
+
+
+def memory_probe():
+    """Ceilings the kernels are read against, from the probe library (csrc/probe.hip):
+    a streaming read of 4 GiB (ordinary and non-temporal 16-byte loads; the best over
+    grid sizes), and direct global -> LDS loads from an L2-resident 4 MiB span and from
+    a 4 GiB span, as whole KB per wave-wide load or as 64-byte pieces of 16 rows."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "mixture_experts_layer_13_amd", "libmoe_probe.so"))
+    P = ctypes.c_void_p
+    lib.moe_probe_stream_read.argtypes = [P, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, P, P]
+    lib.moe_probe_dma_read.argtypes = [P, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
+    nbytes = 4 << 30
+    buf = torch.full((nbytes // 4,), 1, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = P(torch.cuda.current_stream().cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=3):
+        assert fn() == 0
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            assert fn() == 0
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    res = {}
+    for nt, name in ((0, "stream_read_GBps"), (1, "stream_read_nontemporal_GBps")):
+        best = 0.0
+        for blocks in (1024, 2048, 4096, 8192):
+            t = timed(lambda: lib.moe_probe_stream_read(P(buf.data_ptr()), nbytes, nt, blocks, P(sink.data_ptr()),
+                                                        stream))
+            best = max(best, nbytes / t / 1e9)
+        res[name] = round(best, 1)
+    steps, blocks = 256, 8192
+    moved = blocks * 4 * steps * 8192
+    for span, tag in ((4 << 20, "l2"), (nbytes, "hbm")):
+        for gather in (0, 1):
+            t = timed(lambda: lib.moe_probe_dma_read(P(buf.data_ptr()), span, gather, steps, blocks, stream))
+            res[f"dma_{tag}_{'gather64' if gather else 'contig'}_GBps"] = round(moved / t / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    res["method"] = ("stream: 4 GiB once per launch, 16 loads of 16 B in flight per lane, best of 1024-8192 "
+                     "blocks; dma: 8192 blocks x 4 waves x 256 steps x 8 KB, two steps in flight per wave, "
+                     "from the first 4 MiB (l2) or 4 GiB (hbm) of the buffer")
+    return res
 
 
 class HipEvents:
@@ -541,6 +592,9 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
+    if args.memory_probe:
+        print(json.dumps(memory_probe()), flush=True)
+        return
     if args.profile_layer:
         psp = S.SPECS[args.profile_layer]
         play = S.make_layer(psp, device="cuda")
@@ -615,6 +669,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill:
         line["prefill"] = prefill_sweep(args.layout)
+    line["memory_probe"] = memory_probe()
     print(json.dumps(line), flush=True)
 
 

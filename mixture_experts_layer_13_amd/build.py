@@ -27,17 +27,26 @@ def _run(cmd):
     return msgs
 
 
+PROBE_SOURCE = "csrc/probe.hip"   # memory-system probes of the measurement harness (libmoe_probe.so)
+
+
 def build(verbose: bool = False) -> str:
-    """Compiles every source (in parallel) to objects under _build/ and links libmoe.so."""
+    """Compiles every source (in parallel) to objects under _build/ and links libmoe.so, and the
+    probe library libmoe_probe.so beside it."""
     out = os.path.join(HERE, "libmoe.so")
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.basename(src).replace(".hip", ".o")) for src in SOURCES]
     cmds = [[HIPCC] + FLAGS + ["-c", os.path.join(HERE, src), "-o", obj] for src, obj in zip(SOURCES, objs)]
+    probe_obj = os.path.join(objdir, "probe.o")
+    cmds.append([HIPCC] + FLAGS + ["-c", os.path.join(HERE, PROBE_SOURCE), "-o", probe_obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as pool:
         msgs = list(pool.map(_run, cmds))
     tmp = out + ".tmp"
     msgs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]))
+    probe_out = os.path.join(HERE, "libmoe_probe.so")
+    msgs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", probe_obj, "-o", probe_out + ".tmp"]))
+    os.replace(probe_out + ".tmp", probe_out)
     if verbose and any(m.strip() for m in msgs):
         print("\n".join(m for m in msgs if m.strip()))
     os.replace(tmp, out)

@@ -1,0 +1,96 @@
+// Memory-system probes for the measurement harness (bench.py --probe), built
+// into their own library (libmoe_probe.so), apart from the layer's libmoe.so.
+// They give the ceilings the layer's kernels are read against:
+//  - a streaming read of a large buffer (16-byte loads per lane, ordinary or
+//    non-temporal): the practical HBM read rate;
+//  - direct global -> LDS loads (global_load_lds_dwordx4) from a small,
+//    L2-resident span or a large one, each wave-wide load either one
+//    contiguous KB or 16 rows x 64 bytes (the gather pattern of activation
+//    rows): the L2 -> CU rate and its cost per cache-line request.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+// every block reads `chunks` consecutive 16-byte units per lane, 16 in flight per lane
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, size_t nvec,
+                                                          uint32_t* sink) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 15 * stride < nvec; i += 16 * stride) {
+    u32x4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(&buf[i + u * stride]) : buf[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < nvec; i += stride) acc ^= buf[i][0];
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // never true for the probe's fill; keeps the loads
+}
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(g), "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds))
+      : "memory");
+}
+
+// each wave issues 8 loads per step into its own 8 KB of LDS, two steps in flight;
+// GATHER: lanes 4 q .. 4 q + 3 read 64 contiguous bytes of row q of 16 rows 14336 bytes apart
+template <bool GATHER>
+__global__ __launch_bounds__(256) void dma_read_kernel(const char* __restrict__ buf, uint64_t mask, int steps) {
+  __shared__ __attribute__((aligned(1024))) char smem[32768];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  uint64_t off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint64_t wid = (uint64_t)blockIdx.x * 4 + w;
+    off[i] = GATHER ? (wid * 7919 + i * 131 + (lane >> 2)) * 14336 + (lane & 3) * 16 : (wid * 8 + i) * 1024 * 97 + lane * 16;
+  }
+  for (int s = 0; s < steps; ++s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(buf + ((off[i] + (uint64_t)s * 64) & mask), lds0 + (uint32_t)(w * 8 + i) * 1024);
+    __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8));  // vmcnt(16)
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+}
+
+}  // namespace
+
+extern "C" {
+
+// Streams `bytes` (a multiple of 16) from `buf` once with `blocks` blocks of 256 threads.
+int moe_probe_stream_read(const void* buf, uint64_t bytes, int nontemporal, int blocks, uint32_t* sink,
+                          void* stream) {
+  if (!buf || !sink || bytes % 16 || blocks <= 0) return -1;
+  hipStream_t s = (hipStream_t)stream;
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3(blocks), dim3(256), 0, s, (const u32x4*)buf, bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3(blocks), dim3(256), 0, s, (const u32x4*)buf, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Direct-to-LDS reads from the first `span` bytes of `buf` (a power of two >= 1 MiB): `blocks`
+// blocks of 4 waves, `steps` steps of 8 KB per wave.  Bytes moved: blocks * 4 * steps * 8192.
+int moe_probe_dma_read(const void* buf, uint64_t span, int gather, int steps, int blocks, void* stream) {
+  if (!buf || span < (1u << 20) || (span & (span - 1)) || steps <= 0 || blocks <= 0) return -1;
+  hipStream_t s = (hipStream_t)stream;
+  if (gather) hipLaunchKernelGGL(dma_read_kernel<true>, dim3(blocks), dim3(256), 0, s, (const char*)buf, span - 1, steps);
+  else hipLaunchKernelGGL(dma_read_kernel<false>, dim3(blocks), dim3(256), 0, s, (const char*)buf, span - 1, steps);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"

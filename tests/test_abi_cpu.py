@@ -208,3 +208,22 @@ def test_noalloc_forward_rejects_oversized_cfg_before_device_access(B):
     # the decode-sized layers fit: DeepSeek-V3-shaped at T = 256, OLMoE-shaped at T = 64
     assert B.workspace_bytes(B.make_cfg(256, 7168, 256, 8, 2048, 1, 2048)) <= 64 << 20
     assert B.workspace_bytes(B.make_cfg(64, 2048, 64, 8, 1024)) <= 64 << 20
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The measurement probes (libmoe_probe.so) load without a GPU and refuse bad
+    arguments before any launch."""
+    path = os.path.join(ROOT, "mixture_experts_layer_13_amd", "libmoe_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libmoe_probe.so not built")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.moe_probe_stream_read.argtypes = [P, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, P, P]
+    lib.moe_probe_dma_read.argtypes = [P, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
+    fake = P(0x10000)
+    assert lib.moe_probe_stream_read(None, 1 << 20, 0, 64, fake, None) == -1
+    assert lib.moe_probe_stream_read(fake, (1 << 20) + 8, 0, 64, fake, None) == -1  # not a multiple of 16
+    assert lib.moe_probe_stream_read(fake, 1 << 20, 0, 0, fake, None) == -1
+    assert lib.moe_probe_dma_read(fake, (1 << 20) + (1 << 12), 0, 4, 64, None) == -1  # span not a power of two
+    assert lib.moe_probe_dma_read(fake, 1 << 19, 0, 4, 64, None) == -1  # span below 1 MiB
+    assert lib.moe_probe_dma_read(fake, 1 << 20, 1, 0, 64, None) == -1
