@@ -95,7 +95,9 @@ def memory_probe():
     """Ceilings the kernels are read against, from the probe library (csrc/probe.hip):
     a streaming read of 4 GiB (ordinary and non-temporal 16-byte loads; the best over
     grid sizes), and direct global -> LDS loads from an L2-resident 4 MiB span and from
-    a 4 GiB span, as whole KB per wave-wide load or as 64-byte pieces of 16 rows."""
+    a 4 GiB span, as a stream of whole KB per wave-wide load or as 64-byte pieces of 16
+    rows walking along the rows (each 128-byte line read in two halves, so the second
+    half of every line comes from cache even over the 4 GiB span)."""
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "mixture_experts_layer_13_amd", "libmoe_probe.so"))
     P = ctypes.c_void_p
@@ -135,7 +137,8 @@ def memory_probe():
     torch.cuda.empty_cache()
     res["method"] = ("stream: 4 GiB once per launch, 16 loads of 16 B in flight per lane, best of 1024-8192 "
                      "blocks; dma: 8192 blocks x 4 waves x 256 steps x 8 KB, two steps in flight per wave, "
-                     "from the first 4 MiB (l2) or 4 GiB (hbm) of the buffer")
+                     "wrapping over the first 4 MiB (l2) or 4 GiB (hbm) of the buffer; contig = consecutive KBs, "
+                     "gather64 = 16 rows x 64 B per load, the next 64 B of the same rows at the next step")
     return res
 
 
@@ -574,8 +577,10 @@ def main():
     args = parse()
     if args.traffic_record:
         spec, T = TRAFFIC_WORKLOADS[args.traffic_workload]
-        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d <out> -o pmc -- python3 bench.py {a}"
-                for a in (f"--profile-layer {spec} --T {T} --steps 3 --warmup 1", "--copy-probe")
+        cmds = [f"rocprofv3 --pmc {c} --kernel-include-regex {rx} --output-format csv -d <out> -o pmc -- "
+                f"python3 bench.py {a}"
+                for rx, a in (("ffn_tiled", f"--profile-layer {spec} --T {T} --steps 3 --warmup 1"),
+                              ("copyBuffer", "--copy-probe"))
                 for c in ("FETCH_SIZE", "WRITE_SIZE")]
         write_traffic_record(args.traffic_workload, *args.traffic_record, commands=cmds)
         return

@@ -5,8 +5,8 @@
 //    non-temporal): the practical HBM read rate;
 //  - direct global -> LDS loads (global_load_lds_dwordx4) from a small,
 //    L2-resident span or a large one, each wave-wide load either one
-//    contiguous KB or 16 rows x 64 bytes (the gather pattern of activation
-//    rows): the L2 -> CU rate and its cost per cache-line request.
+//    contiguous KB (a stream) or 16 rows x 64 bytes (the gather pattern of
+//    activation rows): the L2 -> CU rate and its cost per cache-line request.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,22 +46,29 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
       : "memory");
 }
 
-// each wave issues 8 loads per step into its own 8 KB of LDS, two steps in flight;
-// GATHER: lanes 4 q .. 4 q + 3 read 64 contiguous bytes of row q of 16 rows 14336 bytes apart
+// each wave issues 8 loads per step into its own 8 KB of LDS, two steps in flight.
+// Contiguous: the wave streams through consecutive KBs (8 new KB per step).
+// GATHER: lanes 4 q .. 4 q + 3 read 64 contiguous bytes of row q of 16 rows 14336
+// bytes apart, the next 64 bytes of the same rows at the next step (the K walk of
+// a gathered activation tile: every 128-byte line is read in two halves).
+// Offsets wrap at the span (mask = span - 1, a power of two; every offset is a
+// multiple of 16, so each 16-byte load stays inside the span).
 template <bool GATHER>
 __global__ __launch_bounds__(256) void dma_read_kernel(const char* __restrict__ buf, uint64_t mask, int steps) {
   __shared__ __attribute__((aligned(1024))) char smem[32768];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint64_t wid = (uint64_t)blockIdx.x * 4 + w;
   uint64_t off[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint64_t wid = (uint64_t)blockIdx.x * 4 + w;
-    off[i] = GATHER ? (wid * 7919 + i * 131 + (lane >> 2)) * 14336 + (lane & 3) * 16 : (wid * 8 + i) * 1024 * 97 + lane * 16;
-  }
+  for (int i = 0; i < 8; ++i)
+    off[i] = GATHER ? (wid * 7919 + i * 131 + (lane >> 2)) * 14336 + (lane & 3) * 16
+                    : (wid * (uint64_t)steps * 8 + i) * 1024 + lane * 16;
+  const uint64_t step_bytes = GATHER ? 64 : 8192;
   for (int s = 0; s < steps; ++s) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(buf + ((off[i] + (uint64_t)s * 64) & mask), lds0 + (uint32_t)(w * 8 + i) * 1024);
+    for (int i = 0; i < 8; ++i)
+      dma16(buf + ((off[i] + (uint64_t)s * step_bytes) & mask), lds0 + (uint32_t)(w * 8 + i) * 1024);
     __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8));  // vmcnt(16)
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
