@@ -1,6 +1,6 @@
 """Builds libmoe.so in-tree with hipcc for gfx950.
 
-Usage: python mixture_experts_layer_13_amd/build.py
+Usage: python mixture_experts_layer_13_amd/build.py [--host-sanitized]
 """
 import os
 import subprocess
@@ -53,6 +53,33 @@ def build(verbose: bool = False) -> str:
     return out
 
 
+HOST_SANITIZERS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def build_host_sanitized() -> str:
+    """A second build of the library whose host code of the C ABI (csrc/api.hip: argument checks,
+    planning, workspace carving, launch sequencing) carries AddressSanitizer and UBSan; the device
+    code and the kernel launchers are the objects of the normal build (run build() first).  Load
+    it with the ASan runtime preloaded (tests/test_host_sanitizers.py does)."""
+    objdir = os.path.join(HERE, "_build")
+    others = [os.path.join(objdir, os.path.basename(src).replace(".hip", ".o")) for src in SOURCES[1:]]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError(f"build() first: {missing[0]} is missing")
+    sandir = os.path.join(objdir, "hostsan")
+    os.makedirs(sandir, exist_ok=True)
+    api_obj = os.path.join(sandir, "api.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"]
+    _run([HIPCC] + flags + HOST_SANITIZERS + ["-c", os.path.join(HERE, SOURCES[0]), "-o", api_obj])
+    out = os.path.join(sandir, "libmoe_hostsan.so")
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + HOST_SANITIZERS[:4] + [api_obj] + others +
+         ["-o", out])
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized())
     sys.exit(0)
