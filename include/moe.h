@@ -200,8 +200,9 @@ moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* sl
  * gate/up SwiGLU GEMM, down GEMM, combine.  "MoE: dynamism the compiler
  * cannot remove", batch-1 recipe and its graph-capture answer: fixed shapes,
  * no host logic and no allocation between launches, so the five launches
- * capture into one HIP graph per token count; the launch-bound study (picx.dev
- * summary) is why they are five and not one per expert.
+ * (four for a small single token, moe_forward_launches) capture into one HIP
+ * graph per token count; the launch-bound study (picx.dev summary) is why they
+ * are five and not one per expert.
  *   x [T][d], w_router [E][d] act dtype; logit_bias, select_bias as in
  *   moe_route; w: expert weights.  Outputs out [T][d] act dtype, topk_idx
  *   [T][k] int32, topk_w [T][k] fp32, drop_mask [T][k] uint8.  ws: workspace of
@@ -263,7 +264,10 @@ moe_status moe_forward_with_routes(const moe_cfg* cfg, const void* x, const int3
  *   load time; scales are not packed.  Async on `stream`. */
 moe_status moe_pack_weights(int32_t dtype, const void* src, void* dst, int64_t rows, int32_t K, void* stream);
 
-/* Kernel launches moe_forward enqueues for this cfg (0 on an invalid cfg). */
+/* Kernel launches moe_forward enqueues for this cfg (0 on an invalid cfg): 5
+ * (router, route / permutation, gate/up, down, combine), or 4 for a single
+ * token whose k routed plus shared down matrices hold at most 24 MiB (the
+ * down projection and the combine are then one launch). */
 int32_t moe_forward_launches(const moe_cfg* cfg);
 
 /* Measurement hook for per-kernel timing with HIP events.  When `events` is

@@ -238,6 +238,44 @@ moe_status hip_ok(hipError_t e, const char* what) {
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// A single token whose down weights (k routed experts plus the shared ones) are small: the
+// down projection and the combine run as one launch (down_combine_one_kernel), so a forward
+// is four launches.  That launch has only d / (16 NT) blocks, one per channel tile, so it
+// cannot pull large weights at full rate; measured (graph replays, one box): Qwen3 INT4-shaped
+// T=1 (6.3 MB of down weights) 37.4 -> 35.1 us and OLMoE-shaped FP8 T=1 (16.8 MB) 35.8 -> 33.2
+// us, but bf16 OLMoE-shaped T=1 (33.5 MB) 41.8 -> 46.0 us and DeepSeek-V3-shaped (293 MB)
+// 153 -> 173 us; hence the limit of 24 MiB.
+constexpr int64_t kFusedDownMaxBytes = (int64_t)24 << 20;
+bool one_token(const Plan& p) {
+  if (p.T != 1 || p.mode != 0) return false;
+  auto bytes = [&](int64_t n) {  // n weights of the expert dtype
+    return p.wdt == MOE_INT4_G128 ? n / 2 : p.wdt == MOE_FP8_E4M3 ? n : p.wdt == MOE_F32 ? 4 * n : 2 * n;
+  };
+  const int64_t down = bytes((int64_t)p.k * p.d * p.F) + bytes((int64_t)p.S * p.d * p.FS);
+  return down <= kFusedDownMaxBytes;
+}
+
+// the expert GEMMs and the combine of moe_forward / moe_forward_with_routes
+// (timing marks 3.. for moe_forward only: `timed`)
+moe_status enqueue_experts_and_combine(const Plan& p, const FfnArgs& a, const int32_t* topk_idx,
+                                       const int32_t* slot, const float* topk_w, const void* ysh, void* out,
+                                       hipStream_t s, bool timed) {
+  const int nl = timed ? (one_token(p) ? 4 : 5) : 1 << 30;  // an impossible count records nothing
+  moe_status st;
+  if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
+  mark(3, nl, s);
+  if (one_token(p)) {
+    st = hip_ok(launch_down_combine_one(p.wdt, a, topk_idx, slot, topk_w, out, p.k, s), "down GEMM + combine");
+    mark(4, nl, s);
+    return st;
+  }
+  if ((st = hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM"))) return st;
+  mark(4, nl, s);
+  st = hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
+  mark(5, nl, s);
+  return st;
+}
+
 RouteArgs route_args(const Plan& p, const float* lb, const float* sb, int32_t* idx, float* gates, float* scores) {
   RouteArgs r;
   r.T = p.T;
@@ -414,7 +452,7 @@ size_t moe_workspace_bytes(const moe_cfg* cfg) {
 int32_t moe_forward_launches(const moe_cfg* cfg) {
   Plan p;
   if (make_plan(cfg, &p) != MOE_OK || p.T == 0) return 0;
-  return 5;
+  return one_token(p) ? 4 : 5;
 }
 
 moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, const float* logit_bias,
@@ -514,7 +552,7 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   int32_t* rowtok = at<int32_t>(ws, p.o_rowtok);
   RouteArgs ra = route_args(p, logit_bias, select_bias, topk_idx, topk_w, nullptr);
   PermArgs pa = perm_args(p, ws, at<int32_t>(ws, p.o_counts), at<int32_t>(ws, p.o_off), rowtok, slot, drop_mask);
-  const int nl = 5;
+  const int nl = one_token(p) ? 4 : 5;
   mark(0, nl, s);
   if (p.single) {
     float* part = at<float>(ws, p.o_part);
@@ -533,13 +571,7 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   mark(2, nl, s);
   void* ysh = p.S ? at<void>(ws, p.o_ysh) : nullptr;
   FfnArgs a = ffn_args(p, ws, x, rowtok, w, at<void>(ws, p.o_y), ysh);
-  if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
-  mark(3, nl, s);
-  if ((st = hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM"))) return st;
-  mark(4, nl, s);
-  st = hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
-  mark(5, nl, s);
-  return st;
+  return enqueue_experts_and_combine(p, a, topk_idx, slot, topk_w, ysh, out, s, true);
 }
 
 moe_status moe_forward_noalloc(const moe_cfg* cfg, const void* x, const void* w_router, const float* logit_bias,
@@ -590,9 +622,7 @@ moe_status moe_forward_with_routes(const moe_cfg* cfg, const void* x, const int3
   }
   void* ysh = p.S ? at<void>(ws, p.o_ysh) : nullptr;
   FfnArgs a = ffn_args(p, ws, x, rowtok, w, at<void>(ws, p.o_y), ysh);
-  if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
-  if ((st = hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM"))) return st;
-  return hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
+  return enqueue_experts_and_combine(p, a, topk_idx, slot, topk_w, ysh, out, s, false);
 }
 
 moe_status moe_pack_weights(int32_t dtype, const void* src, void* dst, int64_t rows, int32_t K, void* stream) {

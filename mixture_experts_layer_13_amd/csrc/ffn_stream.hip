@@ -338,6 +338,115 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ one token: down + combine
+// For a single token (T = 1) the down projection and the weighted combine are one launch:
+// block b covers output channels 16 NT b .. +16 NT - 1; wave j < k runs pick j's h row
+// through its expert's down rows (what one wave of the down kernel above computes for
+// those channels: the same steps in the same K order, so the same fp32 sums) and wave k,
+// when there are shared experts, the shared slab (all S segments in order).  Each wave
+// rounds its row to the activation type, as the down kernel's store does; wave 0 then adds
+// the rows as the combine kernel does: fp32, gate-weighted fma in pick order, picks without
+// a row (dropped) skipped, the shared row added last.  No y rows, no combine launch.
+template <typename TW>
+__global__ __launch_bounds__(1024) void down_combine_one_kernel(FfnArgs a, const int32_t* __restrict__ topk_idx,
+                                                                const int32_t* __restrict__ slot_row,
+                                                                const float* __restrict__ gw, void* __restrict__ out,
+                                                                int k) {
+  using D = Dec<TW>;
+  using TA = typename D::TA;
+  constexpr int NT = stream_tiles<TW>();
+  constexpr int CPW = 16 * NT;  // channels per block (one wave's channel tiles)
+  constexpr int U = std::is_same<TW, INT4>::value ? 2 : (std::is_same<TW, FP8>::value ? 4 : 16);
+  constexpr int AL = D::AL, KSTEP = D::KSTEP;
+  __shared__ float ys[kMaxK + 1][CPW];
+  __shared__ int has[kMaxK + 1];
+  const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  const bool sh = w == k;  // the shared experts' wave (launched only when S > 0)
+  const int r = sh ? 0 : slot_row[w];
+  const bool ok = sh || (unsigned)r < (unsigned)a.R;
+  if (ok) {
+    const int e = sh ? 0 : min(max(topk_idx[w], 0), a.E - 1);
+    const int K = sh ? a.FS : a.F, nseg = sh ? a.S : 1;
+    const TA* arow = sh ? (const TA*)a.hsh : (const TA*)a.h + (size_t)r * a.F;
+    const int n0 = blockIdx.x * CPW + c;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int seg = 0; seg < nseg; ++seg) {
+      const void* m = sh ? expert_mat<TW>(a.shd, seg, a.d, K) : expert_mat<TW>(a.wd, e, a.d, K);
+      const void* sc0 = sh ? expert_scales_of<TW>(a.shsd, seg, a.d, K) : expert_scales_of<TW>(a.sd, e, a.d, K);
+      BRow<TW> b[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) b[j] = BRow<TW>(m, n0 + 16 * j, K, g, sc0, a.wtiled);
+      const int aoff = seg * K, nsteps = K / KSTEP;
+#pragma unroll 1
+      for (int st = 0; st < nsteps; st += U) {
+        u32x4 bq[NT][U];
+        float sc[NT][U];
+        u32x4 av[U][AL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (st + u < nsteps) {
+            const int kb = (st + u) * KSTEP;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              bq[j][u] = b[j].load(kb);
+              sc[j][u] = b[j].scale(kb);
+            }
+#pragma unroll
+            for (int q = 0; q < AL; ++q) av[u][q] = ld16(arow + aoff + kb + (KSTEP / 4) * g + 8 * q);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (st + u < nsteps) {
+            if constexpr (std::is_same<TW, INT4>::value) {
+              const f32x4 xn = int4_group_offset(av[u]);
+#pragma unroll
+              for (int j = 0; j < NT; ++j) acc[j] = dstep_int4(av[u], bq[j][u], sc[j][u], xn, acc[j]);
+            } else if constexpr (std::is_same<TW, FP8>::value) {
+#pragma unroll
+              for (int j = 0; j < NT; ++j) acc[j] = dstep_fp8(av[u], bq[j][u], sc[j][u], acc[j]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < NT; ++j) acc[j] = dstep<TW>(av[u], bq[j][u], sc[j][u], acc[j]);
+            }
+          }
+        }
+      }
+    }
+    // row 0 of the MFMA output (every A row is the token's row): lanes 0..15, element 0
+    if (g == 0) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) ys[w][16 * j + c] = (float)from_f32<TA>(acc[j][0]);
+    }
+  }
+  if (lane == 0) has[w] = ok;
+  __syncthreads();
+  if (w == 0 && lane < CPW) {
+    float o = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (has[j]) o = fmaf(gw[j], ys[j][lane], o);
+    if (a.S > 0) o += ys[k][lane];
+    ((TA*)out)[blockIdx.x * CPW + lane] = from_f32<TA>(o);
+  }
+}
+
+hipError_t launch_down_combine_one(int wdt, const FfnArgs& a, const int32_t* topk_idx, const int32_t* slot_row,
+                                   const float* gw, void* out, int k, hipStream_t s) {
+  const int cpw = stream_channels_per_block(false, wdt) / 4;  // one wave's channels
+  const dim3 grid(a.d / cpw), block(64 * (k + (a.S > 0 ? 1 : 0)));
+  if (wdt == kF32)
+    hipLaunchKernelGGL(down_combine_one_kernel<float>, grid, block, 0, s, a, topk_idx, slot_row, gw, out, k);
+  else if (wdt == kBF16)
+    hipLaunchKernelGGL(down_combine_one_kernel<bf16>, grid, block, 0, s, a, topk_idx, slot_row, gw, out, k);
+  else if (wdt == kFP8)
+    hipLaunchKernelGGL(down_combine_one_kernel<FP8>, grid, block, 0, s, a, topk_idx, slot_row, gw, out, k);
+  else
+    hipLaunchKernelGGL(down_combine_one_kernel<INT4>, grid, block, 0, s, a, topk_idx, slot_row, gw, out, k);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ launch
 template <bool GATEUP, int MT>
 static void launch_stream(int wdt, const FfnArgs& a, int grid, hipStream_t s) {

@@ -103,12 +103,16 @@ def test_forward_matches_oracle(name, T):
     assert rel.max(initial=0) <= tol_of(sp)
 
 
-@pytest.mark.parametrize("name,T", [("tiny_f32", 64), ("olmoe", 1), ("olmoe", 8), ("olmoe", 300), ("olmoe", 20000),
-                                    ("dsv2_lite_cap", 8192),
-                                    ("qwen3_int4", 1), ("qwen3_int4", 32), ("dsv3", 1)])
+@pytest.mark.parametrize("name,T", [("tiny_f32", 64), ("tiny_f32", 1), ("olmoe", 1), ("olmoe", 8), ("olmoe", 300),
+                                    ("olmoe", 20000), ("dsv2_lite_cap", 8192), ("dsv2_lite", 1), ("dsv2_lite_cap", 1),
+                                    ("olmoe_fp8", 1), ("dsv2_lite_fp8", 1), ("qwen3_int4", 1), ("qwen3_int4", 32),
+                                    ("dsv3", 1)])
 def test_split_path_reproduces_forward_bitwise(name, T):
     """Replaying the layer's own routes through route -> permute -> expert_ffn ->
-    combine returns the fused forward's output exactly (the route-replay control)."""
+    combine returns the fused forward's output exactly (the route-replay control).
+    A single token with small down weights (here tiny_f32, the FP8 and INT4 layers,
+    routed and shared experts) runs the down projection and the combine as one
+    launch: still the same bits."""
     sp, lay, ml = get_layer(name)
     x = S.make_tokens(sp, T, device="cuda")
     out, idx, gates, drop = ml.forward(x)
