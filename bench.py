@@ -501,7 +501,11 @@ def prefill_point(sp, ml, x, steps, warmup):
     ms, per, outs, nl, wall = time_layer(ml, x, steps, warmup)
     T = x.shape[0]
     w = alg_work(sp, T, outs[1], outs[3])
+    ai = w["flops"] / w["bytes"]  # flops per algorithmic byte; the ridge is 2.5 PFLOP/s / 8 TB/s = 312.5
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "bound": "mfma" if ai >= BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm",
+            "flops_per_byte": round(ai, 1),
+            "hbm_frac_layer": round(w["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac_layer": round(w["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "mfma_frac_gateup": round(w["gateup_flops"] / (per["gateup"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "per_launch_us": {n: round(v * 1e3, 2) for n, v in per.items()},
