@@ -3,6 +3,7 @@
 // synchronisation, no device reads on the host.
 #include <math.h>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -40,10 +41,19 @@ constexpr int64_t kMaxT = 1 << 20;
 // Experts must average this many rows for the 256-row tiled kernels (ffn_tiled256.hip).  Off by
 // default: measured on the DeepSeek-V3-shaped layer at T=16384 they move half the operand bytes per
 // flop and lift the L2 hit rate from 44% to 74%, but gate/up only went 9.52 -> 9.35 ms and down
-// 4.64 -> 5.29 ms (OLMoE T=4096 gate/up 361 -> 394 us), so the 128-row kernels stay.
+// 4.64 -> 5.29 ms (OLMoE T=4096 gate/up 361 -> 394 us), so the 128-row kernels stay.  The
+// environment variable of the same name, read at every plan, overrides the default (a positive
+// integer; it is how the GPU tests run the 256-row kernels against the 128-row ones).
 #ifndef MOE_ROWS256_MIN_AVG
 #define MOE_ROWS256_MIN_AVG (1 << 30)
 #endif
+int64_t rows256_min_avg() {
+  const char* v = getenv("MOE_ROWS256_MIN_AVG");
+  if (!v || !*v) return MOE_ROWS256_MIN_AVG;
+  char* end = nullptr;
+  const long long n = strtoll(v, &end, 10);
+  return (end && *end == 0 && n > 0) ? (int64_t)(n < (1 << 30) ? n : (1 << 30)) : (int64_t)MOE_ROWS256_MIN_AVG;
+}
 
 struct Plan {
   int T, d, E, k, F, S, FS, act, wdt, score, renorm, tiled;
@@ -169,7 +179,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   // tiled bf16 kernels take 256-row items when experts average at least MOE_ROWS256_MIN_AVG rows
   // (half the operand bytes per flop of 128-row items, one wave per SIMD); below that the extra
   // idle rows of each expert's last item and the coarser tail cost more
-  const bool rows256 = q.wdt == MOE_BF16 && (int64_t)q.T * q.k >= (int64_t)MOE_ROWS256_MIN_AVG * q.E;
+  const bool rows256 = q.wdt == MOE_BF16 && q.mode == 1 && (int64_t)q.T * q.k >= rows256_min_avg() * q.E;
   q.bm = q.mode == 1 ? (rows256 ? 2 * kPrefillRows : kPrefillRows)
                      : ((q.T <= 16 || (int64_t)q.T * q.k <= 8 * (int64_t)q.E) ? 16 : 32);
   // tiled mode with at most 32 rows per expert on average: an expert's weights are read by one

@@ -234,3 +234,26 @@ def test_side_stream_forward_after_default_stream_churn():
     for u, v in zip(ref, outs):
         assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
                            v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
+
+
+@pytest.mark.parametrize("name,T", [("olmoe", 4096), ("dsv2_lite_cap", 8192), ("dsv3", 4096)])
+def test_256_row_kernels_match_the_128_row_kernels_bitwise(name, T, monkeypatch):
+    """The 256-row tiled kernels (direct global -> LDS loads, off by default) sum every
+    output in the same K order as the 128-row kernels: with MOE_ROWS256_MIN_AVG=1 the
+    plan takes them for every bf16 prefill layer, and the forward must not change by a
+    bit (dropless and capacity modes, shared experts, partly filled 256-row items)."""
+    from mixture_experts_layer_13_amd import binding as B
+    sp, lay, ml = get_layer(name)
+    x = S.make_tokens(sp, T, device="cuda")
+    ref = [t.clone() for t in ml.forward(x)]
+    torch.cuda.synchronize()
+    c = ml.cfg_for(T)
+    ws128 = B.workspace_bytes(c)
+    monkeypatch.setenv("MOE_ROWS256_MIN_AVG", "1")
+    assert B.workspace_bytes(c) != ws128  # the plan now holds 256-row items
+    out = ml.forward(x)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("MOE_ROWS256_MIN_AVG")
+    for u, v in zip(ref, out):
+        assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), name
