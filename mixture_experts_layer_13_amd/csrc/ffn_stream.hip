@@ -35,8 +35,8 @@ template <> struct Dec<FP8> {
 //    row 16*(n/16) + c, bytes 16g.. of the chunk, so one wave-wide 16-byte load
 //    of a fragment reads 1 KB of consecutive addresses.
 // Weight bytes are read exactly once per forward: non-temporal 16-byte loads
-// (measured on a plain 2 GiB read: 6.9-7.0 TB/s against 6.1-6.2 TB/s with
-// ordinary loads).
+// (a plain streaming read of 4 GiB, csrc/probe.hip: 6.5-7.0 TB/s against
+// 5.8-6.2 TB/s with ordinary loads, box to box).
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }

@@ -1,4 +1,4 @@
-// Memory-system probes for the measurement harness (bench.py --probe), built
+// Memory-system probes for the measurement harness (bench.py --memory-probe), built
 // into their own library (libmoe_probe.so), apart from the layer's libmoe.so.
 // They give the ceilings the layer's kernels are read against:
 //  - a streaming read of a large buffer (16-byte loads per lane, ordinary or
