@@ -200,7 +200,7 @@ moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* sl
  * gate/up SwiGLU GEMM, down GEMM, combine.  "MoE: dynamism the compiler
  * cannot remove", batch-1 recipe and its graph-capture answer: fixed shapes,
  * no host logic and no allocation between launches, so the five launches
- * (four for a small single token, moe_forward_launches) capture into one HIP
+ * (four for a single token, moe_forward_launches) capture into one HIP
  * graph per token count; the launch-bound study (picx.dev summary) is why they
  * are five and not one per expert.
  *   x [T][d], w_router [E][d] act dtype; logit_bias, select_bias as in
@@ -266,8 +266,7 @@ moe_status moe_pack_weights(int32_t dtype, const void* src, void* dst, int64_t r
 
 /* Kernel launches moe_forward enqueues for this cfg (0 on an invalid cfg): 5
  * (router, route / permutation, gate/up, down, combine), or 4 for a single
- * token whose k routed plus shared down matrices hold at most 24 MiB (the
- * down projection and the combine are then one launch). */
+ * token (T = 1: the down projection and the combine are one launch). */
 int32_t moe_forward_launches(const moe_cfg* cfg);
 
 /* Measurement hook for per-kernel timing with HIP events.  When `events` is

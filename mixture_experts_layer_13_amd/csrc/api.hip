@@ -248,22 +248,12 @@ moe_status hip_ok(hipError_t e, const char* what) {
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// A single token whose down weights (k routed experts plus the shared ones) are small: the
-// down projection and the combine run as one launch (down_combine_one_kernel), so a forward
-// is four launches.  That launch has only d / (16 NT) blocks, one per channel tile, so it
-// cannot pull large weights at full rate; measured (graph replays, one box): Qwen3 INT4-shaped
-// T=1 (6.3 MB of down weights) 37.4 -> 35.1 us and OLMoE-shaped FP8 T=1 (16.8 MB) 35.8 -> 33.2
-// us, but bf16 OLMoE-shaped T=1 (33.5 MB) 41.8 -> 46.0 us and DeepSeek-V3-shaped (293 MB)
-// 153 -> 173 us; hence the limit of 24 MiB.
-constexpr int64_t kFusedDownMaxBytes = (int64_t)24 << 20;
-bool one_token(const Plan& p) {
-  if (p.T != 1 || p.mode != 0) return false;
-  auto bytes = [&](int64_t n) {  // n weights of the expert dtype
-    return p.wdt == MOE_INT4_G128 ? n / 2 : p.wdt == MOE_FP8_E4M3 ? n : p.wdt == MOE_F32 ? 4 * n : 2 * n;
-  };
-  const int64_t down = bytes((int64_t)p.k * p.d * p.F) + bytes((int64_t)p.S * p.d * p.FS);
-  return down <= kFusedDownMaxBytes;
-}
+// A single token: the down projection and the combine run as one launch
+// (down_combine_one_kernel), so a forward is four launches.  Measured (graph replays, one box):
+// Qwen3 INT4-shaped T=1 37.4 -> 34.8 us, OLMoE-shaped FP8 T=1 35.9 -> 33.0 us, bf16 OLMoE-shaped
+// T=1 41.8 -> 40.3 us, DeepSeek-V2-Lite-shaped T=1 51.9 -> 50.3 us, DeepSeek-V3-shaped T=1
+// 154.2 -> 150.4 us (means of two rounds).
+bool one_token(const Plan& p) { return p.T == 1 && p.mode == 0; }
 
 // the expert GEMMs and the combine of moe_forward / moe_forward_with_routes
 // (timing marks 3.. for moe_forward only: `timed`)

@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
 // the rows as the combine kernel does: fp32, gate-weighted fma in pick order, picks without
 // a row (dropped) skipped, the shared row added last.  No y rows, no combine launch.
 template <typename TW>
-__global__ __launch_bounds__(1024) void down_combine_one_kernel(FfnArgs a, const int32_t* __restrict__ topk_idx,
+__global__ __launch_bounds__(64 * (kMaxK + 1)) void down_combine_one_kernel(FfnArgs a, const int32_t* __restrict__ topk_idx,
                                                                 const int32_t* __restrict__ slot_row,
                                                                 const float* __restrict__ gw, void* __restrict__ out,
                                                                 int k) {
@@ -356,7 +356,11 @@ __global__ __launch_bounds__(1024) void down_combine_one_kernel(FfnArgs a, const
   using TA = typename D::TA;
   constexpr int NT = stream_tiles<TW>();
   constexpr int CPW = 16 * NT;  // channels per block (one wave's channel tiles)
-  constexpr int U = std::is_same<TW, INT4>::value ? 2 : (std::is_same<TW, FP8>::value ? 4 : 16);
+  // steps whose loads go out together; measured for this launch (graph replays, one box): bf16
+  // 16 / 8 / 4 took OLMoE-shaped T=1 to 45.8 / 40.5 / 39.5 us and DeepSeek-V3-shaped T=1 to
+  // 174 / 151.7 / 151.1 us (five launches: 41.4 and 153.8), DeepSeek-V2-Lite-shaped T=1 to
+  // 56.1 / 50.5 / 53.1 us (five launches: 52.3)
+  constexpr int U = std::is_same<TW, INT4>::value ? 2 : (std::is_same<TW, FP8>::value ? 4 : 8);
   constexpr int AL = D::AL, KSTEP = D::KSTEP;
   __shared__ float ys[kMaxK + 1][CPW];
   __shared__ int has[kMaxK + 1];

@@ -230,18 +230,14 @@ def test_probe_library_exports_and_rejects_bad_arguments():
 
 
 def test_forward_launch_count_rule(B):
-    """Five launches, or four for a single token whose k routed plus shared down
-    matrices hold at most 24 MiB (down projection and combine in one launch)."""
-    # OLMoE-shaped bf16: 8 x 2048 x 1024 x 2 B = 32 MiB of down weights -> five launches
-    assert B.forward_launches(B.make_cfg(1, 2048, 64, 8, 1024)) == 5
-    # the same with FP8 experts: 16 MiB -> four; with INT4 (Qwen3-shaped): 6 MiB -> four
-    assert B.forward_launches(B.make_cfg(1, 2048, 64, 8, 1024, expert="fp8")) == 4
-    assert B.forward_launches(B.make_cfg(1, 2048, 128, 8, 768, expert="int4")) == 4
-    # shared experts count: FP8 DeepSeek-V2-Lite-shaped (6 routed + 2 shared of 2048 x 1408) fits
-    assert B.forward_launches(B.make_cfg(1, 2048, 64, 6, 1408, 2, 1408, expert="fp8")) == 4
-    # exactly at the limit: k d F = 12 Mi bf16 weights = 24 MiB -> four; a shared expert more -> five
-    assert B.forward_launches(B.make_cfg(1, 3072, 64, 4, 1024)) == 4
-    assert B.forward_launches(B.make_cfg(1, 3072, 64, 4, 1024, 1, 128)) == 5
-    # more than one token: always five; no tokens: none
+    """Five launches, or four for a single token (down projection and combine in one
+    launch), whatever the weight type, shared experts or size."""
+    for cfg in (B.make_cfg(1, 2048, 64, 8, 1024), B.make_cfg(1, 2048, 64, 8, 1024, expert="fp8"),
+                B.make_cfg(1, 2048, 128, 8, 768, expert="int4"), B.make_cfg(1, 2048, 64, 6, 1408, 2, 1408),
+                B.make_cfg(1, 7168, 256, 8, 2048, 1, 2048, score="sigmoid", renorm=True, gate_scale=2.5),
+                B.make_cfg(1, 128, 8, 2, 256, act="f32", expert="f32")):
+        assert B.forward_launches(cfg) == 4
     assert B.forward_launches(B.make_cfg(2, 2048, 64, 8, 1024, expert="fp8")) == 5
+    assert B.forward_launches(B.make_cfg(64, 2048, 64, 8, 1024)) == 5
+    assert B.forward_launches(B.make_cfg(4096, 2048, 64, 8, 1024)) == 5
     assert B.forward_launches(B.make_cfg(0, 2048, 64, 8, 1024)) == 0

@@ -110,9 +110,8 @@ def test_forward_matches_oracle(name, T):
 def test_split_path_reproduces_forward_bitwise(name, T):
     """Replaying the layer's own routes through route -> permute -> expert_ffn ->
     combine returns the fused forward's output exactly (the route-replay control).
-    A single token with small down weights (here tiny_f32, the FP8 and INT4 layers,
-    routed and shared experts) runs the down projection and the combine as one
-    launch: still the same bits."""
+    A single token runs the down projection and the combine as one launch (every
+    weight type, with and without shared experts): still the same bits."""
     sp, lay, ml = get_layer(name)
     x = S.make_tokens(sp, T, device="cuda")
     out, idx, gates, drop = ml.forward(x)
