@@ -348,10 +348,9 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
 // the rows as the combine kernel does: fp32, gate-weighted fma in pick order, picks without
 // a row (dropped) skipped, the shared row added last.  No y rows, no combine launch.
 template <typename TW>
-__global__ __launch_bounds__(64 * (kMaxK + 1)) void down_combine_one_kernel(FfnArgs a, const int32_t* __restrict__ topk_idx,
-                                                                const int32_t* __restrict__ slot_row,
-                                                                const float* __restrict__ gw, void* __restrict__ out,
-                                                                int k) {
+__global__ __launch_bounds__(64 * (kMaxK + 1)) void down_combine_one_kernel(
+    FfnArgs a, const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot_row,
+    const float* __restrict__ gw, void* __restrict__ out, int k) {
   using D = Dec<TW>;
   using TA = typename D::TA;
   constexpr int NT = stream_tiles<TW>();
