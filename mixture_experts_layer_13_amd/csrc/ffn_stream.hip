@@ -142,7 +142,16 @@ int stream_channels_per_block(bool gateup, int wdt) { return (gateup ? 16 : 64) 
 // channels over the whole K, so a block covers 4 NT tiles.  Steps are unrolled
 // U deep so each lane keeps U weight loads per matrix and tile in flight.
 // grid: items_max * (N / channels per block) routed blocks, then the shared blocks.
-template <typename TW, bool GATEUP, int MT>
+// PIPE (bf16, one row tile): two register buffers of PU steps, the loads of the next PU steps
+// in flight while the current ones are multiplied; the same steps in the same order, so the
+// same sums.  Measured (graph replays, one box): it pays for single-row items, where a wave has
+// little to multiply between its loads (layers with the single-token down + combine: OLMoE-shaped
+// T=1 39.8 -> 38.7 us, DeepSeek-V3-shaped T=1 151.8 -> 147.6 us, DeepSeek-V2-Lite-shaped 49.8 ->
+// 48.7 us), and costs from 32 rows per expert on (OLMoE T=32 136.7 -> 138.5 us, T=64 154.4 ->
+// 157.1 us), so the host takes it for T = 1 only.  The same buffers in the single-token down +
+// combine launch were slower (DeepSeek-V3-shaped T=1 147.6 -> 148.3 / 150.3 us with 8 / 4 steps
+// per buffer).
+template <typename TW, bool GATEUP, int MT, bool PIPE = false>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   using D = Dec<TW>;
   using TA = typename D::TA;
@@ -158,6 +167,8 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
                     : std::is_same<TW, FP8>::value ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
                                                    : (MT == 1 ? 16 : (MT == 2 ? 8 : 4));
   constexpr int AL = D::AL, KSTEP = D::KSTEP;
+  constexpr int PU = 4;  // PIPE: steps per register buffer
+  static_assert(!PIPE || (std::is_same<TW, bf16>::value && MT == 1), "PIPE: bf16, one row tile");
   __shared__ f32x4 red[KSPLIT > 1 ? 3 : 1][NM][NT][MT][64];
   const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
 
@@ -231,6 +242,50 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
     const int aoff = seg * K;
     const int nsteps = K / KSTEP;
     const int s0 = kpart * nsteps / KSPLIT, s1 = (kpart + 1) * nsteps / KSPLIT;
+    if constexpr (PIPE) {
+      struct Buf {
+        u32x4 bq[NM][NT][PU];
+        u32x4 av[MT][PU][AL];
+      };
+      auto issue = [&](int st, Buf& b) {
+#pragma unroll
+        for (int u = 0; u < PU; ++u)
+          if (st + u < s1) {
+            const int kb = (st + u) * KSTEP;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              b.bq[0][j][u] = b0[j].load(kb);
+              if (NM > 1) b.bq[NM - 1][j][u] = b1[j].load(kb);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int q = 0; q < AL; ++q) b.av[mt][u][q] = ld16(arow[mt] + aoff + kb + (KSTEP / 4) * g + 8 * q);
+          }
+      };
+      auto consume = [&](int st, const Buf& b) {
+#pragma unroll
+        for (int u = 0; u < PU; ++u)
+          if (st + u < s1)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                  acc[m][j][mt] = dstep<TW>(b.av[mt][u], b.bq[m][j][u], 1.f, acc[m][j][mt]);
+      };
+      Buf A, B;
+      if (s0 < s1) issue(s0, A);
+#pragma unroll 1
+      for (int st = s0; st < s1; st += 2 * PU) {
+        if (st + PU < s1) issue(st + PU, B);
+        consume(st, A);
+        if (st + 2 * PU < s1) issue(st + 2 * PU, A);
+        if (st + PU < s1) consume(st + PU, B);
+      }
+      continue;
+    }
 #pragma unroll 1  // U-deep unroll inside already; a further unroll only costs occupancy
     for (int st = s0; st < s1; st += U) {
       u32x4 bq[NM][NT][U];
@@ -453,7 +508,9 @@ hipError_t launch_down_combine_one(int wdt, const FfnArgs& a, const int32_t* top
 // ------------------------------------------------------------------ launch
 template <bool GATEUP, int MT>
 static void launch_stream(int wdt, const FfnArgs& a, int grid, hipStream_t s) {
-  if (wdt == kF32)
+  if (MT == 1 && wdt == kBF16 && a.T == 1)
+    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, 1, true>), dim3(grid), dim3(256), 0, s, a);
+  else if (wdt == kF32)
     hipLaunchKernelGGL((ffn_stream_kernel<float, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
   else if (wdt == kBF16)
     hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
