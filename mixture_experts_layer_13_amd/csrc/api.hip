@@ -38,21 +38,24 @@ constexpr int kSingleMaxT = 256;   // T up to which routing runs as split router
 static_assert(kSingleMaxT * kMaxK <= kSmallMaxPairs, "every small-T forward must fit the small route's pair buffers");
 constexpr int kStreamMaxT = 64;    // T up to which the expert GEMMs use the streaming kernels
 constexpr int64_t kMaxT = 1 << 20;
-// Experts must average this many rows for the 256-row tiled kernels (ffn_tiled256.hip).  Off by
-// default: measured on the DeepSeek-V3-shaped layer at T=16384 they move half the operand bytes per
-// flop and lift the L2 hit rate from 44% to 74%, but gate/up only went 9.52 -> 9.35 ms and down
-// 4.64 -> 5.29 ms (OLMoE T=4096 gate/up 361 -> 394 us), so the 128-row kernels stay.  The
-// environment variable of the same name, read at every plan, overrides the default (a positive
-// integer; it is how the GPU tests run the 256-row kernels against the 128-row ones).
-#ifndef MOE_ROWS256_MIN_AVG
-#define MOE_ROWS256_MIN_AVG (1 << 30)
-#endif
+// The 256-row tiled kernels (ffn_tiled256.hip, eight waves) and when the plan takes them.  By
+// default: the bf16 gate/up GEMM of a layer with a long K (d >= 4096) whose experts average at
+// least 128 rows, on the many-token route path; its down GEMM keeps 128-row items (a second
+// tile map).  Measured on the DeepSeek-V3-shaped layer (d = 7168), one box: gate/up T=16384
+// 9.58 -> 9.12 ms, T=4096 3.59 -> 3.45 ms; down T=16384 4.56 -> 4.88 ms, T=4096 1.69 -> 1.91 ms
+// (K = F = 2048 is too short for the deeper ring to pay); and with d = 2048 gate/up loses too
+// (OLMoE T=4096 365 -> 402 us, DeepSeek-V2-Lite T=8192 800 -> 825 us).  The environment variable
+// MOE_ROWS256_MIN_AVG, read at every plan, overrides the rule for both GEMMs: a positive n takes
+// the 256-row kernels wherever experts average at least n rows, 0 never (the GPU tests use both
+// to check the kernels against each other bit for bit).
+constexpr int64_t kRows256Default = -1;
 int64_t rows256_min_avg() {
   const char* v = getenv("MOE_ROWS256_MIN_AVG");
-  if (!v || !*v) return MOE_ROWS256_MIN_AVG;
+  if (!v || !*v) return kRows256Default;
   char* end = nullptr;
   const long long n = strtoll(v, &end, 10);
-  return (end && *end == 0 && n > 0) ? (int64_t)(n < (1 << 30) ? n : (1 << 30)) : (int64_t)MOE_ROWS256_MIN_AVG;
+  if (!end || *end != 0 || n < 0) return kRows256Default;
+  return (int64_t)(n < (1 << 30) ? n : (1 << 30));  // 0: never
 }
 
 struct Plan {
@@ -65,11 +68,13 @@ struct Plan {
   int KS, kchunk;
   int rt, n_rt, rpb, n_rb;
   int mode, bm;
+  int bm_dn;  // rows per item of the down GEMM (bm unless the gate/up GEMM takes 256-row items alone)
   bool wstream;  // tiled kernels stream the weights non-temporally
   bool rowskip_gu, rowskip_dn;  // tiled kernels skip the idle row tiles of partly filled items
-  int64_t items_max;
-  int sh_items;
-  size_t o_part, o_arrived, o_hist, o_counts, o_off, o_rowtok, o_slot, o_items, o_nitems, o_h, o_hsh, o_y, o_ysh, total;
+  int64_t items_max, items_max_dn;
+  int sh_items, sh_items_dn;
+  size_t o_part, o_arrived, o_hist, o_counts, o_off, o_rowtok, o_slot, o_items, o_nitems, o_items_dn, o_nitems_dn, o_h,
+      o_hsh, o_y, o_ysh, total;
 };
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -176,12 +181,16 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   // registers of 32-row items: measured on OLMoE T=64, 170 -> 161 us) or 32 rows; above 32 a hot
   // expert is split into two items (its weights are read twice), which costs less than the
   // registers (occupancy) of 64-row items
-  // tiled bf16 kernels take 256-row items when experts average at least MOE_ROWS256_MIN_AVG rows
-  // (half the operand bytes per flop of 128-row items, one wave per SIMD); below that the extra
-  // idle rows of each expert's last item and the coarser tail cost more
-  const bool rows256 = q.wdt == MOE_BF16 && q.mode == 1 && (int64_t)q.T * q.k >= rows256_min_avg() * q.E;
-  q.bm = q.mode == 1 ? (rows256 ? 2 * kPrefillRows : kPrefillRows)
+  // tiled bf16 kernels: 256-row items per the rule above rows256_min_avg()
+  bool gu256 = false, dn256 = false;
+  if (q.wdt == MOE_BF16 && q.mode == 1) {
+    const int64_t env = rows256_min_avg(), tk = (int64_t)q.T * q.k;
+    if (env > 0) gu256 = dn256 = tk >= env * q.E;
+    else if (env < 0) gu256 = !q.single && q.d >= 4096 && tk >= (int64_t)kPrefillRows * q.E;
+  }
+  q.bm = q.mode == 1 ? (gu256 ? 2 * kPrefillRows : kPrefillRows)
                      : ((q.T <= 16 || (int64_t)q.T * q.k <= 8 * (int64_t)q.E) ? 16 : 32);
+  q.bm_dn = q.mode == 1 ? (dn256 ? 2 * kPrefillRows : kPrefillRows) : q.bm;
   // tiled mode with at most 32 rows per expert on average: an expert's weights are read by one
   // row tile (measured: DeepSeek-V3 T=256 2.81 -> 2.61 ms; with several row tiles per expert the
   // L2 reuse they lose costs far more, e.g. OLMoE T=4096 gate/up 313 -> 401 us)
@@ -204,6 +213,8 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   }
   q.items_max = q.R / q.bm + (q.R < q.E ? q.R : q.E);
   q.sh_items = q.S > 0 ? (q.T + q.bm - 1) / q.bm : 0;
+  q.items_max_dn = q.R / q.bm_dn + (q.R < q.E ? q.R : q.E);
+  q.sh_items_dn = q.S > 0 ? (q.T + q.bm_dn - 1) / q.bm_dn : 0;
 
   const size_t es = q.act == MOE_F32 ? 4 : 2;
   size_t o = 0;
@@ -221,6 +232,8 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   q.o_slot = take((size_t)pairs * 4);
   q.o_items = take((size_t)q.items_max * 16);
   q.o_nitems = take(4);
+  q.o_items_dn = q.bm_dn != q.bm ? take((size_t)q.items_max_dn * 16) : q.o_items;
+  q.o_nitems_dn = q.bm_dn != q.bm ? take(4) : q.o_nitems;
   q.o_h = take((size_t)q.R * q.F * es);
   q.o_hsh = take((size_t)q.T * q.S * q.FS * es);
   q.o_y = take((size_t)q.R * q.d * es);
@@ -255,9 +268,19 @@ moe_status hip_ok(hipError_t e, const char* what) {
 // 154.2 -> 150.4 us (means of two rounds).
 bool one_token(const Plan& p) { return p.T == 1 && p.mode == 0; }
 
+// the down GEMM's arguments: its own tile map when its items differ from the gate/up GEMM's
+FfnArgs down_args(const Plan& p, void* ws, FfnArgs a) {
+  a.items = at<int4>(ws, p.o_items_dn);
+  a.n_items = at<int32_t>(ws, p.o_nitems_dn);
+  a.items_max = (int)p.items_max_dn;
+  a.sh_items = p.sh_items_dn;
+  a.bm = p.bm_dn;
+  return a;
+}
+
 // the expert GEMMs and the combine of moe_forward / moe_forward_with_routes
 // (timing marks 3.. for moe_forward only: `timed`)
-moe_status enqueue_experts_and_combine(const Plan& p, const FfnArgs& a, const int32_t* topk_idx,
+moe_status enqueue_experts_and_combine(const Plan& p, void* ws, const FfnArgs& a, const int32_t* topk_idx,
                                        const int32_t* slot, const float* topk_w, const void* ysh, void* out,
                                        hipStream_t s, bool timed) {
   const int nl = timed ? (one_token(p) ? 4 : 5) : 1 << 30;  // an impossible count records nothing
@@ -269,7 +292,7 @@ moe_status enqueue_experts_and_combine(const Plan& p, const FfnArgs& a, const in
     mark(4, nl, s);
     return st;
   }
-  if ((st = hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM"))) return st;
+  if ((st = hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, down_args(p, ws, a), s), "down GEMM"))) return st;
   mark(4, nl, s);
   st = hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
   mark(5, nl, s);
@@ -311,6 +334,11 @@ PermArgs perm_args(const Plan& p, void* ws, int32_t* counts, int32_t* offsets, i
   a.items = at<int4>(ws, p.o_items);
   a.n_items = at<int32_t>(ws, p.o_nitems);
   a.bm = p.bm;
+  // the down GEMM's own tile map (many-token path only: the plan splits nowhere else)
+  const bool split = p.bm_dn != p.bm;
+  a.items_dn = split ? at<int4>(ws, p.o_items_dn) : nullptr;
+  a.n_items_dn = split ? at<int32_t>(ws, p.o_nitems_dn) : nullptr;
+  a.bm_dn = p.bm_dn;
   a.rt = p.rt * p.rpb;  // tokens per permute block
   return a;
 }
@@ -512,9 +540,14 @@ moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offs
   if ((st = hip_ok(launch_tile_map(offsets, p.E, (int)p.R, p.bm, at<int4>(ws, p.o_items), at<int32_t>(ws, p.o_nitems), s),
                    "tile map")))
     return st;
+  if (p.bm_dn != p.bm &&
+      (st = hip_ok(launch_tile_map(offsets, p.E, (int)p.R, p.bm_dn, at<int4>(ws, p.o_items_dn),
+                                   at<int32_t>(ws, p.o_nitems_dn), s),
+                   "down tile map")))
+    return st;
   FfnArgs a = ffn_args(p, ws, x, row_token, w, y_rows, y_shared);
   if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
-  return hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM");
+  return hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, down_args(p, ws, a), s), "down GEMM");
 }
 
 moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* slot_row, const float* topk_w,
@@ -571,7 +604,7 @@ moe_status moe_forward(const moe_cfg* cfg, const void* x, const void* w_router, 
   mark(2, nl, s);
   void* ysh = p.S ? at<void>(ws, p.o_ysh) : nullptr;
   FfnArgs a = ffn_args(p, ws, x, rowtok, w, at<void>(ws, p.o_y), ysh);
-  return enqueue_experts_and_combine(p, a, topk_idx, slot, topk_w, ysh, out, s, true);
+  return enqueue_experts_and_combine(p, ws, a, topk_idx, slot, topk_w, ysh, out, s, true);
 }
 
 moe_status moe_forward_noalloc(const moe_cfg* cfg, const void* x, const void* w_router, const float* logit_bias,
@@ -622,7 +655,7 @@ moe_status moe_forward_with_routes(const moe_cfg* cfg, const void* x, const int3
   }
   void* ysh = p.S ? at<void>(ws, p.o_ysh) : nullptr;
   FfnArgs a = ffn_args(p, ws, x, rowtok, w, at<void>(ws, p.o_y), ysh);
-  return enqueue_experts_and_combine(p, a, topk_idx, slot, topk_w, ysh, out, s, false);
+  return enqueue_experts_and_combine(p, ws, a, topk_idx, slot, topk_w, ysh, out, s, false);
 }
 
 moe_status moe_pack_weights(int32_t dtype, const void* src, void* dst, int64_t rows, int32_t K, void* stream) {

@@ -2,13 +2,16 @@
 // 256-weight-row blocks fed through an LDS ring by direct global -> LDS loads.
 //
 // The 128-row kernel (ffn_tiled.hip) keeps one K step of operands in flight per
-// wave in registers; at the chip's measured 1-2 us memory latency under load
-// that leaves its matrix cores waiting about half the time.  Here a block of
-// four waves (one per SIMD) owns 256 rows x 256 weight rows, which halves the
-// operand bytes per flop, and stages both operands in a ring of P = 4 LDS slots
-// of one 32-wide K step each, filled by global_load_lds_dwordx4 (each lane's 16
-// bytes go straight to LDS, no registers held): three K steps stay in flight
-// while one is computed.
+// wave in registers.  Here a block of eight waves (two per SIMD) owns 256 rows x
+// 256 weight rows, which halves the operand bytes per flop, and stages both
+// operands in a ring of P = 4 LDS slots of one 32-wide K step each (128 KB, one
+// block per CU), filled by global_load_lds_dwordx4 (each lane's 16 bytes go
+// straight to LDS, no registers held): three K steps stay in flight while one
+// is computed.  With two waves per SIMD one wave's LDS fragment reads and waits
+// overlap the other's MFMAs (a four-wave form, one wave per SIMD and 4 x 4
+// tiles each, lost that time: DeepSeek-V3-shaped gate/up at T=16384 9.42 ms
+// against 9.12, down 5.33 against 4.88); a fifth slot (the whole 160 KB)
+// measured slower (9.35 ms).
 //
 // LDS image of one slot: A (activation rows) then B (weight rows), each 16
 // groups of 16 rows x 64 bytes (32 bf16 of K), 1 KB per group, written by one
@@ -26,15 +29,15 @@
 // workgroup fence drains them at every barrier), so the DMA instructions are
 // written as inline assembly the compiler does not model, and the kernel waits
 // on the vector-memory counter itself: before the barrier that publishes K step
-// t + 1 each wave waits until only the 8 loads per step it issued for later
+// t + 1 each wave waits until only the 4 loads per step it issued for later
 // steps are outstanding; the barrier then also tells every wave that all waves
 // have finished reading the slot that the next DMA overwrites.  The main loop
 // issues no other vector-memory instruction, so those counts are exact.
 //
-// Waves: wave w = 2 i + j owns rows 128 i .. +127 and weight rows of column
-// half j (gate/up: gate channels n0 + 64 j .. +63 and the up rows of the same
-// channels; down: output columns n0 + 128 j .. +127) as 4 x 4 tiles of 32 x 32
-// (v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane).  Every output
+// Waves: wave w = 4 i + j owns rows 128 i .. +127 and weight rows of column
+// quarter j (gate/up: gate channels n0 + 32 j .. +31 and the up rows of the
+// same channels; down: output columns n0 + 64 j .. +63) as 4 x 2 tiles of 32 x
+// 32 (v_mfma_f32_32x32x16_bf16, 128 fp32 accumulators per lane).  Every output
 // element sums the same products in the same K order as the 128-row kernel, so
 // the two give identical results, bit for bit.
 #include "ffn_common.hpp"
@@ -43,11 +46,11 @@ namespace moe {
 
 namespace {
 
+constexpr int kWaves = 8;                // waves per block
 constexpr int kRingP = 4;                // LDS slots
 constexpr int kStepK = 32;               // K elements per slot
 constexpr int kSlotB = 16384;            // bytes of one operand in a slot (16 groups x 1 KB)
 constexpr int kSlot = 2 * kSlotB;        // A then B
-constexpr int kDmaPerStep = 8;           // DMA instructions per wave and K step (4 A + 4 B groups)
 
 // 16 bytes per lane from global memory into LDS at lds + 16 * lane.  M0 carries
 // the wave-uniform LDS address; it is restored afterwards, so the compiler's own
@@ -71,6 +74,14 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// waits until at most n K steps of D loads each are outstanding (n wave-uniform, 0..4)
+template <int D> __device__ __forceinline__ void wait_steps(int n) {
+  if (n >= 4) wait_vm<4 * D>();
+  else if (n == 3) wait_vm<3 * D>();
+  else if (n == 2) wait_vm<2 * D>();
+  else if (n == 1) wait_vm<D>();
+  else wait_vm<0>();
+}
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 // keeps the compiler from moving memory accesses across this point (emits nothing)
 __device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
@@ -84,13 +95,20 @@ __device__ __forceinline__ void block_barrier() {
 }  // namespace
 
 template <bool GATEUP, bool TILED>
-__global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 1) void ffn_tiled256_kernel(FfnArgs a) {
+  constexpr int NW = kWaves;
   constexpr int NT = GATEUP ? 128 : 256;  // output channels (gate/up) or columns (down) per block
+  constexpr int NTH = 64 * NW;            // threads
+  constexpr int GPW = 16 / NW;            // A groups and B groups each wave loads per K step
+  constexpr int kDma = 2 * GPW;           // DMA instructions per wave and K step
+  constexpr int NCW = NW / 2;             // waves over the weight rows (two over the rows)
+  constexpr int NB = 8 / NCW;             // 32-row weight tiles per wave
+  constexpr int GT = NB / 2;              // gate/up: gate tiles per wave (and as many up tiles)
   __shared__ __attribute__((aligned(1024))) char smem[kRingP * kSlot];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int tid = threadIdx.x, lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wi = w >> 1, wj = w & 1;
+  const int wi = w / NCW, wj = w % NCW;
   TileInfo ti;
   if (!tile_of(a, NT, ti)) return;
   const int e = ti.e, row0 = ti.row0, mrows = ti.mrows, n0 = ti.n0;
@@ -100,17 +118,17 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
   const int Kb = Kseg * 2;  // bytes per weight row of one K segment
   const int nkt = Kfull / kStepK;
 
-  // ---- DMA sources: this wave fills A groups and B groups 4 w .. 4 w + 3.
+  // ---- DMA sources: this wave fills A groups and B groups GPW w .. GPW w + GPW - 1.
   // Row-major image (activations, and weights in the row layout): lane l loads row l / 4 of the
   // group, so every group of four lanes reads one contiguous 64-byte run (rows spread over the
   // lanes of a quad cost the address and tag units one lookup per lane), and it stores K unit
   // v = l % 4 of that row's slot, holding logical unit u = v ^ ((row / 2) % 4): the XOR keeps
   // the fragment reads below (eight lanes, eight rows, one unit) on distinct banks.
   const int rn = lane >> 2, ru = (lane & 3) ^ ((rn >> 1) & 3);  // row in group, logical 16-byte unit
-  const char* asrc[4];
+  const char* asrc[GPW];
 #pragma unroll
-  for (int gi = 0; gi < 4; ++gi) {
-    const int r = min(16 * (4 * w + gi) + rn, mrows - 1);
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int r = min(16 * (GPW * w + gi) + rn, mrows - 1);
     if (GATEUP) {
       int tok = shared ? row0 + r : a.row_token[row0 + r];
       tok = min(max(tok, 0), a.T - 1);
@@ -126,11 +144,11 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
   } else {
     bmat[0] = bmat[1] = (const char*)(shared ? a.shd : expert_mat<bf16>(a.wd, e, a.d, Kseg));
   }
-  uint32_t boff[4];
-  const char* bsrc[4];
+  uint32_t boff[GPW];
+  const char* bsrc[GPW];
 #pragma unroll
-  for (int gi = 0; gi < 4; ++gi) {
-    const int g = 4 * w + gi;  // B group of the block: gate/up 0..7 gate, 8..15 up
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = GPW * w + gi;  // B group of the block: gate/up 0..7 gate, 8..15 up
     int row;
     if (GATEUP) row = n0 + 16 * (g & 7) + rn;
     else row = min(n0 + 16 * g, a.d - 16) + rn;  // a last block may run past d: re-read, never stored
@@ -151,9 +169,9 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
     const uint32_t slot = lds0 + (uint32_t)(kt % kRingP) * kSlot;
     const size_t wo = woff(kt);
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) dma16(asrc[gi] + (size_t)kt * (kStepK * 2), slot + (4 * w + gi) * 1024);
+    for (int gi = 0; gi < GPW; ++gi) dma16(asrc[gi] + (size_t)kt * (kStepK * 2), slot + (GPW * w + gi) * 1024);
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) dma16(bsrc[gi] + wo + boff[gi], slot + kSlotB + (4 * w + gi) * 1024);
+    for (int gi = 0; gi < GPW; ++gi) dma16(bsrc[gi] + wo + boff[gi], slot + kSlotB + (GPW * w + gi) * 1024);
   };
 
   // ---- fragment reads: lane l takes row n = l % 16 of group 2 m + (l % 32) / 16 of a 32-row tile
@@ -165,41 +183,41 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
   const int uofs = ((lane >> 4) & 1) * 1024 + 256 * fh + 16 * fn;
   const int aofs[2] = {rofs, rofs ^ 32};
   const int bofs[2] = {TILED ? uofs : rofs, TILED ? uofs + 512 : (rofs ^ 32)};
-  int ga[4], gb[4];
+  int ga[4], gb[NB];
 #pragma unroll
   for (int m = 0; m < 4; ++m) ga[m] = 8 * wi + 2 * m;
 #pragma unroll
-  for (int n = 0; n < 4; ++n) gb[n] = GATEUP ? ((n >> 1) * 8 + 4 * wj + 2 * (n & 1)) : (8 * wj + 2 * n);
+  for (int n = 0; n < NB; ++n) gb[n] = GATEUP ? ((n / GT) * 8 + 2 * GT * wj + 2 * (n % GT)) : (2 * NB * wj + 2 * n);
   const bool active = 128 * wi < mrows;  // a wave whose rows lie past the item's end only moves data
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NB];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x16{};
-  u32x4 fa[2][4], fb[2][4];
-  auto rd = [&](int kt, int s, u32x4 (&A)[4], u32x4 (&B)[4]) {
+    for (int n = 0; n < NB; ++n) acc[m][n] = f32x16{};
+  u32x4 fa[2][4], fb[2][NB];
+  auto rd = [&](int kt, int s, u32x4 (&A)[4], u32x4 (&B)[NB]) {
     const char* slot = smem + (kt % kRingP) * kSlot;
 #pragma unroll
     for (int m = 0; m < 4; ++m) A[m] = *reinterpret_cast<const u32x4*>(slot + aofs[s] + ga[m] * 1024);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) B[n] = *reinterpret_cast<const u32x4*>(slot + kSlotB + bofs[s] + gb[n] * 1024);
+    for (int n = 0; n < NB; ++n) B[n] = *reinterpret_cast<const u32x4*>(slot + kSlotB + bofs[s] + gb[n] * 1024);
   };
-  auto mma = [&](const u32x4 (&A)[4], const u32x4 (&B)[4]) {
+  auto mma = [&](const u32x4 (&A)[4], const u32x4 (&B)[NB]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int n = 0; n < 4; ++n) acc[m][n] = mma32_bf16(A[m], B[n], acc[m][n]);
+      for (int n = 0; n < NB; ++n) acc[m][n] = mma32_bf16(A[m], B[n], acc[m][n]);
   };
-  // the 8 LDS reads of one slice go out between the first 8 of the 16 MFMAs of the other
+  // the 4 + NB LDS reads of one slice go out between the first MFMAs of the other
   // (pinned: left alone, the scheduler bunches them)
   auto pin_slice = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4 + NB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 3 * NB - 4, 0);
   };
 
   // Main loop.  ACT: this wave has rows to compute (else it only moves data and meets the barriers).
@@ -207,15 +225,12 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
     constexpr bool ACT = decltype(act_tag)::value;
     const int pro = min(kRingP, nkt);
     for (int kt = 0; kt < pro; ++kt) issue(kt);
-    if (pro >= 4) wait_vm<3 * kDmaPerStep>();  // K step 0 landed; the others stay in flight
-    else if (pro == 3) wait_vm<2 * kDmaPerStep>();
-    else if (pro == 2) wait_vm<kDmaPerStep>();
-    else wait_vm<0>();
+    wait_steps<kDma>(pro - 1);  // K step 0 landed; the others stay in flight
     block_barrier();
     if (ACT) rd(0, 0, fa[0], fb[0]);
     int kt = 0;
-    // steady state: K step kt + 1 must have landed at the barrier, kt + 2 and kt + 3 stay in
-    // flight, and K step kt + 4 goes into the slot of kt (every wave has read it by then)
+    // steady state: K step kt + 1 must have landed at the barrier, kt + 2 .. kt + P - 1 stay in
+    // flight, and K step kt + P goes into the slot of kt (every wave has read it by then)
     for (; kt + kRingP < nkt; ++kt) {
       if (ACT) {
         rd(kt, 1, fa[1], fb[1]);
@@ -224,7 +239,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
         mem_fence_compiler();
         wait_lgkm0();
       }
-      wait_vm<2 * kDmaPerStep>();
+      wait_steps<kDma>(kRingP - 2);
       block_barrier();
       issue(kt + kRingP);
       if (ACT) {
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
         pin_slice();
       }
     }
-    // the last (at most four) K steps: everything is issued, the waits shrink
+    // the last (at most P) K steps: everything is issued, the waits shrink
     for (; kt < nkt; ++kt) {
       if (ACT) {
         rd(kt, 1, fa[1], fb[1]);
@@ -243,9 +258,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
       }
       if (kt + 1 < nkt) {
         const int later = nkt - 2 - kt;  // K steps issued after kt + 1
-        if (later >= 2) wait_vm<2 * kDmaPerStep>();
-        else if (later == 1) wait_vm<kDmaPerStep>();
-        else wait_vm<0>();
+        wait_steps<kDma>(min(later, kRingP - 2));
         block_barrier();
         if (ACT) rd(kt + 1, 0, fa[0], fb[0]);
       }
@@ -263,17 +276,17 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
   const int ld = GATEUP ? (shared ? a.S * a.FS : a.F) : a.d;
   const int h = lane >> 5, c = lane & 31;
   if (GATEUP) {
-    // 256 rows x 128 channels: wave (i, j) writes rows 128 i.., channels 64 j..
+    // 256 rows x 128 channels: wave (i, j) writes rows 128 i.., channels 32 GT j..
     constexpr int LDH = 128 + 8;
     if (active) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < GT; ++n)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int r = 128 * wi + 32 * m + 8 * (i >> 2) + 4 * h + (i & 3);
-            stage[r * LDH + 64 * wj + 32 * n + c] = (bf16)(silu(acc[m][n][i]) * acc[m][n + 2][i]);
+            stage[r * LDH + 32 * GT * wj + 32 * n + c] = (bf16)(silu(acc[m][n][i]) * acc[m][n + GT][i]);
           }
         mem_fence_compiler();
       }
@@ -281,8 +294,8 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
     __syncthreads();
     constexpr int CK = 128 / 8;
 #pragma unroll 4
-    for (int q = 0; q < 256 * CK / 256; ++q) {
-      const int idx = tid + 256 * q, r = idx / CK, ck = idx % CK;
+    for (int q = 0; q < 256 * CK / NTH; ++q) {
+      const int idx = tid + NTH * q, r = idx / CK, ck = idx % CK;
       if (r < mrows) st16(out + (size_t)(row0 + r) * ld + n0 + 8 * ck, *reinterpret_cast<const u32x4*>(&stage[r * LDH + 8 * ck]));
     }
   } else {
@@ -295,19 +308,19 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
 #pragma unroll
-          for (int n = 0; n < 4; ++n)
+          for (int n = 0; n < NB; ++n)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int r = 32 * m + 8 * (i >> 2) + 4 * h + (i & 3);
-              stage[r * LDH + 128 * wj + 32 * n + c] = (bf16)acc[m][n][i];
+              stage[r * LDH + 32 * NB * wj + 32 * n + c] = (bf16)acc[m][n][i];
             }
           mem_fence_compiler();  // one row tile at a time keeps the accumulator reads short-lived
         }
       }
       __syncthreads();
 #pragma unroll 4
-      for (int q = 0; q < 128 * CK / 256; ++q) {
-        const int idx = tid + 256 * q, r = idx / CK, ck = idx % CK, col = n0 + 8 * ck;
+      for (int q = 0; q < 128 * CK / NTH; ++q) {
+        const int idx = tid + NTH * q, r = idx / CK, ck = idx % CK, col = n0 + 8 * ck;
         const int row = 128 * pass + r;
         if (row < mrows && col < a.d)
           st16(out + (size_t)(row0 + row) * ld + col, *reinterpret_cast<const u32x4*>(&stage[r * LDH + 8 * ck]));
@@ -318,12 +331,13 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled256_kernel(FfnArgs a) {
 }
 
 void launch_tiled256_bf16(bool gateup, const FfnArgs& a, int grid, hipStream_t s) {
+  const dim3 blk(64 * kWaves);
   if (gateup) {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled256_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled256_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled256_kernel<true, true>), dim3(grid), blk, 0, s, a);
+    else hipLaunchKernelGGL((ffn_tiled256_kernel<true, false>), dim3(grid), blk, 0, s, a);
   } else {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled256_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled256_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled256_kernel<false, true>), dim3(grid), blk, 0, s, a);
+    else hipLaunchKernelGGL((ffn_tiled256_kernel<false, false>), dim3(grid), blk, 0, s, a);
   }
 }
 

@@ -44,6 +44,9 @@ struct PermArgs {
   int4* items;               // tile map {expert, first row, rows, 0} (null: not built)
   int32_t* n_items;
   int bm;                    // rows per tile-map item
+  int4* items_dn;            // many-token permutation: the down GEMM's own tile map of bm_dn-row
+  int32_t* n_items_dn;       // items (null: the down GEMM reads `items`)
+  int bm_dn;
   int rt;                    // tokens per router block / tile-histogram row (large T)
 };
 

@@ -906,6 +906,10 @@ __global__ __launch_bounds__(512) void permute_multi_kernel(const int32_t* __res
     for (int x = tid; x < E; x += blockDim.x) pa.counts[x] = tot[x];
     for (int x = tid; x <= E; x += blockDim.x) pa.offsets[x] = off[x];
     if (pa.items) write_tile_map(kept, off, E, pa.bm, pa.items, pa.n_items, tmp);
+    if (pa.items_dn) {
+      __syncthreads();  // tmp is reused
+      write_tile_map(kept, off, E, pa.bm_dn, pa.items_dn, pa.n_items_dn, tmp);
+    }
   }
   const int t0 = tile * pa.rt, nt = min(pa.rt, T - t0), np = nt * k;
   for (int p0 = 0; p0 < np; p0 += blockDim.x) {

@@ -241,3 +241,31 @@ def test_forward_launch_count_rule(B):
     assert B.forward_launches(B.make_cfg(64, 2048, 64, 8, 1024)) == 5
     assert B.forward_launches(B.make_cfg(4096, 2048, 64, 8, 1024)) == 5
     assert B.forward_launches(B.make_cfg(0, 2048, 64, 8, 1024)) == 0
+
+
+def test_256_row_item_rule(B, monkeypatch):
+    """Which GEMMs take 256-row items, read off the workspace size (a second tile map,
+    or fewer, larger items): by default the bf16 gate/up GEMM of a long-K layer (d >=
+    4096) whose experts average at least 128 rows, with the down GEMM on its own
+    128-row map; MOE_ROWS256_MIN_AVG=n takes them for both GEMMs from n rows on, 0
+    never."""
+    dsv3 = dict(n_shared=1, ffn_shared=2048, score="sigmoid", renorm=True, gate_scale=2.5)
+
+    def ws(T, d, E, k, F, env, **kw):
+        if env is None:
+            monkeypatch.delenv("MOE_ROWS256_MIN_AVG", raising=False)
+        else:
+            monkeypatch.setenv("MOE_ROWS256_MIN_AVG", env)
+        return B.workspace_bytes(B.make_cfg(T, d, E, k, F, **kw))
+
+    for T in (4096, 16384):
+        never, default, both = (ws(T, 7168, 256, 8, 2048, e, **dsv3) for e in ("0", None, "1"))
+        assert default > never and both != never and both != default
+    # below 128 rows per expert, a short K, INT4 / FP8 weights or the small route: 128-row items
+    for args, kw in (((2048, 7168, 256, 8, 2048), dsv3), ((4096, 2048, 64, 8, 1024), {}),
+                     ((8192, 2048, 64, 6, 1408), dict(n_shared=2, ffn_shared=1408)),
+                     ((4096, 7168, 256, 8, 2048), dict(dsv3, expert="fp8")), ((1, 7168, 256, 8, 2048), dsv3)):
+        assert ws(*args, None, **kw) == ws(*args, "0", **kw), args
+    # the override reaches layers the default leaves alone
+    assert ws(4096, 2048, 64, 8, 1024, "1") != ws(4096, 2048, 64, 8, 1024, "0")
+    monkeypatch.delenv("MOE_ROWS256_MIN_AVG", raising=False)

@@ -106,7 +106,7 @@ def test_forward_matches_oracle(name, T):
 @pytest.mark.parametrize("name,T", [("tiny_f32", 64), ("tiny_f32", 1), ("olmoe", 1), ("olmoe", 8), ("olmoe", 300),
                                     ("olmoe", 20000), ("dsv2_lite_cap", 8192), ("dsv2_lite", 1), ("dsv2_lite_cap", 1),
                                     ("olmoe_fp8", 1), ("dsv2_lite_fp8", 1), ("qwen3_int4", 1), ("qwen3_int4", 32),
-                                    ("dsv3", 1)])
+                                    ("dsv3", 1), ("dsv3", 4096)])
 def test_split_path_reproduces_forward_bitwise(name, T):
     """Replaying the layer's own routes through route -> permute -> expert_ffn ->
     combine returns the fused forward's output exactly (the route-replay control).
@@ -235,24 +235,32 @@ def test_side_stream_forward_after_default_stream_churn():
                            v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
 
 
-@pytest.mark.parametrize("name,T", [("olmoe", 4096), ("dsv2_lite_cap", 8192), ("dsv3", 4096)])
+@pytest.mark.parametrize("name,T", [("olmoe", 4096), ("dsv2_lite_cap", 8192), ("dsv3", 4096), ("dsv3", 16384)])
 def test_256_row_kernels_match_the_128_row_kernels_bitwise(name, T, monkeypatch):
-    """The 256-row tiled kernels (direct global -> LDS loads, off by default) sum every
-    output in the same K order as the 128-row kernels: with MOE_ROWS256_MIN_AVG=1 the
-    plan takes them for every bf16 prefill layer, and the forward must not change by a
-    bit (dropless and capacity modes, shared experts, partly filled 256-row items)."""
+    """The 256-row tiled kernels (direct global -> LDS loads, eight waves) sum every
+    output in the same K order as the 128-row kernels, so the forward must not change
+    by a bit whichever the plan takes: MOE_ROWS256_MIN_AVG=0 keeps 128-row items for
+    both GEMMs, =1 takes 256-row items for both in every bf16 prefill layer, and the
+    default takes them for the gate/up GEMM of the DeepSeek-V3-shaped layer alone, its
+    down GEMM reading a second tile map of 128-row items (dropless and capacity modes,
+    shared experts, partly filled 256-row items)."""
     from mixture_experts_layer_13_amd import binding as B
     sp, lay, ml = get_layer(name)
     x = S.make_tokens(sp, T, device="cuda")
-    ref = [t.clone() for t in ml.forward(x)]
-    torch.cuda.synchronize()
     c = ml.cfg_for(T)
-    ws128 = B.workspace_bytes(c)
-    monkeypatch.setenv("MOE_ROWS256_MIN_AVG", "1")
-    assert B.workspace_bytes(c) != ws128  # the plan now holds 256-row items
-    out = ml.forward(x)
-    torch.cuda.synchronize()
-    monkeypatch.delenv("MOE_ROWS256_MIN_AVG")
-    for u, v in zip(ref, out):
-        assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
-                           v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), name
+    runs, sizes = {}, {}
+    for env in ("0", None, "1"):
+        if env is None:
+            monkeypatch.delenv("MOE_ROWS256_MIN_AVG", raising=False)
+        else:
+            monkeypatch.setenv("MOE_ROWS256_MIN_AVG", env)
+        sizes[env] = B.workspace_bytes(c)
+        runs[env] = [t.clone() for t in ml.forward(x)]
+        torch.cuda.synchronize()
+    monkeypatch.delenv("MOE_ROWS256_MIN_AVG", raising=False)
+    assert sizes["1"] != sizes["0"]  # the plan holds 256-row items
+    assert (sizes[None] != sizes["0"]) == (name == "dsv3")  # default: the DeepSeek-V3 gate/up alone
+    for env in (None, "1"):
+        for u, v in zip(runs["0"], runs[env]):
+            assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                               v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), (name, T, env)
