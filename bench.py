@@ -222,21 +222,30 @@ def alg_work(sp, T, idx, drop):
 
 
 # gate/up traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE of the bf16 tiled gate/up kernel),
-# one per workload: (spec, T, file under profiles/)
-TRAFFIC_WORKLOADS = {"dsv3_T16384": ("dsv3", 16384), "olmoe_T4096": ("olmoe", 4096)}
-GATEUP_KERNEL = ("ffn_tiled32_kernel<true", "ffn_tiled32_kernelILb1E")  # demangled or mangled name
-# the sources the dominant (bf16 tiled gate/up) kernel is compiled from
-KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", f)
-                  for f in ("ffn_tiled.hip", "ffn_common.hpp", "common.hpp", "kernels.hpp")]
+# one per workload: (spec, T, the kernel the plan runs there)
+TRAFFIC_WORKLOADS = {"dsv3_T16384": ("dsv3", 16384, "tiled256"), "olmoe_T4096": ("olmoe", 4096, "tiled32")}
+# per kernel: its name in the counter csv (demangled or mangled), as reported, and the sources it is compiled from
+GATEUP_KERNELS = {
+    "tiled32": (("ffn_tiled32_kernel<true", "ffn_tiled32_kernelILb1E"),
+                "ffn_tiled32_kernel<gate/up + SwiGLU, tiled weights>", "ffn_tiled.hip"),
+    "tiled256": (("ffn_tiled256_kernel<true", "ffn_tiled256_kernelILb1E"),
+                 "ffn_tiled256_kernel<gate/up + SwiGLU, tiled weights>", "ffn_tiled256.hip"),
+}
+
+
+def kernel_sources(workload):
+    src = GATEUP_KERNELS[TRAFFIC_WORKLOADS[workload][2]][2]
+    return [os.path.join(ROOT, "mixture_experts_layer_13_amd", "csrc", f)
+            for f in (src, "ffn_common.hpp", "common.hpp", "kernels.hpp")]
 
 
 def traffic_path(workload):
     return os.path.join(ROOT, "profiles", f"gateup_tiled_{workload}_traffic.json")
 
 
-def kernel_sha():
+def kernel_sha(workload):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in kernel_sources(workload):
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
@@ -248,7 +257,7 @@ def traffic_record(workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != kernel_sha():
+    if rec.get("source_sha256") != kernel_sha(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -276,19 +285,20 @@ def write_traffic_record(workload, fetch_dir, write_dir, copy_fetch_dir, copy_wr
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the workload, and of the copy probe,
     whose known 1 GiB read + 1 GiB write calibrates each counter."""
     copy = ("copyBuffer",)  # the runtime's device-to-device copy kernel behind the probe's Tensor.copy_
-    f_k = _pmc_mean_kib(fetch_dir, "FETCH_SIZE", GATEUP_KERNEL)
-    w_k = _pmc_mean_kib(write_dir, "WRITE_SIZE", GATEUP_KERNEL)
+    names, label, _ = GATEUP_KERNELS[TRAFFIC_WORKLOADS[workload][2]]
+    f_k = _pmc_mean_kib(fetch_dir, "FETCH_SIZE", names)
+    w_k = _pmc_mean_kib(write_dir, "WRITE_SIZE", names)
     cf = _pmc_mean_kib(copy_fetch_dir, "FETCH_SIZE", copy, largest=3)
     cw = _pmc_mean_kib(copy_write_dir, "WRITE_SIZE", copy, largest=3)
     nbytes = 1 << 30
     fs, ws = nbytes / (cf * 1024), nbytes / (cw * 1024)
-    rec = {"kernel": "ffn_tiled32_kernel<gate/up + SwiGLU, tiled weights>", "workload": workload,
+    rec = {"kernel": label, "workload": workload,
            "fetch_size_kib_per_launch": round(f_k, 1), "write_size_kib_per_launch": round(w_k, 1),
            "copy_probe": {"bytes_read": nbytes, "bytes_written": nbytes, "fetch_size_kib": round(cf, 1),
                           "write_size_kib": round(cw, 1), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
            "hbm_bytes_per_launch": int(f_k * 1024 * fs + w_k * 1024 * ws),
-           "commands": commands, "source_files": [os.path.relpath(f, ROOT) for f in KERNEL_SOURCES],
-           "source_sha256": kernel_sha()}
+           "commands": commands, "source_files": [os.path.relpath(f, ROOT) for f in kernel_sources(workload)],
+           "source_sha256": kernel_sha(workload)}
     with open(traffic_path(workload), "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
@@ -571,7 +581,8 @@ def prefill_sweep(layout, steps=20, warmup=3):
 def roofline_of(sp, T, w, per, workload):
     t_gu = per["gateup"] * 1e-3
     achieved = w["gateup_flops"] / t_gu / 1e12
-    return {"bound": "mfma", "kernel": "ffn_tiled32_kernel<gate/up + SwiGLU>", "achieved": round(achieved, 2),
+    kernel = GATEUP_KERNELS[TRAFFIC_WORKLOADS[workload][2]][1] if workload in TRAFFIC_WORKLOADS else "gate/up"
+    return {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_record(workload), "alg_bytes_per_launch": gateup_alg_bytes(sp, T, w),
             "avg_launch_us": round(per["gateup"] * 1e3, 2), "alg_flops_per_launch": w["gateup_flops"]}
@@ -580,7 +591,7 @@ def roofline_of(sp, T, w, per, workload):
 def main():
     args = parse()
     if args.traffic_record:
-        spec, T = TRAFFIC_WORKLOADS[args.traffic_workload]
+        spec, T, _ = TRAFFIC_WORKLOADS[args.traffic_workload]
         cmds = [f"rocprofv3 --pmc {c} --kernel-include-regex {rx} --output-format csv -d <out> -o pmc -- "
                 f"python3 bench.py {a}"
                 for rx, a in (("ffn_tiled", f"--profile-layer {spec} --T {T} --steps 3 --warmup 1"),
