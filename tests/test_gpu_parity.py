@@ -235,8 +235,9 @@ def test_side_stream_forward_after_default_stream_churn():
                            v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
 
 
-@pytest.mark.parametrize("name,T", [("olmoe", 4096), ("dsv2_lite_cap", 8192), ("dsv3", 4096), ("dsv3", 16384)])
-def test_256_row_kernels_match_the_128_row_kernels_bitwise(name, T, monkeypatch):
+@pytest.mark.parametrize("name,T,cap", [("olmoe", 4096, None), ("dsv2_lite_cap", 8192, None), ("dsv3", 4096, None),
+                                        ("dsv3", 4096, (5, 4)), ("dsv3", 16384, None)])
+def test_256_row_kernels_match_the_128_row_kernels_bitwise(name, T, cap, monkeypatch):
     """The 256-row tiled kernels (direct global -> LDS loads, eight waves) sum every
     output in the same K order as the 128-row kernels, so the forward must not change
     by a bit whichever the plan takes: MOE_ROWS256_MIN_AVG=0 keeps 128-row items for
@@ -246,6 +247,10 @@ def test_256_row_kernels_match_the_128_row_kernels_bitwise(name, T, monkeypatch)
     shared experts, partly filled 256-row items)."""
     from mixture_experts_layer_13_amd import binding as B
     sp, lay, ml = get_layer(name)
+    if cap is not None:  # the same weights with a capacity (C = 5/4): the two tile maps hold the kept rows
+        capped = B.MoeCfg.from_buffer_copy(ml.cfg)
+        capped.cap_num, capped.cap_den = cap
+        monkeypatch.setattr(ml, "cfg", capped)
     x = S.make_tokens(sp, T, device="cuda")
     c = ml.cfg_for(T)
     runs, sizes = {}, {}
@@ -263,4 +268,6 @@ def test_256_row_kernels_match_the_128_row_kernels_bitwise(name, T, monkeypatch)
     for env in (None, "1"):
         for u, v in zip(runs["0"], runs[env]):
             assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
-                               v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), (name, T, env)
+                               v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), (name, T, cap, env)
+    if cap is not None:
+        assert int(runs["0"][3].sum()) > 0  # some pairs were dropped
