@@ -20,9 +20,14 @@
 // bytes 16 q .. +15 of row n), so a B group is one contiguous KB of memory.
 // Gathered activation rows use a row-major order (unit 4 n + v holds row n),
 // so each group of four lanes reads one contiguous 64-byte run, with the four
-// units of a row XOR-permuted by (n / 2) % 4.  In both images the MFMA
-// fragment reads (lane l: row l % 32, K half l / 32 of a 16-wide slice) hit
-// distinct banks within every group of eight lanes.
+// units of a row XOR-permuted by f(n) = ((n / 2) xor (n / 8)) % 4.  In both
+// images the MFMA fragment reads (lane l: row l % 32, K half l / 32 of a
+// 16-wide slice) hit distinct banks within every group of sixteen lanes (and
+// so of eight): a 128-bit LDS read of gfx950 serves sixteen lanes, 256 bytes,
+// per cycle.  The four rows n = r, r + 4, r + 8, r + 12 share a 256-byte bank
+// window there and f gives them four different units; the earlier f = (n / 2)
+// % 4, distinct only over eight lanes, cost 2.6 bank-conflict cycles per LDS
+// instruction (SQ_LDS_BANK_CONFLICT).
 //
 // Waits.  The compiler tracks LDS written by DMA only coarsely (it drains every
 // outstanding load before the first LDS read of a loop iteration, and a
@@ -122,9 +127,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void ffn_tiled256_kernel(FfnArgs a)
   // Row-major image (activations, and weights in the row layout): lane l loads row l / 4 of the
   // group, so every group of four lanes reads one contiguous 64-byte run (rows spread over the
   // lanes of a quad cost the address and tag units one lookup per lane), and it stores K unit
-  // v = l % 4 of that row's slot, holding logical unit u = v ^ ((row / 2) % 4): the XOR keeps
-  // the fragment reads below (eight lanes, eight rows, one unit) on distinct banks.
-  const int rn = lane >> 2, ru = (lane & 3) ^ ((rn >> 1) & 3);  // row in group, logical 16-byte unit
+  // v = l % 4 of that row's slot, holding logical unit u = v ^ f(row): the XOR keeps the
+  // fragment reads below (sixteen lanes, sixteen rows, one unit) on distinct banks.
+  const int rn = lane >> 2, ru = (lane & 3) ^ (((rn >> 1) ^ (rn >> 3)) & 3);  // row in group, logical 16-byte unit
   const char* asrc[GPW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
@@ -175,10 +180,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void ffn_tiled256_kernel(FfnArgs a)
   };
 
   // ---- fragment reads: lane l takes row n = l % 16 of group 2 m + (l % 32) / 16 of a 32-row tile
-  // and logical unit u = 2 s + l / 32 of slice s: at byte 64 n + 16 (u ^ ((n / 2) % 4)) of the
-  // row-major image, at 256 u + 16 n of the unit-major one.  Slice 1 of the row-major image is
-  // slice 0's offset with bit 5 flipped.
-  const int fn = lane & 15, fh = lane >> 5, fx = (fn >> 1) & 3;
+  // and logical unit u = 2 s + l / 32 of slice s: at byte 64 n + 16 (u ^ f(n)) of the row-major
+  // image, at 256 u + 16 n of the unit-major one.  Slice 1 of the row-major image is slice 0's
+  // offset with bit 5 flipped.
+  const int fn = lane & 15, fh = lane >> 5, fx = ((fn >> 1) ^ (fn >> 3)) & 3;
   const int rofs = ((lane >> 4) & 1) * 1024 + 64 * fn + 16 * ((fx & 2) | (fh ^ (fx & 1)));
   const int uofs = ((lane >> 4) & 1) * 1024 + 256 * fh + 16 * fn;
   const int aofs[2] = {rofs, rofs ^ 32};
