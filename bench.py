@@ -14,7 +14,9 @@ library around that launch on its own stream during the timed steps.
 layer on a seeded 1024-token subset, extrapolated to the workload.  Sub-keys:
 the OLMoE-shaped layer at T=4096 (`olmoe_T4096`), decode sizes as hipGraph
 replays with weights rotated over several copies so the Infinity Cache does
-not serve them (`decode`, `decode_other`, against HBM bandwidth), the other
+not serve them, several layer forwards per graph as a model's captured decode
+step holds its layers, and one per graph beside it (`decode`, `decode_other`,
+against HBM bandwidth), the other
 prefill layers (`prefill`), routing near-ties and INT4 drift (`routing`), and the
 memory-system probe rates the kernels are read against (`memory_probe`).
 
@@ -397,7 +399,11 @@ def clone_weights(lay):
 
 def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name="olmoe_1b7b"):
     """Decode-sized forwards as hipGraph replays over `copies` weight copies (cold in
-    the 256 MB Infinity Cache), reported as achieved HBM bandwidth."""
+    the 256 MB Infinity Cache), reported as achieved HBM bandwidth.  `us_per_layer`: one
+    graph holds 2 * copies forwards (the copies in turn), as a model's captured decode
+    step holds its layers, so no graph launch falls between two layers;
+    `us_per_layer_one_graph_each`: one forward per graph, replayed round-robin, which adds
+    a graph launch to every layer."""
     import torch
 
     import moe_synth as S
@@ -406,6 +412,8 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name
         layers.append(moe_layer(sp, clone_weights(lay), layout))
     res = {}
     s = torch.cuda.Stream()
+    per_graph = 2 * copies
+    stacked = max(1, replays // per_graph)
     for T in Ts:
         x = S.make_tokens(sp, T, device="cuda")
         # the weights, their packing and x were made on the default stream: finish them before
@@ -427,23 +435,41 @@ def decode_sweep(sp, lay, layout, Ts=(1, 8, 32, 64), replays=200, copies=4, name
                 ml.forward(x, *o)
             graphs.append(g)
             outs.append(o)
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs, stream=s):
+            for j in range(per_graph):
+                layers[j % copies].forward(x, *outs[j % copies])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def timed(run, n):
+            e0.record()
+            for i in range(n):
+                run(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1000.0
+
         for i in range(max(len(graphs), replays // 4)):  # untimed replays: steady clocks and queues
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(replays):
-            graphs[i % len(graphs)].replay()
-        e1.record()
+        us_each = timed(lambda i: graphs[i % len(graphs)].replay(), replays) / replays
+        for _ in range(max(2, stacked // 4)):
+            gs.replay()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1000.0 / replays
+        us = timed(lambda i: gs.replay(), stacked) / (stacked * per_graph)
         w = alg_work(sp, T, outs[0][1], outs[0][3])
         gbs = w["bytes"] / (us * 1e-6) / 1e9
+        gbs_each = w["bytes"] / (us_each * 1e-6) / 1e9
         res[f"T{T}"] = {"us_per_layer": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
                         "alg_bytes": w["bytes"], "touched_experts": w["touched"], "hbm_GBps": round(gbs, 1),
-                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "routing": routing_report(layers[0], sp, x)}
-        del graphs
-    return {"layer": name, "method": f"hipGraph replay, {copies} weight copies round-robin, {replays} replays",
+                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "us_per_layer_one_graph_each": round(us_each, 2),
+                        "hbm_frac_one_graph_each": round(gbs_each / HBM_PEAK_GBS, 4),
+                        "routing": routing_report(layers[0], sp, x)}
+        del graphs, gs
+    return {"layer": name,
+            "method": f"hipGraph replays over {copies} weight copies: {per_graph} forwards (the copies in turn) "
+                      f"per graph, {stacked} replays; one_graph_each: one forward per graph, {replays} replays "
+                      "round-robin (a graph launch per layer)",
             "points": res}
 
 
