@@ -28,12 +28,15 @@ SMALL = {
                                                       ffn_shared=256),
     "qwen3_int4": S.SPECS["qwen3_int4"].replace(name="replay_qwen3", cfg_id=23, d=512, ffn=256),
     "dsv3": S.SPECS["dsv3"].replace(name="replay_dsv3", cfg_id=24, d=512, ffn=256, ffn_shared=256),
+    # d >= 4096 with >= 128 rows per expert: the gate/up GEMM on 256-row items, the down GEMM on
+    # its own 128-row tile map
+    "dsv3_wide": S.SPECS["dsv3"].replace(name="replay_dsv3_wide", cfg_id=26, d=4096, ffn=256, ffn_shared=256),
 }
 
 
 @pytest.mark.parametrize("name,T", [("olmoe", 1), ("olmoe", 300), ("olmoe", 5000), ("dsv2_lite_cap", 200),
                                     ("dsv2_lite_cap", 3000), ("qwen3_int4", 32), ("qwen3_int4", 2000),
-                                    ("dsv3", 16), ("dsv3", 9000)])
+                                    ("dsv3", 16), ("dsv3", 9000), ("dsv3_wide", 4096)])
 def test_own_routes_replay_bitwise(name, T):
     sp = SMALL[name]
     lay = S.make_layer(sp, device="cuda")
