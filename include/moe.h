@@ -139,7 +139,12 @@ int64_t moe_capacity(const moe_cfg* cfg);
  * the size depends on the cfg only (R = T*k rows dropless, E*cap with a
  * capacity, never on how the tokens route), so one caller-owned buffer of this
  * size serves every forward of that cfg.  0 on an invalid cfg.  The workspace
- * needs no initialisation; its contents after a call are unspecified. */
+ * needs no initialisation; its contents after a call are unspecified.
+ * The environment variable MOE_ROWS256_MIN_AVG (a test and tuning override of
+ * which GEMMs take 256-row tile items: a positive n from n rows per expert on,
+ * 0 never, unset the built-in rule) is read by every call and changes this
+ * size: size a workspace under the setting it will be used with (a call whose
+ * plan needs more than ws_bytes returns MOE_ERR_WORKSPACE). */
 size_t moe_workspace_bytes(const moe_cfg* cfg);
 
 /* Router: logits, scores, top-k and gates ("MoE: dynamism ...", natural
