@@ -14,7 +14,11 @@
 //    weight slice once, straight from memory into MFMA operands;
 //  - tiled kernels (large M, prefill; ffn_tiled.hip for bf16,
 //    ffn_tiled_int4.hip for INT4 and ffn_tiled_fp8.hip for FP8 weights):
-//    128-row x 256-weight-row blocks, activations through double-buffered LDS.
+//    128-row x 256-weight-row blocks, activations through double-buffered LDS;
+//    for the bf16 gate/up GEMM of long-K layers (d >= 4096, at least 128 rows
+//    per expert) 256-row x 256-weight-row blocks of eight waves fed through an
+//    LDS ring by direct loads (ffn_tiled256.hip), the down GEMM then reading a
+//    tile map of its own with 128-row items.
 // The gate/up kernels fuse the SwiGLU epilogue silu(x Wg) * (x Wu) and write
 // the bf16 (fp32 for fp32 layers) intermediate h; the down kernels write
 // y_rows.  INT4 weights (two's-complement nibbles, bf16 scale per 128-K group)
