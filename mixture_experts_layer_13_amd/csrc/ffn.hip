@@ -138,7 +138,7 @@ hipError_t launch_ffn_gateup(int mode, int act, int wdt, const FfnArgs& a, hipSt
 
 hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStream_t s) {
   if (mode == 0) {
-    const int cpb = stream_channels_per_block(false, wdt);
+    const int cpb = stream_channels_per_block(false, wdt) / stream_down_split(wdt, a.T);
     const int grid = ffn_grid(a, a.d / cpb, a.d / cpb);
     if (grid == 0) return hipSuccess;
     launch_stream_ffn(false, wdt, a, grid, s);

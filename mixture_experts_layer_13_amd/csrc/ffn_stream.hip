@@ -4,6 +4,10 @@
 // memory into MFMA operands, so the weight stream is the whole cost.
 #include "ffn_common.hpp"
 
+#ifndef MOE_DOWN_KSPLIT
+#define MOE_DOWN_KSPLIT 2
+#endif
+
 namespace moe {
 
 // Per weight type: K covered by one 16-byte weight load per lane (KSTEP),
@@ -132,14 +136,22 @@ __device__ __forceinline__ f32x4 int4_group_offset(const u32x4 (&av)[4]) {
 template <typename TW> constexpr int stream_tiles() { return std::is_same<TW, INT4>::value ? 2 : 1; }
 static_assert(Dec<FP8>::AL == 2 && Dec<FP8>::KSTEP == 64, "FP8 steps: 16 bytes per lane, two bf16 operands");
 int stream_channels_per_block(bool gateup, int wdt) { return (gateup ? 16 : 64) * (wdt == kINT4 ? 2 : 1); }
+// waves sharing one channel tile of the streaming down GEMM (each a contiguous part of K):
+// bf16 and FP8 weights from two tokens on; one token keeps whole-K waves, the order of the
+// single-token down + combine launch
+int stream_down_split(int wdt, int T) { return (T > 1 && (wdt == kBF16 || wdt == kFP8)) ? MOE_DOWN_KSPLIT : 1; }
 
 // GATEUP: h[row][n] = silu(A Wg^T) * (A Wu^T); else y[row][n] = A Wd^T.
 // A block owns one item (<= 16 * MT rows of one expert).  A wave covers NT
 // tiles of 16 channels (INT4: two, so one set of activation registers feeds
 // twice the weight bytes in flight; else one).  Gate/up (K = d, large): the
 // four waves split K into quarters for the same channels and add their
-// partial sums in LDS in wave order.  Down (K = ffn): each wave owns its
-// channels over the whole K, so a block covers 4 NT tiles.  Steps are unrolled
+// partial sums in LDS in wave order.  Down (K = ffn): DKS waves share a
+// channel tile, each over a contiguous part of K, added in LDS in wave order, so
+// a block covers 4 / DKS times NT tiles (DKS = 2 for bf16 and FP8 weights from two
+// tokens on, measured on graph replays of one box: FP8 OLMoE-shaped T=64 99.9 ->
+// 97.8 us, T=8 63.0 -> 62.3 us, bf16 within noise; else 1, the whole K per wave,
+// which one token keeps: the order of the single-token down + combine).  Steps are unrolled
 // U deep so each lane keeps U weight loads per matrix and tile in flight.
 // grid: items_max * (N / channels per block) routed blocks, then the shared blocks.
 // PIPE (bf16, one row tile): two register buffers of PU steps, the loads of the next PU steps
@@ -151,14 +163,15 @@ int stream_channels_per_block(bool gateup, int wdt) { return (gateup ? 16 : 64) 
 // 157.1 us), so the host takes it for T = 1 only.  The same buffers in the single-token down +
 // combine launch were slower (DeepSeek-V3-shaped T=1 147.6 -> 148.3 / 150.3 us with 8 / 4 steps
 // per buffer).
-template <typename TW, bool GATEUP, int MT, bool PIPE = false>
+template <typename TW, bool GATEUP, int MT, bool PIPE = false, int DKS = 1>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   using D = Dec<TW>;
   using TA = typename D::TA;
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int NT = stream_tiles<TW>();
-  constexpr int KSPLIT = GATEUP ? 4 : 1;         // waves sharing one channel block
+  constexpr int KSPLIT = GATEUP ? 4 : DKS;       // waves sharing one channel tile (K parts)
   constexpr int CPB = 16 * NT * (4 / KSPLIT);     // channels per block
+  constexpr int NRED = KSPLIT > 1 ? (4 / KSPLIT) * (KSPLIT - 1) : 1;  // partial-sum slots
   // steps whose loads go out together (per step: weights, scales, then activations, so a step's
   // MFMAs can start while later steps land).  Measured on decode layers: INT4 gate/up 1 (its
   // small register footprint keeps 5 blocks per CU), INT4 down 2, bf16 16 / 8 / 4 for items of
@@ -169,7 +182,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   constexpr int AL = D::AL, KSTEP = D::KSTEP;
   constexpr int PU = 4;  // PIPE: steps per register buffer
   static_assert(!PIPE || (std::is_same<TW, bf16>::value && MT == 1), "PIPE: bf16, one row tile");
-  __shared__ f32x4 red[KSPLIT > 1 ? 3 : 1][NM][NT][MT][64];
+  __shared__ f32x4 red[NRED][NM][NT][MT][64];
   const int lane = lane_id(), w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
 
   const int Nr = GATEUP ? a.F : a.d;
@@ -190,8 +203,8 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
     mrows = min(a.bm, a.T - row0);
   }
   const int nmt = (mrows + 15) / 16;
-  const int kpart = KSPLIT > 1 ? w : 0;
-  const int n0 = nb * CPB + (KSPLIT > 1 ? 0 : 16 * NT * w) + c;  // channel of tile j: n0 + 16 j
+  const int kpart = w % KSPLIT, tgrp = w / KSPLIT;  // K part, channel tile group of this wave
+  const int n0 = nb * CPB + 16 * NT * tgrp + c;     // channel of tile j: n0 + 16 j
 
   const int K = GATEUP ? a.d : (shared ? a.FS : a.F);  // K of one segment
   const int nseg = (!GATEUP && shared) ? a.S : 1;
@@ -349,26 +362,27 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
   }
 
   if (KSPLIT > 1) {
-    // add the K slices (fixed order) in wave 0
-    if (w > 0) {
+    // add the K parts of each channel tile (fixed order) in its part-0 wave
+    if (kpart > 0) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            if (mt < nmt) red[w - 1][m][j][mt][lane] = acc[m][j][mt];
+            if (mt < nmt) red[tgrp * (KSPLIT - 1) + kpart - 1][m][j][mt][lane] = acc[m][j][mt];
     }
     __syncthreads();
-    if (w != 0) return;
+    if (kpart != 0) return;
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int p = 1; p < KSPLIT; ++p)
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          if (mt < nmt)
-            acc[m][j][mt] = ((acc[m][j][mt] + red[0][m][j][mt][lane]) + red[1][m][j][mt][lane]) + red[2][m][j][mt][lane];
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (mt < nmt) acc[m][j][mt] = acc[m][j][mt] + red[tgrp * (KSPLIT - 1) + p - 1][m][j][mt][lane];
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -512,8 +526,12 @@ static void launch_stream(int wdt, const FfnArgs& a, int grid, hipStream_t s) {
     hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, 1, true>), dim3(grid), dim3(256), 0, s, a);
   else if (wdt == kF32)
     hipLaunchKernelGGL((ffn_stream_kernel<float, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+  else if (wdt == kBF16 && !GATEUP && stream_down_split(wdt, a.T) == 2)
+    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT, false, 2>), dim3(grid), dim3(256), 0, s, a);
   else if (wdt == kBF16)
     hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+  else if (wdt == kFP8 && !GATEUP && stream_down_split(wdt, a.T) == 2)
+    hipLaunchKernelGGL((ffn_stream_kernel<FP8, GATEUP, MT, false, 2>), dim3(grid), dim3(256), 0, s, a);
   else if (wdt == kFP8)
     hipLaunchKernelGGL((ffn_stream_kernel<FP8, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
   else
