@@ -59,7 +59,7 @@ hipError_t launch_pack_tiled(const void* src, void* dst, int64_t rows, int64_t r
 // loads and stores (measured, one box: DeepSeek-V3-shaped T=16384 441-449 -> 385-386 us,
 // DeepSeek-V2-Lite-shaped T=8192 50 -> 45 us, OLMoE-shaped T=4096 29.1 -> 27.5-28.0 us;
 // the decode layers unchanged).
-template <typename TA>
+template <typename TA, bool PRE>
 __global__ __launch_bounds__(1024) void combine_kernel(const TA* __restrict__ y, const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ gw, const TA* __restrict__ ysh,
                                                       TA* __restrict__ out, int T, int d, int k, int R) {
@@ -70,28 +70,45 @@ __global__ __launch_bounds__(1024) void combine_kernel(const TA* __restrict__ y,
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int r = slot_row[(size_t)t * k + j];
-    if ((unsigned)r >= (unsigned)R) continue;
-    const float gj = gw[(size_t)t * k + j];
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + (size_t)r * d + c0));
+  auto load = [&](const TA* row) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c0)); };
+  // acc += g * row (g = 1: the shared experts' row, added, not multiplied)
+  auto add = [&](float g, u32x4 v, bool scaled) {
     if constexpr (sizeof(TA) == 2) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(gj, bf16_bits_to_f32((v[i / 2] >> (16 * (i & 1))) & 0xFFFFu), acc[i]);
+      for (int i = 0; i < 8; ++i) {
+        const float x = bf16_bits_to_f32((v[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+        acc[i] = scaled ? fmaf(g, x, acc[i]) : acc[i] + x;
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(gj, __uint_as_float(v[i]), acc[i]);
+      for (int i = 0; i < 4; ++i) acc[i] = scaled ? fmaf(g, __uint_as_float(v[i]), acc[i]) : acc[i] + __uint_as_float(v[i]);
     }
-  }
-  if (ysh) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ysh + (size_t)t * d + c0));
-    if constexpr (sizeof(TA) == 2) {
+  };
+  if constexpr (PRE) {
+    // every load first (slot rows and gates, then the up to k + 1 rows), then the sums in order
+    int rr[kMaxK];
+    float gg[kMaxK];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += bf16_bits_to_f32((v[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(v[i]);
+    for (int j = 0; j < kMaxK; ++j) {
+      rr[j] = j < k ? slot_row[(size_t)t * k + j] : -1;
+      gg[j] = j < k ? gw[(size_t)t * k + j] : 0.f;
     }
+    u32x4 vv[kMaxK], vs = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if ((unsigned)rr[j] < (unsigned)R) vv[j] = load(y + (size_t)rr[j] * d);
+    if (ysh) vs = load(ysh + (size_t)t * d);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if ((unsigned)rr[j] < (unsigned)R) add(gg[j], vv[j], true);
+    if (ysh) add(1.f, vs, false);
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int r = slot_row[(size_t)t * k + j];
+      if ((unsigned)r >= (unsigned)R) continue;
+      add(gw[(size_t)t * k + j], load(y + (size_t)r * d), true);
+    }
+    if (ysh) add(1.f, load(ysh + (size_t)t * d), false);
   }
   u32x4 o;
   if constexpr (sizeof(TA) == 2) {
@@ -103,6 +120,9 @@ __global__ __launch_bounds__(1024) void combine_kernel(const TA* __restrict__ y,
   }
   __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (size_t)t * d + c0));
 }
+
+// tokens up to which the combine issues every load of a thread at once (the decode sizes)
+constexpr int kCombinePrefetchMaxT = 64;
 
 // ------------------------------------------------------------------ host launchers
 static int ffn_grid(const FfnArgs& a, int nt_routed, int nt_shared) {
@@ -164,12 +184,27 @@ hipError_t launch_combine(int act, const void* y, const int32_t* slot_row, const
   const int tpb = per <= 1024 ? per : 256;
   dim3 grid(T, (d + tpb * V - 1) / (tpb * V));
   if (T == 0) return hipSuccess;
-  if (act == kF32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(tpb), 0, s, (const float*)y, slot_row, w, (const float*)ysh,
-                       (float*)out, T, d, k, R);
-  else
-    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(tpb), 0, s, (const bf16*)y, slot_row, w, (const bf16*)ysh,
-                       (bf16*)out, T, d, k, R);
+  // few tokens: every load of a thread issued at once (latency-bound); many: one row at a time,
+  // which keeps more blocks in flight (measured, graph replays with several layers per graph /
+  // eager, two boxes: OLMoE-shaped T=8 87.1 -> 84.0 and 87.3 -> 85.4 us per layer, T=32 129.8 ->
+  // 128.1 and 131.0 -> 130.0, T=64 148.9 -> 147.2 and 149.7 -> 148.9, Qwen3 INT4-shaped T=32
+  // 82.8 -> 81.0; DeepSeek-V3-shaped T=16384 combine 385 -> 417 us with it)
+  const bool pre = T <= kCombinePrefetchMaxT;
+  if (act == kF32) {
+    if (pre)
+      hipLaunchKernelGGL((combine_kernel<float, true>), grid, dim3(tpb), 0, s, (const float*)y, slot_row, w,
+                         (const float*)ysh, (float*)out, T, d, k, R);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, false>), grid, dim3(tpb), 0, s, (const float*)y, slot_row, w,
+                         (const float*)ysh, (float*)out, T, d, k, R);
+  } else {
+    if (pre)
+      hipLaunchKernelGGL((combine_kernel<bf16, true>), grid, dim3(tpb), 0, s, (const bf16*)y, slot_row, w,
+                         (const bf16*)ysh, (bf16*)out, T, d, k, R);
+    else
+      hipLaunchKernelGGL((combine_kernel<bf16, false>), grid, dim3(tpb), 0, s, (const bf16*)y, slot_row, w,
+                         (const bf16*)ysh, (bf16*)out, T, d, k, R);
+  }
   return hipGetLastError();
 }
 
