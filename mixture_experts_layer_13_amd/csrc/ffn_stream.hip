@@ -4,10 +4,6 @@
 // memory into MFMA operands, so the weight stream is the whole cost.
 #include "ffn_common.hpp"
 
-#ifndef MOE_DOWN_KSPLIT
-#define MOE_DOWN_KSPLIT 2
-#endif
-
 namespace moe {
 
 // Per weight type: K covered by one 16-byte weight load per lane (KSTEP),
@@ -139,7 +135,7 @@ int stream_channels_per_block(bool gateup, int wdt) { return (gateup ? 16 : 64) 
 // waves sharing one channel tile of the streaming down GEMM (each a contiguous part of K):
 // bf16 and FP8 weights from two tokens on; one token keeps whole-K waves, the order of the
 // single-token down + combine launch
-int stream_down_split(int wdt, int T) { return (T > 1 && (wdt == kBF16 || wdt == kFP8)) ? MOE_DOWN_KSPLIT : 1; }
+int stream_down_split(int wdt, int T) { return (T > 1 && (wdt == kBF16 || wdt == kFP8)) ? 2 : 1; }
 
 // GATEUP: h[row][n] = silu(A Wg^T) * (A Wu^T); else y[row][n] = A Wd^T.
 // A block owns one item (<= 16 * MT rows of one expert).  A wave covers NT
