@@ -44,7 +44,13 @@
 // same channels; down: output columns n0 + 64 j .. +63) as 4 x 2 tiles of 32 x
 // 32 (v_mfma_f32_32x32x16_bf16, 128 fp32 accumulators per lane).  Every output
 // element sums the same products in the same K order as the 128-row kernel, so
-// the two give identical results, bit for bit.
+// the two give identical results, bit for bit.  The main loop is instantiated
+// for 0-4 of a wave's 32-row tiles holding rows of the item: the idle tiles of
+// a partly filled item cost no MFMAs and no LDS fragment reads (their rows are
+// still fetched, as copies of the item's last row, so that every wave issues
+// the same loads per K step and the waits keep their exact counts).  The host
+// turns this off where an expert's items share weight slabs: a skipping item
+// runs ahead of the others over the same slab and their L2 hits turn to misses.
 #include "ffn_common.hpp"
 
 namespace moe {
@@ -99,7 +105,8 @@ __device__ __forceinline__ void block_barrier() {
 
 }  // namespace
 
-template <bool GATEUP, bool TILED>
+// SKIP: skip the idle 32-row tiles (else a wave computes all four of its tiles or none)
+template <bool GATEUP, bool TILED, bool SKIP>
 __global__ __launch_bounds__(64 * kWaves, 1) void ffn_tiled256_kernel(FfnArgs a) {
   constexpr int NW = kWaves;
   constexpr int NT = GATEUP ? 128 : 256;  // output channels (gate/up) or columns (down) per block
@@ -193,7 +200,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void ffn_tiled256_kernel(FfnArgs a)
   for (int m = 0; m < 4; ++m) ga[m] = 8 * wi + 2 * m;
 #pragma unroll
   for (int n = 0; n < NB; ++n) gb[n] = GATEUP ? ((n / GT) * 8 + 2 * GT * wj + 2 * (n % GT)) : (2 * NB * wj + 2 * n);
-  const bool active = 128 * wi < mrows;  // a wave whose rows lie past the item's end only moves data
+  // 32-row tiles of this wave that it computes: those holding rows of the item, or without
+  // SKIP all four unless none does (0: the wave only moves data)
+  const int ma = SKIP ? min(max((mrows - 128 * wi + 31) / 32, 0), 4) : (128 * wi < mrows ? 4 : 0);
+  const bool active = ma > 0;
 
   f32x16 acc[4][NB];
 #pragma unroll
@@ -201,46 +211,52 @@ __global__ __launch_bounds__(64 * kWaves, 1) void ffn_tiled256_kernel(FfnArgs a)
 #pragma unroll
     for (int n = 0; n < NB; ++n) acc[m][n] = f32x16{};
   u32x4 fa[2][4], fb[2][NB];
-  auto rd = [&](int kt, int s, u32x4 (&A)[4], u32x4 (&B)[NB]) {
+  // MA: the wave's row tiles that hold rows (compile-time), the first MA of its four
+  auto rd = [&](auto ma_tag, int kt, int s, u32x4 (&A)[4], u32x4 (&B)[NB]) {
+    constexpr int MA = decltype(ma_tag)::value;
     const char* slot = smem + (kt % kRingP) * kSlot;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) A[m] = *reinterpret_cast<const u32x4*>(slot + aofs[s] + ga[m] * 1024);
+    for (int m = 0; m < MA; ++m) A[m] = *reinterpret_cast<const u32x4*>(slot + aofs[s] + ga[m] * 1024);
 #pragma unroll
     for (int n = 0; n < NB; ++n) B[n] = *reinterpret_cast<const u32x4*>(slot + kSlotB + bofs[s] + gb[n] * 1024);
   };
-  auto mma = [&](const u32x4 (&A)[4], const u32x4 (&B)[NB]) {
+  auto mma = [&](auto ma_tag, const u32x4 (&A)[4], const u32x4 (&B)[NB]) {
+    constexpr int MA = decltype(ma_tag)::value;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MA; ++m)
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[m][n] = mma32_bf16(A[m], B[n], acc[m][n]);
   };
-  // the 4 + NB LDS reads of one slice go out between the first MFMAs of the other
+  // the MA + NB LDS reads of one slice go out between the first MFMAs of the other
   // (pinned: left alone, the scheduler bunches them)
-  auto pin_slice = [&]() {
+  auto pin_slice = [&](auto ma_tag) {
+    constexpr int MA = decltype(ma_tag)::value;
+    constexpr int R = MA + NB, M = MA * NB, P = R < M ? R : M;
 #pragma unroll
-    for (int i = 0; i < 4 + NB; ++i) {
+    for (int i = 0; i < P; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 3 * NB - 4, 0);
+    if constexpr (M > P) __builtin_amdgcn_sched_group_barrier(0x008, M - P, 0);
+    if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
   };
 
-  // Main loop.  ACT: this wave has rows to compute (else it only moves data and meets the barriers).
-  auto run = [&](auto act_tag) {
-    constexpr bool ACT = decltype(act_tag)::value;
+  // Main loop.  MA = 0: the wave only moves data and meets the barriers.
+  auto run = [&](auto ma_tag) {
+    constexpr bool ACT = decltype(ma_tag)::value > 0;
     const int pro = min(kRingP, nkt);
     for (int kt = 0; kt < pro; ++kt) issue(kt);
     wait_steps<kDma>(pro - 1);  // K step 0 landed; the others stay in flight
     block_barrier();
-    if (ACT) rd(0, 0, fa[0], fb[0]);
+    if (ACT) rd(ma_tag, 0, 0, fa[0], fb[0]);
     int kt = 0;
     // steady state: K step kt + 1 must have landed at the barrier, kt + 2 .. kt + P - 1 stay in
     // flight, and K step kt + P goes into the slot of kt (every wave has read it by then)
     for (; kt + kRingP < nkt; ++kt) {
       if (ACT) {
-        rd(kt, 1, fa[1], fb[1]);
-        mma(fa[0], fb[0]);
-        pin_slice();
+        rd(ma_tag, kt, 1, fa[1], fb[1]);
+        mma(ma_tag, fa[0], fb[0]);
+        pin_slice(ma_tag);
         mem_fence_compiler();
         wait_lgkm0();
       }
@@ -248,16 +264,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void ffn_tiled256_kernel(FfnArgs a)
       block_barrier();
       issue(kt + kRingP);
       if (ACT) {
-        rd(kt + 1, 0, fa[0], fb[0]);
-        mma(fa[1], fb[1]);
-        pin_slice();
+        rd(ma_tag, kt + 1, 0, fa[0], fb[0]);
+        mma(ma_tag, fa[1], fb[1]);
+        pin_slice(ma_tag);
       }
     }
     // the last (at most P) K steps: everything is issued, the waits shrink
     for (; kt < nkt; ++kt) {
       if (ACT) {
-        rd(kt, 1, fa[1], fb[1]);
-        mma(fa[0], fb[0]);
+        rd(ma_tag, kt, 1, fa[1], fb[1]);
+        mma(ma_tag, fa[0], fb[0]);
         mem_fence_compiler();
         wait_lgkm0();
       }
@@ -265,13 +281,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void ffn_tiled256_kernel(FfnArgs a)
         const int later = nkt - 2 - kt;  // K steps issued after kt + 1
         wait_steps<kDma>(min(later, kRingP - 2));
         block_barrier();
-        if (ACT) rd(kt + 1, 0, fa[0], fb[0]);
+        if (ACT) rd(ma_tag, kt + 1, 0, fa[0], fb[0]);
       }
-      if (ACT) mma(fa[1], fb[1]);
+      if (ACT) mma(ma_tag, fa[1], fb[1]);
     }
   };
-  if (active) run(std::true_type{});
-  else run(std::false_type{});
+  // (the instantiations for 1-3 tiles exist only with SKIP: beside them the compiler schedules
+  // the four-tile loop less well, DeepSeek-V3-shaped gate/up at T=16384 1.5% slower)
+  if (ma == 4) run(std::integral_constant<int, 4>{});
+  else if (SKIP && ma == 3) run(std::integral_constant<int, SKIP ? 3 : 4>{});
+  else if (SKIP && ma == 2) run(std::integral_constant<int, SKIP ? 2 : 4>{});
+  else if (SKIP && ma == 1) run(std::integral_constant<int, SKIP ? 1 : 4>{});
+  else run(std::integral_constant<int, 0>{});
 
   // ---- epilogue through LDS: staged 16-byte row chunks
   wait_vm<0>();
@@ -335,14 +356,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void ffn_tiled256_kernel(FfnArgs a)
   }
 }
 
-void launch_tiled256_bf16(bool gateup, const FfnArgs& a, int grid, hipStream_t s) {
+template <bool GATEUP, bool TILED>
+static void launch256(const FfnArgs& a, int grid, hipStream_t s) {
   const dim3 blk(64 * kWaves);
+  if (GATEUP ? a.rowskip_gu : a.rowskip_dn) hipLaunchKernelGGL((ffn_tiled256_kernel<GATEUP, TILED, true>), dim3(grid), blk, 0, s, a);
+  else hipLaunchKernelGGL((ffn_tiled256_kernel<GATEUP, TILED, false>), dim3(grid), blk, 0, s, a);
+}
+
+void launch_tiled256_bf16(bool gateup, const FfnArgs& a, int grid, hipStream_t s) {
   if (gateup) {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled256_kernel<true, true>), dim3(grid), blk, 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled256_kernel<true, false>), dim3(grid), blk, 0, s, a);
+    if (a.wtiled) launch256<true, true>(a, grid, s);
+    else launch256<true, false>(a, grid, s);
   } else {
-    if (a.wtiled) hipLaunchKernelGGL((ffn_tiled256_kernel<false, true>), dim3(grid), blk, 0, s, a);
-    else hipLaunchKernelGGL((ffn_tiled256_kernel<false, false>), dim3(grid), blk, 0, s, a);
+    if (a.wtiled) launch256<false, true>(a, grid, s);
+    else launch256<false, false>(a, grid, s);
   }
 }
 
