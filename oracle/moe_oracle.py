@@ -21,8 +21,9 @@ Sources (the pages this follows):
              max-subtract-expsum softmax before top-k) and "Sub-study 2"
              (route replay; the replay of a model's own routes must return the
              baseline exactly).
-  [MoE-inf]  "MoE at the inference level ..." -- Workarounds (int4 expert
-             weights, auxiliary-loss-free bias term).
+  [MoE-inf]  "MoE at the inference level ..." -- Workarounds (int4 / fp8
+             expert weights, auxiliary-loss-free bias term) and Fields
+             (weight_dtype).
   [MoE-res]  "MoE Research", section 2 (shared always-on experts;
              loss-free balancing bias used for selection; node-limited
              routing: a token's experts come from at most M nodes) and
@@ -97,6 +98,65 @@ def fp8_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
 def fp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """w[n, k] = fp8(code[n, k]) * s[n] with one fp32 scale per output channel, exactly."""
     return fp8_e4m3_to_f64(codes) * np.asarray(scales, np.float64)[..., None]
+
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """float64 -> the nearest bf16 value (8 significant bits, ties to even), as float64.
+
+    v = m 2^e with 0.5 <= |m| < 1; m 2^8 rounded half-to-even is the bf16
+    significand.  (Normal range only: the values here are far from bf16's
+    subnormals and its overflow threshold.)"""
+    m, e = np.frexp(np.asarray(v, np.float64))
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+E4M3_MAX = 448.0
+
+
+def round_to_e4m3(v: np.ndarray) -> np.ndarray:
+    """float64 -> the nearest OCP E4M3 ("fn") value, ties to the even significand, as float64.
+
+    In the binade [2^b, 2^(b+1)) with b >= -6 the values are spaced 2^(b-3);
+    below 2^-6 (subnormals) they are spaced 2^-9.  Magnitudes past the largest
+    finite value 448 are held at 448 (reading: the format has no infinity and
+    the quantiser below never produces more than 448 (1 + 2^-23))."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    b = np.clip(ex - 1, -6, 8)              # binade exponent (frexp's exponent is one above it)
+    step = np.exp2(b - 3.0)
+    q = np.minimum(np.rint(a / step) * step, E4M3_MAX)
+    return np.where(v < 0, -q, q)
+
+
+def quantize_rows_e4m3(v: np.ndarray):
+    """Per-row symmetric E4M3 quantisation of activations, with fp32 scale arithmetic.
+
+    Reading of "fp8 expert weights" run on an FP8 matrix unit ([MoE-inf]
+    workarounds and Fields, weight_dtype): the matrix unit takes both operands
+    in FP8, so each row of a GEMM's activation operand (a token's x, or its
+    SwiGLU output h) is quantised on its own.  With v the row's values (exact
+    fp32 values: bf16 here) and amax = max |v|, in IEEE fp32:
+        inv = 448 / amax,  code_i = E4M3(v_i * inv),  scale = amax / 448;
+    the row stands for code_i * scale.  An all-zero row has codes 0, scale 0.
+    Returns (codes as float64 values [.., n], scale float64 [..])."""
+    v32 = np.asarray(v, np.float64).astype(np.float32)
+    if not np.array_equal(v32.astype(np.float64), np.asarray(v, np.float64)):
+        raise ValueError("quantize_rows_e4m3 takes fp32-representable values")
+    amax = np.abs(v32).max(axis=-1)
+    nz = amax > 0
+    safe = np.where(nz, amax, np.float32(1))
+    inv = np.where(nz, np.float32(448.0) / safe, np.float32(0)).astype(np.float32)
+    prod = (v32 * inv[..., None]).astype(np.float32)
+    codes = round_to_e4m3(prod.astype(np.float64))
+    scale = np.where(nz, safe / np.float32(448.0), np.float32(0)).astype(np.float32)
+    return codes, scale.astype(np.float64)
+
+
+def dequant_rows_e4m3(v: np.ndarray) -> np.ndarray:
+    """The row as the FP8 matrix unit sees it: code_i * scale (exact in float64)."""
+    codes, scale = quantize_rows_e4m3(v)
+    return codes * scale[..., None]
 
 
 # --------------------------------------------------------------------------
@@ -256,6 +316,17 @@ def swiglu_ffn(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.n
     return (silu(g) * u) @ np.asarray(w_down, np.float64).T
 
 
+def swiglu_ffn_a8(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """One expert with FP8 activations on both GEMMs (weights as given, e.g. fp8 * channel scale):
+    x rows quantised per row (quantize_rows_e4m3) before x W_gate and x W_up; the SwiGLU output
+    rounded to bf16 (the intermediate's storage type) and quantised per row before the down GEMM."""
+    xa = dequant_rows_e4m3(x)
+    g = xa @ np.asarray(w_gate, np.float64).T
+    u = xa @ np.asarray(w_up, np.float64).T
+    h = round_to_bf16(silu(g) * u)
+    return dequant_rows_e4m3(h) @ np.asarray(w_down, np.float64).T
+
+
 # An expert provider maps an expert number to its float64 (w_gate, w_up, w_down).
 ExpertFn = Callable[[int], Sequence[np.ndarray]]
 
@@ -265,7 +336,7 @@ def moe_layer(x: np.ndarray, w_router: np.ndarray, experts: ExpertFn, E: int, k:
               logit_bias: Optional[np.ndarray] = None, select_bias: Optional[np.ndarray] = None,
               capacity: Optional[tuple] = None, shared: Optional[ExpertFn] = None, n_shared: int = 0,
               ffn_rows: Optional[np.ndarray] = None, routes: Optional[tuple] = None,
-              groups: Optional[tuple] = None) -> dict:
+              groups: Optional[tuple] = None, act_fp8: bool = False) -> dict:
     """The whole layer, step by step.
 
     1. logits = x W_r (+ skew bias); 2. scores (softmax, or sigmoid);
@@ -280,6 +351,9 @@ def moe_layer(x: np.ndarray, w_router: np.ndarray, experts: ExpertFn, E: int, k:
     ffn_rows: optional sorted token subset for steps 7-8 (routing always runs
     over every token); out rows outside the subset are NaN.
     routes: optional (idx, gates) that replace steps 2-5 (route replay).
+    act_fp8: the expert GEMMs take FP8 activations (swiglu_ffn_a8); the shared
+    experts' SwiGLU outputs are quantised as one row per token over all of them
+    (their down GEMMs form one sum over the concatenated intermediate).
     """
     x = np.asarray(x, np.float64)
     T = x.shape[0]
@@ -316,11 +390,20 @@ def moe_layer(x: np.ndarray, w_router: np.ndarray, experts: ExpertFn, E: int, k:
         if sel_t.size == 0:
             continue
         wg, wu, wd = experts(e)
-        y = swiglu_ffn(x[sel_t], wg, wu, wd)
+        y = (swiglu_ffn_a8 if act_fp8 else swiglu_ffn)(x[sel_t], wg, wu, wd)
         np.add.at(out, sel_t, gates[sel_t, sel_j][:, None] * y)
-    for s in range(n_shared):
-        wg, wu, wd = shared(s)
-        out[rows] += swiglu_ffn(x[rows], wg, wu, wd)
+    if act_fp8 and n_shared > 0:
+        xa = dequant_rows_e4m3(x[rows])
+        ws = [shared(s) for s in range(n_shared)]
+        h = np.concatenate([round_to_bf16(silu(xa @ np.asarray(wg, np.float64).T) * (xa @ np.asarray(wu, np.float64).T))
+                            for wg, wu, _ in ws], axis=1)
+        ha = dequant_rows_e4m3(h)
+        wd_cat = np.concatenate([np.asarray(wd, np.float64) for _, _, wd in ws], axis=1)
+        out[rows] += ha @ wd_cat.T
+    else:
+        for s in range(n_shared):
+            wg, wu, wd = shared(s)
+            out[rows] += swiglu_ffn(x[rows], wg, wu, wd)
     return dict(out=out, logits=logits, scores=scores, key=key, idx=idx, gates=gates,
                 margin=margin, group_margin=group_margin, cap=cap, **asg)
 

@@ -495,3 +495,147 @@ def test_logit_bias_steers_selection_and_gates():
     L = x @ wr.T + bias
     expect = np.exp(L[:, 3]) / np.exp(L).sum(1)
     assert np.allclose(res["gates"][:, 0], expect, rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# FP8 activations: bf16 rounding, E4M3 rounding, per-row quantisation
+# --------------------------------------------------------------------------
+def test_bf16_rounding_matches_library():
+    """round_to_bf16 against torch's float32 -> bfloat16 cast (round to nearest even, a
+    library routine) on fp32 values of every magnitude; bf16 values map to themselves;
+    exact midpoints go to the even significand."""
+    import torch
+    v = (rng.normal(size=20000) * np.exp2(rng.integers(-40, 40, size=20000))).astype(np.float32)
+    lib = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_to_bf16(v.astype(np.float64)), lib)
+    b = O.bf16_to_f64(np.arange(0x0080, 0x7F00, 7, dtype=np.uint16))
+    assert np.array_equal(O.round_to_bf16(b), b)
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties to even -> 1; 1 + 3 2^-8 -> 1 + 2^-6
+    assert O.round_to_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    assert O.round_to_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+    assert O.round_to_bf16(np.array([-(1 + 2.0 ** -8)]))[0] == -1.0
+
+
+def _e4m3_finite_values():
+    v = O.fp8_e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    return v[~np.isnan(v)]
+
+
+def test_e4m3_rounding_round_trips_every_value_and_ties_to_even():
+    vals = _e4m3_finite_values()
+    assert np.array_equal(O.round_to_e4m3(vals), vals)
+    pos = np.unique(vals[vals >= 0])
+    codes = {float(O.fp8_e4m3_to_f64(np.uint8(c))): c for c in range(0x7F)}
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = (a + b) / 2
+        even = a if codes[float(a)] % 2 == 0 else b   # the code with mantissa bit 0
+        assert O.round_to_e4m3(np.array([mid]))[0] == even
+        assert O.round_to_e4m3(np.array([-mid]))[0] == -even
+        # just off the midpoint: the nearer neighbour
+        assert O.round_to_e4m3(np.array([mid - (b - a) / 64]))[0] == a
+        assert O.round_to_e4m3(np.array([mid + (b - a) / 64]))[0] == b
+    # beyond the largest finite value: held at 448
+    assert np.array_equal(O.round_to_e4m3(np.array([448.0 * (1 + 2.0 ** -23), 463.9, 1e6, -500.0])),
+                          np.array([448.0, 448.0, 448.0, -448.0]))
+
+
+def test_e4m3_rounding_matches_library():
+    """Against torch's float32 -> float8_e4m3fn cast (round to nearest even) over the whole
+    finite range, subnormals included."""
+    import torch
+    v = (rng.uniform(-1, 1, size=50000) * np.exp2(rng.uniform(-12, 8.8, size=50000))).astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    lib = torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(O.round_to_e4m3(v.astype(np.float64)), lib)
+
+
+def test_row_quantisation_exact_cases_and_bounds():
+    vals = _e4m3_finite_values()
+    # a row of E4M3 values times 2^j holding +-448 2^j: codes are the values, scale is 2^j
+    for j in (-20, -3, 0, 5):
+        row = rng.choice(vals, size=(3, 200))
+        row[:, 7] = 448.0
+        row[1, 9] = -448.0
+        codes, scale = O.quantize_rows_e4m3(row * 2.0 ** j)
+        assert np.array_equal(codes, row) and np.array_equal(scale, np.full(3, 2.0 ** j))
+    # an all-zero row: codes 0, scale 0
+    codes, scale = O.quantize_rows_e4m3(np.zeros((2, 64)))
+    assert not codes.any() and not scale.any()
+    # random bf16 rows: the largest magnitude always lands on +-448; every element within half an
+    # E4M3 step (2^-4 of its magnitude, or 2^-10 in the subnormal range) times the fp32 scale
+    bits = rng.integers(0, 0x7F00, size=(50, 300)) | (rng.integers(0, 2, size=(50, 300)) << 15)
+    x = O.bf16_to_f64(bits.astype(np.uint16))   # every finite bf16 magnitude, both signs
+    codes, scale = O.quantize_rows_e4m3(x)
+    top = np.abs(x).argmax(axis=1)
+    assert np.array_equal(np.abs(codes[np.arange(50), top]), np.full(50, 448.0))
+    assert np.all(np.abs(codes) <= 448.0)
+    err = np.abs(codes * scale[:, None] - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None]) * (1 + 2.0 ** -20) + 1e-300
+    assert np.all(err <= bound)
+    # the scale is amax / 448 in fp32
+    assert np.array_equal(scale, (np.abs(x).max(axis=1).astype(np.float32) / np.float32(448)).astype(np.float64))
+
+
+def test_a8_ffn_in_the_code_domain():
+    """swiglu_ffn_a8 against the same layer computed from the integer codes: with every E4M3
+    value times 2^9 an integer, a GEMM of quantised rows is the exact integer sum of code
+    products, times the row scale and the weight's own scale, times 2^-18."""
+    T, d, F = 5, 16, 12
+    vals = _e4m3_finite_values()
+    wq = [rng.choice(vals, size=(F, d)), rng.choice(vals, size=(F, d)), rng.choice(vals, size=(d, F))]
+    ws = [rng.uniform(0.5, 2, size=F) / 448, rng.uniform(0.5, 2, size=F) / 448, rng.uniform(0.5, 2, size=d) / 448]
+    W = [q * s[:, None] for q, s in zip(wq, ws)]
+    x = O.bf16_to_f64(rng.integers(0x3C00, 0x4100, size=(T, d)).astype(np.uint16) ^ (rng.integers(0, 2, size=(T, d)) << 15).astype(np.uint16))
+    got = O.swiglu_ffn_a8(x, *W)
+
+    def gemm_codes(rows, wi):
+        codes, scale = O.quantize_rows_e4m3(rows)
+        ci = (codes * 512).astype(np.int64)
+        wi_int = (wq[wi] * 512).astype(np.int64)
+        out = np.empty((rows.shape[0], wi_int.shape[0]))
+        for t in range(rows.shape[0]):
+            for n in range(wi_int.shape[0]):
+                acc = sum(int(ci[t, k]) * int(wi_int[n, k]) for k in range(ci.shape[1]))
+                out[t, n] = acc * 2.0 ** -18 * scale[t] * ws[wi][n]
+        return out
+    g, u = gemm_codes(x, 0), gemm_codes(x, 1)
+    h = O.round_to_bf16(g / (1 + np.exp(-g)) * u)
+    ref = gemm_codes(h, 2)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_a8_layer_structure_and_size_of_the_quantisation_error():
+    """E = 1, k = 1 and a shared expert: the FP8-activation layer is swiglu_ffn_a8 plus the
+    shared expert's own FP8-activation FFN; against the bf16-activation layer it differs, by
+    an amount of the order of E4M3's relative precision (2^-4 per element at most)."""
+    T, d, F = 64, 128, 96
+    x = O.round_to_bf16(rng.normal(size=(T, d)))
+    mk = lambda *s: O.round_to_bf16(rng.normal(size=s) / math.sqrt(s[-1]))
+    ex = [(mk(F, d), mk(F, d), mk(d, F))]
+    sh = [(mk(F, d), mk(F, d), mk(d, F))]
+    kw = dict(logit_bias=np.array([0.1]), shared=_experts_fn(sh), n_shared=1)
+    a8 = O.moe_layer(x, rng.normal(size=(1, d)), _experts_fn(ex), 1, 1, act_fp8=True, **kw)["out"]
+    ref = O.swiglu_ffn_a8(x, *ex[0]) + O.swiglu_ffn_a8(x, *sh[0])
+    assert np.allclose(a8, ref, rtol=1e-13, atol=1e-13)
+    plain = O.moe_layer(x, rng.normal(size=(1, d)), _experts_fn(ex), 1, 1, **kw)["out"]
+    rel = np.abs(a8 - plain).max(axis=1) / np.abs(plain).max(axis=1)
+    assert 1e-3 < np.median(rel) < 6e-2 and rel.max() < 0.15
+
+
+def test_a8_shared_experts_quantise_one_concatenated_row():
+    """Two shared experts share one quantised row per token: a second expert of zeros changes
+    nothing (its h is 0, the row maximum is the first's), and a second copy of the first
+    doubles the shared output exactly (the same maximum, the same codes)."""
+    T, d, F = 16, 128, 64
+    x = O.round_to_bf16(rng.normal(size=(T, d)))
+    mk = lambda *s: O.round_to_bf16(rng.normal(size=s) / math.sqrt(s[-1]))
+    ex = [(mk(F, d), mk(F, d), mk(d, F))]
+    sh = (mk(F, d), mk(F, d), mk(d, F))
+    zero = tuple(np.zeros_like(w) for w in sh)
+    wr = rng.normal(size=(1, d))
+    run = lambda shs: O.moe_layer(x, wr, _experts_fn(ex), 1, 1, act_fp8=True, shared=_experts_fn(shs),
+                                  n_shared=len(shs))["out"]
+    one = run([sh])
+    assert np.array_equal(run([sh, zero]), one)
+    routed = O.swiglu_ffn_a8(x, *ex[0])
+    assert np.allclose(run([sh, sh]) - routed, 2 * (one - routed), rtol=1e-13, atol=1e-13)
