@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0   # dense FP8 MFMA (layers with FP8 weights and FP8 activations)
 METRIC = "MoE-layer tokens/s at 1 MI355X; decode HBM GB/s and prefill MFMA % of peak"
 
 
@@ -195,7 +196,7 @@ def expert_bytes(sp, ffn=None):
     n = 3 * sp.d * ffn
     if sp.expert == "int4":
         return n // 2 + (3 * sp.d * ffn // 128) * 2
-    if sp.expert == "fp8":  # one byte per weight and an fp32 scale per output channel
+    if sp.expert in ("fp8", "fp8a8"):  # one byte per weight and an fp32 scale per output channel
         return n + (2 * ffn + sp.d) * 4
     return n * (4 if sp.expert == "f32" else 2)
 
@@ -537,13 +538,15 @@ def prefill_point(sp, ml, x, steps, warmup):
     ms, per, outs, nl, wall = time_layer(ml, x, steps, warmup)
     T = x.shape[0]
     w = alg_work(sp, T, outs[1], outs[3])
-    ai = w["flops"] / w["bytes"]  # flops per algorithmic byte; the ridge is 2.5 PFLOP/s / 8 TB/s = 312.5
+    # flops per algorithmic byte; the ridge is the matrix peak over 8 TB/s (bf16 312.5, FP8 625)
+    ai = w["flops"] / w["bytes"]
+    peak = FP8_PEAK_TFLOPS if sp.expert == "fp8a8" else BF16_PEAK_TFLOPS
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
-            "bound": "mfma" if ai >= BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm",
-            "flops_per_byte": round(ai, 1),
+            "bound": "mfma" if ai >= peak / HBM_PEAK_GBS * 1e3 else "hbm",
+            "flops_per_byte": round(ai, 1), "mfma_peak_tflops": peak,
             "hbm_frac_layer": round(w["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "mfma_frac_layer": round(w["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "mfma_frac_gateup": round(w["gateup_flops"] / (per["gateup"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_layer": round(w["flops"] / (ms * 1e-3) / 1e12 / peak, 4),
+            "mfma_frac_gateup": round(w["gateup_flops"] / (per["gateup"] * 1e-3) / 1e12 / peak, 4),
             "per_launch_us": {n: round(v * 1e3, 2) for n, v in per.items()},
             "kept_pairs": w["kept"], "pairs": T * sp.k, "routing": routing_report(ml, sp, x)}, (ms, per, outs, nl,
                                                                                               wall, w)
@@ -580,15 +583,19 @@ def int4_drift(sp, lay, ml, x, layout):
 def prefill_sweep(layout, steps=20, warmup=3):
     """The other prefill layers: DeepSeek-V2-Lite T=8192 (dropless and C=1.25), the
     DeepSeek-V3 token-sweep step T=4096, the INT4 layer at T=4096 (with its routing drift),
-    and FP8 experts (OLMoE-shaped T=4096, DeepSeek-V2-Lite-shaped T=8192 with FP8 shared
-    experts): useful-flop fraction of the bf16 MFMA peak (every path multiplies in bf16) of
-    the whole layer and of its gate/up launch."""
+    FP8 experts (OLMoE-shaped T=4096, DeepSeek-V2-Lite-shaped T=8192 with FP8 shared
+    experts), and FP8 experts with FP8 activations (OLMoE-shaped T=4096, DeepSeek-V3-shaped
+    T=16384): useful-flop fraction of the matrix peak the layer multiplies at (bf16, or FP8
+    for FP8 activations; `mfma_peak_tflops`) of the whole layer and of its gate/up launch
+    (with FP8 activations the gate/up and down figures include the row quantisation ahead of
+    each GEMM)."""
     import torch
 
     import moe_synth as S
     res = {}
     for name, Ts in (("dsv2_lite", (8192,)), ("dsv2_lite_cap", (8192,)), ("dsv3", (4096,)), ("qwen3_int4", (4096,)),
-                     ("olmoe_fp8", (4096,)), ("dsv2_lite_fp8", (8192,))):
+                     ("olmoe_fp8", (4096,)), ("dsv2_lite_fp8", (8192,)), ("olmoe_fp8a8", (4096,)),
+                     ("dsv3_fp8a8", (16384,))):
         sp = S.SPECS[name]
         lay = S.make_layer(sp, device="cuda")
         ml = moe_layer(sp, lay, layout)

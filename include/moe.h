@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -62,7 +62,7 @@ typedef enum {
   MOE_ERR_HIP = -4           /* a HIP launch failed                           */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2, MOE_FP8_E4M3 = 3 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2, MOE_FP8_E4M3 = 3, MOE_FP8_E4M3_A8 = 4 } moe_dtype;
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
 
@@ -79,6 +79,17 @@ typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
  * (shared experts: shs_gate / shs_up [S][ffn_shared], shs_down [S][d]); the
  * activations stay bf16.  The decode kernels convert each byte to bf16 exactly
  * and apply the scale in fp32; the prefill kernels round fp8 * s to bf16 once.
+ * MOE_FP8_E4M3_A8 (act_dtype MOE_BF16, n_shared <= 1): the same weights, and
+ * the activations of both expert GEMMs in FP8 as well, so that the GEMMs run
+ * on the FP8 matrix unit ("MoE at the inference level", Fields, weight_dtype,
+ * and workarounds: fp8 expert weights).  Each GEMM row is quantised on its own:
+ * x_t for gate/up, and for down the bf16 SwiGLU output row (the shared expert's
+ * likewise); with amax = max |v| over the row, inv = 448 / amax and
+ * scale = amax / 448 in IEEE fp32, code_i = E4M3(v_i * inv) rounded to
+ * nearest even (an all-zero row: codes 0, scale 0), and the row stands for
+ * code_i * scale.  The GEMMs accumulate code products in fp32 and scale by the
+ * row's and the output channel's scales.  Every T takes the tiled kernels;
+ * a forward is seven launches (two row quantisations added).
  * Group-limited selection ("MoE Research", section 2, node-limited routing;
  * "MoE at the inference level", workarounds, device-limited routing): with
  * n_groups = G > 0 the experts form G equal groups of consecutive indices

@@ -18,11 +18,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIBRARY", os.path.join(HERE, "libmoe.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_INT4_G128, MOE_FP8_E4M3 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_INT4_G128, MOE_FP8_E4M3, MOE_FP8_E4M3_A8 = 0, 1, 2, 3, 4
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 
-_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128, "fp8": MOE_FP8_E4M3}
+_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128, "fp8": MOE_FP8_E4M3, "fp8a8": MOE_FP8_E4M3_A8}
 _SCORES = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
 _LAYOUTS = {"rows": MOE_LAYOUT_ROWS, "tiled": MOE_LAYOUT_TILED}
 
@@ -33,7 +33,7 @@ class MoeError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 3  # MOE_ABI_VERSION of include/moe.h
+ABI_VERSION = 4  # MOE_ABI_VERSION of include/moe.h
 
 
 class MoeCfg(ctypes.Structure):

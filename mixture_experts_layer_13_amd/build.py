@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["csrc/api.hip", "csrc/route.hip", "csrc/ffn.hip", "csrc/ffn_stream.hip", "csrc/ffn_tiled.hip",
            "csrc/ffn_tiled256.hip", "csrc/ffn_tiled_int4.hip",
-           "csrc/ffn_tiled_fp8.hip"]
+           "csrc/ffn_tiled_fp8.hip", "csrc/ffn_tiled_f8f8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 VALU forms stay off for every HIP file of this library

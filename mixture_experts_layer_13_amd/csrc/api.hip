@@ -11,6 +11,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "kernels_f8f8.hpp"
 #include "moe.h"
 
 using namespace moe;
@@ -74,8 +75,11 @@ struct Plan {
   int64_t items_max, items_max_dn;
   int sh_items, sh_items_dn;
   size_t o_part, o_arrived, o_hist, o_counts, o_off, o_rowtok, o_slot, o_items, o_nitems, o_items_dn, o_nitems_dn, o_h,
-      o_hsh, o_y, o_ysh, total;
+      o_hsh, o_y, o_ysh, o_xq, o_xs, o_hq, o_hs, o_hshq, o_hshs, total;
+  bool a8;  // FP8 activations on the FP8 MFMA (MOE_FP8_E4M3_A8)
 };
+
+bool fp8_weights(int wdt) { return wdt == MOE_FP8_E4M3 || wdt == MOE_FP8_E4M3_A8; }
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -93,11 +97,13 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "act_dtype=%d is not MOE_F32 or MOE_BF16", c->act_dtype);
   if (c->expert_dtype != MOE_F32 && c->expert_dtype != MOE_BF16 && c->expert_dtype != MOE_INT4_G128 &&
-      c->expert_dtype != MOE_FP8_E4M3)
+      !fp8_weights(c->expert_dtype))
     return fail(MOE_ERR_INVALID_ARG, "expert_dtype=%d is not a moe_dtype", c->expert_dtype);
-  const bool quant = c->expert_dtype == MOE_INT4_G128 || c->expert_dtype == MOE_FP8_E4M3;
+  const bool quant = c->expert_dtype == MOE_INT4_G128 || fp8_weights(c->expert_dtype);
   if (!(c->expert_dtype == c->act_dtype || (quant && c->act_dtype == MOE_BF16)))
     return fail(MOE_ERR_UNSUPPORTED, "expert_dtype=%d with act_dtype=%d", c->expert_dtype, c->act_dtype);
+  if (c->expert_dtype == MOE_FP8_E4M3_A8 && c->n_shared > 1)
+    return fail(MOE_ERR_UNSUPPORTED, "n_shared=%d: FP8 activations take at most one shared expert", c->n_shared);
   if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID)
     return fail(MOE_ERR_INVALID_ARG, "score=%d is not a moe_score", c->score);
   if (c->renorm != 0 && c->renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm=%d is not 0 or 1", c->renorm);
@@ -175,7 +181,10 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   q.rpb = (q.n_rt + kMaxRouteBlocks - 1) / kMaxRouteBlocks;
   if (q.rpb < 1) q.rpb = 1;
   q.n_rb = (q.n_rt + q.rpb - 1) / q.rpb;
-  q.mode = (q.act == MOE_F32 || q.T <= kStreamMaxT) ? 0 : 1;
+  q.a8 = q.wdt == MOE_FP8_E4M3_A8;
+  // FP8 activations run on the tiled FP8 MFMA kernels at every T (the streaming kernels take
+  // bf16 activations)
+  q.mode = q.a8 ? 1 : ((q.act == MOE_F32 || q.T <= kStreamMaxT) ? 0 : 1);
   // streaming kernels take items of 16 rows (T <= 16: an expert gets each token at most once; or
   // at most 8 pairs per expert on average, where splitting a hot expert costs less than the
   // registers of 32-row items: measured on OLMoE T=64, 170 -> 161 us) or 32 rows; above 32 a hot
@@ -245,6 +254,12 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   q.o_hsh = take((size_t)q.T * q.S * q.FS * es);
   q.o_y = take((size_t)q.R * q.d * es);
   q.o_ysh = take(q.S ? (size_t)q.T * q.d * es : 0);
+  q.o_xq = take(q.a8 ? (size_t)q.T * q.d : 0);
+  q.o_xs = take(q.a8 ? (size_t)q.T * 4 : 0);
+  q.o_hq = take(q.a8 ? (size_t)q.R * q.F : 0);
+  q.o_hs = take(q.a8 ? (size_t)q.R * 4 : 0);
+  q.o_hshq = take(q.a8 && q.S ? (size_t)q.T * q.FS : 0);
+  q.o_hshs = take(q.a8 && q.S ? (size_t)q.T * 4 : 0);
   q.total = o;
   return MOE_OK;
 }
@@ -285,6 +300,37 @@ FfnArgs down_args(const Plan& p, void* ws, FfnArgs a) {
   return a;
 }
 
+// FP8 activations: E4M3 codes and row scales of x ahead of the gate/up GEMM, and of the routed
+// and shared h ahead of the down GEMM (every one of the R routed rows: rows past the kept count
+// hold stale values whose codes no tile reads)
+A8Args a8_args(const Plan& p, void* ws) {
+  A8Args q;
+  q.xq = at<uint8_t>(ws, p.o_xq);
+  q.xs = at<float>(ws, p.o_xs);
+  q.hq = at<uint8_t>(ws, p.o_hq);
+  q.hs = at<float>(ws, p.o_hs);
+  q.hshq = p.S ? at<uint8_t>(ws, p.o_hshq) : nullptr;
+  q.hshs = p.S ? at<float>(ws, p.o_hshs) : nullptr;
+  return q;
+}
+// the gate/up GEMM (and with FP8 activations the quantisation of x before it)
+moe_status enqueue_gateup(const Plan& p, void* ws, const FfnArgs& a, hipStream_t s) {
+  if (!p.a8) return hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM");
+  const A8Args q = a8_args(p, ws);
+  moe_status st = hip_ok(launch_quant_rows(a.x, (void*)q.xq, (float*)q.xs, p.T, p.d, nullptr, nullptr, nullptr, 0, 0, s),
+                         "activation quantisation");
+  return st ? st : hip_ok(launch_ffn_a8(true, a, q, s), "gate/up GEMM");
+}
+// the down GEMM (a: its own tile map; with FP8 activations the quantisation of h before it)
+moe_status enqueue_down(const Plan& p, void* ws, const FfnArgs& a, hipStream_t s) {
+  if (!p.a8) return hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM");
+  const A8Args q = a8_args(p, ws);
+  moe_status st = hip_ok(launch_quant_rows(a.h, (void*)q.hq, (float*)q.hs, (int)p.R, p.F, p.S ? a.hsh : nullptr,
+                                           (void*)q.hshq, (float*)q.hshs, p.T, p.FS, s),
+                         "intermediate quantisation");
+  return st ? st : hip_ok(launch_ffn_a8(false, a, q, s), "down GEMM");
+}
+
 // the expert GEMMs and the combine of moe_forward / moe_forward_with_routes
 // (timing marks 3.. for moe_forward only: `timed`)
 moe_status enqueue_experts_and_combine(const Plan& p, void* ws, const FfnArgs& a, const int32_t* topk_idx,
@@ -292,14 +338,14 @@ moe_status enqueue_experts_and_combine(const Plan& p, void* ws, const FfnArgs& a
                                        hipStream_t s, bool timed) {
   const int nl = timed ? (one_token(p) ? 4 : 5) : 1 << 30;  // an impossible count records nothing
   moe_status st;
-  if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
+  if ((st = enqueue_gateup(p, ws, a, s))) return st;
   mark(3, nl, s);
   if (one_token(p)) {
     st = hip_ok(launch_down_combine_one(p.wdt, a, topk_idx, slot, topk_w, out, p.k, s), "down GEMM + combine");
     mark(4, nl, s);
     return st;
   }
-  if ((st = hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, down_args(p, ws, a), s), "down GEMM"))) return st;
+  if ((st = enqueue_down(p, ws, down_args(p, ws, a), s))) return st;
   mark(4, nl, s);
   st = hip_ok(launch_combine(p.act, a.y, slot, topk_w, ysh, out, p.T, p.d, p.k, (int)p.R, s), "combine");
   mark(5, nl, s);
@@ -355,9 +401,9 @@ moe_status check_experts(const Plan& p, const moe_experts* w) {
   if (!w->w_gate || !w->w_up || !w->w_down) return fail(MOE_ERR_INVALID_ARG, "routed expert weight pointer is NULL");
   if (!al16(w->w_gate) || !al16(w->w_up) || !al16(w->w_down))
     return fail(MOE_ERR_INVALID_ARG, "routed expert weights must be 16-byte aligned");
-  if ((p.wdt == MOE_INT4_G128 || p.wdt == MOE_FP8_E4M3) && (!w->s_gate || !w->s_up || !w->s_down))
+  if ((p.wdt == MOE_INT4_G128 || fp8_weights(p.wdt)) && (!w->s_gate || !w->s_up || !w->s_down))
     return fail(MOE_ERR_INVALID_ARG, "INT4 and FP8 experts need s_gate, s_up and s_down");
-  if (p.wdt == MOE_FP8_E4M3 && (!al4(w->s_gate) || !al4(w->s_up) || !al4(w->s_down)))
+  if (fp8_weights(p.wdt) && (!al4(w->s_gate) || !al4(w->s_up) || !al4(w->s_down)))
     return fail(MOE_ERR_INVALID_ARG, "FP8 scales must be 4-byte aligned");
   if (p.wdt == MOE_INT4_G128 && (!al2(w->s_gate) || !al2(w->s_up) || !al2(w->s_down)))
     return fail(MOE_ERR_INVALID_ARG, "INT4 scales must be 2-byte aligned");
@@ -369,9 +415,9 @@ moe_status check_experts(const Plan& p, const moe_experts* w) {
       return fail(MOE_ERR_INVALID_ARG, "INT4 shared experts need shs_gate, shs_up and shs_down");
     if (p.wdt == MOE_INT4_G128 && (!al2(w->shs_gate) || !al2(w->shs_up) || !al2(w->shs_down)))
       return fail(MOE_ERR_INVALID_ARG, "INT4 shared-expert scales must be 2-byte aligned");
-    if (p.wdt == MOE_FP8_E4M3 && (!w->shs_gate || !w->shs_up || !w->shs_down))
+    if (fp8_weights(p.wdt) && (!w->shs_gate || !w->shs_up || !w->shs_down))
       return fail(MOE_ERR_INVALID_ARG, "FP8 shared experts need shs_gate, shs_up and shs_down");
-    if (p.wdt == MOE_FP8_E4M3 && (!al4(w->shs_gate) || !al4(w->shs_up) || !al4(w->shs_down)))
+    if (fp8_weights(p.wdt) && (!al4(w->shs_gate) || !al4(w->shs_up) || !al4(w->shs_down)))
       return fail(MOE_ERR_INVALID_ARG, "FP8 shared-expert scales must be 4-byte aligned");
   }
   return MOE_OK;
@@ -487,7 +533,7 @@ size_t moe_workspace_bytes(const moe_cfg* cfg) {
 int32_t moe_forward_launches(const moe_cfg* cfg) {
   Plan p;
   if (make_plan(cfg, &p) != MOE_OK || p.T == 0) return 0;
-  return one_token(p) ? 4 : 5;
+  return one_token(p) ? 4 : (p.a8 ? 7 : 5);
 }
 
 moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, const float* logit_bias,
@@ -553,8 +599,8 @@ moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offs
                    "down tile map")))
     return st;
   FfnArgs a = ffn_args(p, ws, x, row_token, w, y_rows, y_shared);
-  if ((st = hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM"))) return st;
-  return hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, down_args(p, ws, a), s), "down GEMM");
+  if ((st = enqueue_gateup(p, ws, a, s))) return st;
+  return enqueue_down(p, ws, down_args(p, ws, a), s);
 }
 
 moe_status moe_combine(const moe_cfg* cfg, const void* y_rows, const int32_t* slot_row, const float* topk_w,
@@ -666,11 +712,11 @@ moe_status moe_forward_with_routes(const moe_cfg* cfg, const void* x, const int3
 }
 
 moe_status moe_pack_weights(int32_t dtype, const void* src, void* dst, int64_t rows, int32_t K, void* stream) {
-  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_INT4_G128 && dtype != MOE_FP8_E4M3)
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_INT4_G128 && !fp8_weights(dtype))
     return fail(MOE_ERR_INVALID_ARG, "dtype=%d is not a moe_dtype", dtype);
   if (rows < 0 || rows % 16) return fail(MOE_ERR_INVALID_ARG, "rows=%lld is not a non-negative multiple of 16", (long long)rows);
   const int64_t rb = dtype == MOE_INT4_G128 ? (int64_t)K / 2
-                     : dtype == MOE_FP8_E4M3  ? (int64_t)K
+                     : fp8_weights(dtype)     ? (int64_t)K
                                               : (int64_t)K * (dtype == MOE_F32 ? 4 : 2);
   if (K <= 0 || (dtype == MOE_INT4_G128 && K % kInt4Group) || rb % 64)
     return fail(MOE_ERR_INVALID_ARG, "K=%d: a row must be a positive multiple of 64 bytes (INT4: K multiple of 128)", K);

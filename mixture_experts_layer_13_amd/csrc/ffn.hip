@@ -13,7 +13,8 @@
 //    item (<= 64 rows of one expert) and a few output channels and reads its
 //    weight slice once, straight from memory into MFMA operands;
 //  - tiled kernels (large M, prefill; ffn_tiled.hip for bf16,
-//    ffn_tiled_int4.hip for INT4 and ffn_tiled_fp8.hip for FP8 weights):
+//    ffn_tiled_int4.hip for INT4 and ffn_tiled_fp8.hip for FP8 weights,
+//    ffn_tiled_f8f8.hip for FP8 weights with FP8 activations on the FP8 MFMA):
 //    128-row x 256-weight-row blocks, activations through double-buffered LDS;
 //    for the bf16 gate/up GEMM of long-K layers (d >= 4096, at least 128 rows
 //    per expert) 256-row x 256-weight-row blocks of eight waves fed through an
@@ -25,6 +26,7 @@
 // are dequantised in-kernel.  This file holds the launch dispatch, the
 // weight packing kernel and the weighted combine.
 #include "ffn_common.hpp"
+#include "kernels_f8f8.hpp"
 
 namespace moe {
 
@@ -171,6 +173,14 @@ hipError_t launch_ffn_down(int mode, int act, int wdt, const FfnArgs& a, hipStre
     else launch_tiled_int4(false, a, grid, s);
   }
   (void)act;
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_a8(bool gateup, const FfnArgs& a, const A8Args& q, hipStream_t s) {
+  const int grid = gateup ? ffn_grid_xcd(a, true, a.F / 128, a.S * a.FS / 128)
+                          : ffn_grid_xcd(a, false, (a.d + 255) / 256, (a.d + 255) / 256);
+  if (grid == 0) return hipSuccess;
+  launch_tiled_f8f8(gateup, a, q, grid, s);
   return hipGetLastError();
 }
 

@@ -1,0 +1,29 @@
+// Internal interface of the FP8-activation expert FFN (ffn_tiled_f8f8.hip):
+// FP8 weights with FP8 activations on the FP8 matrix unit.  Not part of the
+// public header.
+#pragma once
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kFP8A8 = 4;  // moe_dtype MOE_FP8_E4M3_A8
+
+// E4M3 codes and fp32 row scales of the GEMMs' activation operands
+struct A8Args {
+  const uint8_t* xq;    // [T][d]
+  const float* xs;      // [T]
+  const uint8_t* hq;    // [R][F]
+  const float* hs;      // [R]
+  const uint8_t* hshq;  // [T][FS] (at most one shared expert; null without)
+  const float* hshs;    // [T]
+};
+
+void launch_tiled_f8f8(bool gateup, const FfnArgs& a, const A8Args& q, int grid, hipStream_t s);
+// the gate/up (gateup) or down GEMM over the tiled kernels' grid
+hipError_t launch_ffn_a8(bool gateup, const FfnArgs& a, const A8Args& q, hipStream_t s);
+// per-row E4M3 quantisation of bf16 rows (codes and fp32 scales), two segments in one launch
+// (src1 null: one segment)
+hipError_t launch_quant_rows(const void* src0, void* q0, float* sc0, int rows0, int cols0, const void* src1, void* q1,
+                             float* sc1, int rows1, int cols1, hipStream_t s);
+
+}  // namespace moe

@@ -49,7 +49,7 @@ class LayerSpec:
     n_shared: int
     ffn_shared: int
     act: str              # 'f32' | 'bf16'  (x, router weight, outputs)
-    expert: str           # 'f32' | 'bf16' | 'int4' | 'fp8'
+    expert: str           # 'f32' | 'bf16' | 'int4' | 'fp8' | 'fp8a8' (fp8 weights, FP8 activations)
     score: str            # 'softmax' | 'sigmoid'
     renorm: bool          # gates /= sum over the selected k
     gate_scale: float     # multiplies routed gates (2.5 for DeepSeek-V3)
@@ -92,6 +92,10 @@ SPECS["dsv2_lite_cap"] = SPECS["dsv2_lite"].replace(name="dsv2_lite_cap", capaci
 SPECS["olmoe_fp8"] = SPECS["olmoe"].replace(name="olmoe_fp8", cfg_id=5, expert="fp8", tokens=(1, 8, 32, 64, 4096))
 # the DeepSeek-V2-Lite-shaped layer with FP8 routed and shared experts (prefill)
 SPECS["dsv2_lite_fp8"] = SPECS["dsv2_lite"].replace(name="dsv2_lite_fp8", cfg_id=6, expert="fp8")
+# FP8 weights with FP8 activations (the same weights as the fp8 layers of the same cfg_id): the
+# OLMoE-shaped layer and the DeepSeek-V3-shaped layer (one shared expert)
+SPECS["olmoe_fp8a8"] = SPECS["olmoe_fp8"].replace(name="olmoe_fp8a8", expert="fp8a8")
+SPECS["dsv3_fp8a8"] = SPECS["dsv3"].replace(name="dsv3_fp8a8", expert="fp8a8")
 
 
 def spec(name: str) -> LayerSpec:
@@ -192,7 +196,7 @@ def _expert_mats(sp: LayerSpec, n: int, ffn: int, ids, seed, device, chunk):
                 packed[e0:e1], scales[e0:e1] = _quantise_int4(w)
                 del w
             out.append((packed, scales))
-        elif sp.expert == "fp8":
+        elif sp.expert in ("fp8", "fp8a8"):
             codes = torch.empty((n,) + shape_tail, dtype=torch.uint8, device=device)
             scales = torch.empty((n, shape_tail[0]), dtype=torch.float32, device=device)
             for e0 in range(0, n, chunk):
@@ -230,7 +234,7 @@ def make_layer(sp: LayerSpec, device="cpu", seed: int = 0, chunk: int = 16) -> L
                                                  sp.n_shared, sp.ffn_shared, (_T_SG, _T_SU, _T_SD), seed,
                                                  device, chunk)
         lay.sh_gate, lay.sh_up, lay.sh_down = a, b, c
-        if sp.expert == "fp8":
+        if sp.expert in ("fp8", "fp8a8"):
             lay.shs_gate, lay.shs_up, lay.shs_down = sa, sb, sc
     return lay
 

@@ -14,6 +14,13 @@ import moe_synth as S
 import oracle as O
 
 BF16_TOL, INT4_TOL, F32_TOL = 2e-2, 5e-2, 1e-4
+# FP8 activations: the oracle quantises the same bf16 rows with the same fp32 arithmetic, but
+# h comes from fp32 sums in another order, so its bf16 rounding, and then an E4M3 code, can
+# differ now and then; where the element holding a row's maximum differs, the whole row takes
+# another scale, which moves that expert's row by about the E4M3 rounding error (2^-4 at most
+# per element, a few 1e-2 over a row).  Bar: the INT4 bar for the worst row, and a median row
+# error at bf16 level.
+A8_TOL, A8_MEDIAN_TOL = 5e-2, 5e-3
 LOOSE_MARGIN, STRICT_MARGIN = 1e-3, 1e-5
 
 
@@ -63,7 +70,7 @@ class ExpertSource:
     def __call__(self, e: int):
         L = self.lay
         if self.shared:
-            if self.sp.expert == "fp8":
+            if self.sp.expert in ("fp8", "fp8a8"):
                 return [O.fp8_dequant(q[e].cpu().numpy(), s[e].cpu().numpy())
                         for q, s in ((L.sh_gate, L.shs_gate), (L.sh_up, L.shs_up), (L.sh_down, L.shs_down))]
             mats = (L.sh_gate[e], L.sh_up[e], L.sh_down[e])
@@ -73,7 +80,7 @@ class ExpertSource:
             for q, s in ((L.w_gate, L.s_gate), (L.w_up, L.s_up), (L.w_down, L.s_down)):
                 out.append(O.int4_dequant(q[e].cpu().numpy(), s[e].cpu().view(torch.int16).numpy()))
             return out
-        if self.sp.expert == "fp8":
+        if self.sp.expert in ("fp8", "fp8a8"):
             return [O.fp8_dequant(q[e].cpu().numpy(), s[e].cpu().numpy())
                     for q, s in ((L.w_gate, L.s_gate), (L.w_up, L.s_up), (L.w_down, L.s_down))]
         return [to_f64(L.w_gate[e]), to_f64(L.w_up[e]), to_f64(L.w_down[e])]
@@ -84,7 +91,7 @@ def oracle_run(sp: S.LayerSpec, lay: S.Layer, x: torch.Tensor, ffn_rows=None, ro
                        renorm=sp.renorm, gate_scale=sp.gate_scale, logit_bias=to_f64(lay.logit_bias),
                        select_bias=to_f64(lay.select_bias), capacity=sp.capacity,
                        shared=ExpertSource(sp, lay, shared=True) if sp.n_shared else None, n_shared=sp.n_shared,
-                       ffn_rows=ffn_rows, routes=routes, groups=sp.groups)
+                       ffn_rows=ffn_rows, routes=routes, groups=sp.groups, act_fp8=sp.expert == "fp8a8")
 
 
 def min_gap(key: np.ndarray, k: int) -> np.ndarray:
@@ -132,4 +139,4 @@ def row_rel_err(y: np.ndarray, ref: np.ndarray) -> np.ndarray:
 
 
 def tol_of(sp: S.LayerSpec) -> float:
-    return {"f32": F32_TOL, "bf16": BF16_TOL, "int4": INT4_TOL, "fp8": BF16_TOL}[sp.expert]
+    return {"f32": F32_TOL, "bf16": BF16_TOL, "int4": INT4_TOL, "fp8": BF16_TOL, "fp8a8": A8_TOL}[sp.expert]

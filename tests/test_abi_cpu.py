@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     lib.moe_abi_version.restype = ctypes.c_int32
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 @pytest.fixture(scope="module")
@@ -269,3 +269,20 @@ def test_256_row_item_rule(B, monkeypatch):
     # the override reaches layers the default leaves alone
     assert ws(4096, 2048, 64, 8, 1024, "1") != ws(4096, 2048, 64, 8, 1024, "0")
     monkeypatch.delenv("MOE_ROWS256_MIN_AVG", raising=False)
+
+
+def test_fp8_activation_mode_rules(B):
+    """FP8 weights with FP8 activations: bf16 activations only, at most one shared expert,
+    seven launches (two row quantisations), and a workspace holding the E4M3 codes and row
+    scales of x and h beyond the weight-only FP8 mode's."""
+    a8 = B.make_cfg(4096, 2048, 64, 8, 1024, expert="fp8a8")
+    w8 = B.make_cfg(4096, 2048, 64, 8, 1024, expert="fp8")
+    assert B.validate(a8) == B.MOE_OK
+    assert B.lib.moe_forward_launches(a8) == 7 and B.lib.moe_forward_launches(w8) == 5
+    T, d, R, F = 4096, 2048, 4096 * 8, 1024
+    assert B.workspace_bytes(a8) >= B.workspace_bytes(w8) + T * d + T * 4 + R * F + R * 4
+    # a single token keeps the tiled path (no one-launch down + combine)
+    assert B.lib.moe_forward_launches(B.cfg_with_T(a8, 1)) == 7
+    assert B.validate(B.make_cfg(64, 7168, 256, 8, 2048, 1, 2048, expert="fp8a8", score="sigmoid")) == B.MOE_OK
+    assert B.validate(B.make_cfg(64, 2048, 64, 6, 1408, 2, 1408, expert="fp8a8")) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(B.make_cfg(64, 128, 8, 2, 256, act="f32", expert="fp8a8")) == B.MOE_ERR_UNSUPPORTED
