@@ -77,7 +77,7 @@ def test_a8_layouts_and_split_path_bitwise():
         assert torch.equal(b.view(torch.int16), c.view(torch.int16))
 
 
-@pytest.mark.parametrize("T,nsamp", [(16, None), (256, 64), (4096, 48)])
+@pytest.mark.parametrize("T,nsamp", [(16, None), (4096, 12)])
 def test_a8_deepseek_v3_with_shared_expert(T, nsamp):
     sp, lay = _layer("dsv3_fp8a8")
     ml = layer_of(sp, lay, "tiled")
