@@ -7,7 +7,8 @@ expert weights): each GEMM row quantised to E4M3 with an fp32 row scale.
   decode and prefill sizes (a ragged T among them) and on the DeepSeek-V3-shaped
   layer with its shared expert.
 - The two weight layouts, and the split path (route -> permute -> expert_ffn ->
-  combine) against the fused forward, bit for bit."""
+  combine) against the fused forward, bit for bit; the forward captured in a HIP
+  graph (seven launches, no memset nodes) replays to the eager result."""
 import numpy as np
 import pytest
 import torch
@@ -83,3 +84,31 @@ def test_a8_deepseek_v3_with_shared_expert(T, nsamp):
     ml = layer_of(sp, lay, "tiled")
     print(f"case dsv3_fp8a8 T={T}", flush=True)
     _check(sp, lay, ml, T, seed=T, nsamp=nsamp)
+
+
+def test_a8_graph_replay_matches_eager():
+    sp, lay = _layer("olmoe_fp8a8")
+    ml = layer_of(sp, lay, "tiled")
+    for T in (8, 300):
+        x = S.make_tokens(sp, T, device="cuda", seed=3)
+        ref = [t.clone() for t in ml.forward(x)]
+        outs = [torch.empty_like(t) for t in ref]
+        ml.workspace(ml.cfg_for(T))
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            ml.forward(x, *outs)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            ml.forward(x, *outs)
+        for rep in range(3):
+            for t in outs:
+                t.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for u, v in zip(ref, outs):
+                assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                                   v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), (T, rep)
+        del g

@@ -15,7 +15,8 @@ def _bits(t):
     return t.view(torch.uint8) if t.dtype == torch.bfloat16 else t
 
 
-@pytest.mark.parametrize("name,Ts", [("olmoe", (300, 7)), ("qwen3_int4", (64, 1)), ("dsv2_lite_cap", (256, 33))])
+@pytest.mark.parametrize("name,Ts", [("olmoe", (300, 7)), ("qwen3_int4", (64, 1)), ("dsv2_lite_cap", (256, 33)),
+                                     ("olmoe_fp8a8", (200, 5))])
 def test_noalloc_forward_matches_forward(name, Ts):
     from mixture_experts_layer_13_amd import binding as B
     sp = S.SPECS[name]
