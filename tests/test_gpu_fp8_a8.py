@@ -78,7 +78,7 @@ def test_a8_layouts_and_split_path_bitwise():
         assert torch.equal(b.view(torch.int16), c.view(torch.int16))
 
 
-@pytest.mark.parametrize("T,nsamp", [(16, None), (4096, 12)])
+@pytest.mark.parametrize("T,nsamp", [(16, None), (4096, 12), (16384, 8)])
 def test_a8_deepseek_v3_with_shared_expert(T, nsamp):
     sp, lay = _layer("dsv3_fp8a8")
     ml = layer_of(sp, lay, "tiled")
@@ -112,3 +112,22 @@ def test_a8_graph_replay_matches_eager():
                 assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
                                    v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), (T, rep)
         del g
+
+
+def test_a8_capacity_drops_match_oracle():
+    """FP8 activations with a capacity (C = 5/4): the down GEMM's operand is quantised over
+    all of its R rows (stale rows past the kept count included, which no tile reads).  The
+    oracle replays the GPU's own routes, so the drop mask must equal the capacity rule on
+    them exactly, and every token's output must match."""
+    sp = S.SPECS["olmoe_fp8a8"].replace(capacity=(5, 4))
+    _, lay = _layer("olmoe_fp8a8")
+    ml = layer_of(sp, lay, "tiled")
+    x = S.make_tokens(sp, 4096, device="cuda", seed=11)
+    out, idx, gates, drop = ml.forward(x)
+    torch.cuda.synchronize()
+    ref = oracle_run(sp, lay, x, routes=(idx.cpu().numpy(), gates.cpu().numpy().astype(np.float64)))
+    assert np.array_equal(drop.cpu().numpy(), ref["drop"]) and int(ref["drop"].sum()) > 0
+    rel = row_rel_err(out.float().cpu().numpy().astype(np.float64), ref["out"])
+    print(f"  olmoe_fp8a8 C=5/4 T=4096: {int(ref['drop'].sum())} pairs dropped, max row rel err "
+          f"{rel.max():.2e}, median {np.median(rel):.2e}")
+    assert rel.max() <= tol_of(sp) and np.median(rel) <= A8_MEDIAN_TOL
