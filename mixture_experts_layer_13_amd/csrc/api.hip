@@ -317,7 +317,7 @@ A8Args a8_args(const Plan& p, void* ws) {
 moe_status enqueue_gateup(const Plan& p, void* ws, const FfnArgs& a, hipStream_t s) {
   if (!p.a8) return hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM");
   const A8Args q = a8_args(p, ws);
-  moe_status st = hip_ok(launch_quant_rows(a.x, (void*)q.xq, (float*)q.xs, p.T, p.d, nullptr, nullptr, nullptr, 0, 0, s),
+  moe_status st = hip_ok(launch_quant_rows(a.x, q.xq, q.xs, p.T, p.d, nullptr, nullptr, nullptr, 0, 0, s),
                          "activation quantisation");
   return st ? st : hip_ok(launch_ffn_a8(true, a, q, s), "gate/up GEMM");
 }
@@ -325,8 +325,8 @@ moe_status enqueue_gateup(const Plan& p, void* ws, const FfnArgs& a, hipStream_t
 moe_status enqueue_down(const Plan& p, void* ws, const FfnArgs& a, hipStream_t s) {
   if (!p.a8) return hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM");
   const A8Args q = a8_args(p, ws);
-  moe_status st = hip_ok(launch_quant_rows(a.h, (void*)q.hq, (float*)q.hs, (int)p.R, p.F, p.S ? a.hsh : nullptr,
-                                           (void*)q.hshq, (float*)q.hshs, p.T, p.FS, s),
+  moe_status st = hip_ok(launch_quant_rows(a.h, q.hq, q.hs, (int)p.R, p.F, p.S ? a.hsh : nullptr,
+                                           q.hshq, q.hshs, p.T, p.FS, s),
                          "intermediate quantisation");
   return st ? st : hip_ok(launch_ffn_a8(false, a, q, s), "down GEMM");
 }

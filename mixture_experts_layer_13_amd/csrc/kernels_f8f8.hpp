@@ -6,16 +6,15 @@
 
 namespace moe {
 
-constexpr int kFP8A8 = 4;  // moe_dtype MOE_FP8_E4M3_A8
-
-// E4M3 codes and fp32 row scales of the GEMMs' activation operands
+// E4M3 codes and fp32 row scales of the GEMMs' activation operands (written by the row
+// quantisation, read by the GEMMs)
 struct A8Args {
-  const uint8_t* xq;    // [T][d]
-  const float* xs;      // [T]
-  const uint8_t* hq;    // [R][F]
-  const float* hs;      // [R]
-  const uint8_t* hshq;  // [T][FS] (at most one shared expert; null without)
-  const float* hshs;    // [T]
+  uint8_t* xq;    // [T][d]
+  float* xs;      // [T]
+  uint8_t* hq;    // [R][F]
+  float* hs;      // [R]
+  uint8_t* hshq;  // [T][FS] (at most one shared expert; null without)
+  float* hshs;    // [T]
 };
 
 void launch_tiled_f8f8(bool gateup, const FfnArgs& a, const A8Args& q, int grid, hipStream_t s);
