@@ -42,7 +42,7 @@ constexpr int64_t kMaxT = 1 << 20;
 // The 256-row tiled kernels (ffn_tiled256.hip, eight waves) and when the plan takes them.  By
 // default: the bf16 gate/up GEMM of a layer with a long K (d >= 4096) whose experts average at
 // least 128 rows, on the many-token route path; its down GEMM keeps 128-row items (a second
-// tile map).  Measured on the DeepSeek-V3-shaped layer (d = 7168), one box: gate/up T=16384
+// tile map).  Measured on the DeepSeek-V3-shaped layer (d = 7168), one GPU: gate/up T=16384
 // 9.58 -> 9.12 ms, T=4096 3.59 -> 3.45 ms; down T=16384 4.56 -> 4.88 ms, T=4096 1.69 -> 1.91 ms
 // (K = F = 2048 is too short for the deeper ring to pay); and with d = 2048 gate/up loses too
 // (OLMoE T=4096 365 -> 402 us, DeepSeek-V2-Lite T=8192 800 -> 825 us).  The environment variable
@@ -284,7 +284,7 @@ moe_status hip_ok(hipError_t e, const char* what) {
 }
 
 // A single token: the down projection and the combine run as one launch
-// (down_combine_one_kernel), so a forward is four launches.  Measured (graph replays, one box):
+// (down_combine_one_kernel), so a forward is four launches.  Measured (graph replays, one GPU):
 // Qwen3 INT4-shaped T=1 37.4 -> 34.8 us, OLMoE-shaped FP8 T=1 35.9 -> 33.0 us, bf16 OLMoE-shaped
 // T=1 41.8 -> 40.3 us, DeepSeek-V2-Lite-shaped T=1 51.9 -> 50.3 us, DeepSeek-V3-shaped T=1
 // 154.2 -> 150.4 us (means of two rounds).

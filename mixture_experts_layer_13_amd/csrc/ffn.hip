@@ -58,7 +58,7 @@ hipError_t launch_pack_tiled(const void* src, void* dst, int64_t rows, int64_t r
 // ------------------------------------------------------------------ combine
 // out[t] = sum_j gate[t,j] * y_rows[slot_row[t,j]] (+ y_shared[t]), fp32, j in order.
 // Every y row is read once and out written once, so both go through non-temporal
-// loads and stores (measured, one box: DeepSeek-V3-shaped T=16384 441-449 -> 385-386 us,
+// loads and stores (measured, one GPU: DeepSeek-V3-shaped T=16384 441-449 -> 385-386 us,
 // DeepSeek-V2-Lite-shaped T=8192 50 -> 45 us, OLMoE-shaped T=4096 29.1 -> 27.5-28.0 us;
 // the decode layers unchanged).
 template <typename TA, bool PRE>
@@ -196,7 +196,7 @@ hipError_t launch_combine(int act, const void* y, const int32_t* slot_row, const
   if (T == 0) return hipSuccess;
   // few tokens: every load of a thread issued at once (latency-bound); many: one row at a time,
   // which keeps more blocks in flight (measured, graph replays with several layers per graph /
-  // eager, two boxes: OLMoE-shaped T=8 87.1 -> 84.0 and 87.3 -> 85.4 us per layer, T=32 129.8 ->
+  // eager, two GPUs: OLMoE-shaped T=8 87.1 -> 84.0 and 87.3 -> 85.4 us per layer, T=32 129.8 ->
   // 128.1 and 131.0 -> 130.0, T=64 148.9 -> 147.2 and 149.7 -> 148.9, Qwen3 INT4-shaped T=32
   // 82.8 -> 81.0; DeepSeek-V3-shaped T=16384 combine 385 -> 417 us with it)
   const bool pre = T <= kCombinePrefetchMaxT;

@@ -36,7 +36,7 @@ template <> struct Dec<FP8> {
 //    of a fragment reads 1 KB of consecutive addresses.
 // Weight bytes are read exactly once per forward: non-temporal 16-byte loads
 // (a plain streaming read of 4 GiB, csrc/probe.hip: 6.5-7.0 TB/s against
-// 5.8-6.2 TB/s with ordinary loads, box to box).
+// 5.8-6.2 TB/s with ordinary loads, GPU to GPU).
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -145,14 +145,14 @@ int stream_down_split(int wdt, int T) { return (T > 1 && (wdt == kBF16 || wdt ==
 // partial sums in LDS in wave order.  Down (K = ffn): DKS waves share a
 // channel tile, each over a contiguous part of K, added in LDS in wave order, so
 // a block covers 4 / DKS times NT tiles (DKS = 2 for bf16 and FP8 weights from two
-// tokens on, measured on graph replays of one box: FP8 OLMoE-shaped T=64 99.9 ->
+// tokens on, measured on graph replays of one GPU: FP8 OLMoE-shaped T=64 99.9 ->
 // 97.8 us, T=8 63.0 -> 62.3 us, bf16 within noise; else 1, the whole K per wave,
 // which one token keeps: the order of the single-token down + combine).  Steps are unrolled
 // U deep so each lane keeps U weight loads per matrix and tile in flight.
 // grid: items_max * (N / channels per block) routed blocks, then the shared blocks.
 // PIPE (bf16, one row tile): two register buffers of PU steps, the loads of the next PU steps
 // in flight while the current ones are multiplied; the same steps in the same order, so the
-// same sums.  Measured (graph replays, one box): it pays for single-row items, where a wave has
+// same sums.  Measured (graph replays, one GPU): it pays for single-row items, where a wave has
 // little to multiply between its loads (layers with the single-token down + combine: OLMoE-shaped
 // T=1 39.8 -> 38.7 us, DeepSeek-V3-shaped T=1 151.8 -> 147.6 us, DeepSeek-V2-Lite-shaped 49.8 ->
 // 48.7 us), and costs from 32 rows per expert on (OLMoE T=32 136.7 -> 138.5 us, T=64 154.4 ->
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(64 * (kMaxK + 1)) void down_combine_one_kernel(
   using TA = typename D::TA;
   constexpr int NT = stream_tiles<TW>();
   constexpr int CPW = 16 * NT;  // channels per block (one wave's channel tiles)
-  // steps whose loads go out together; measured for this launch (graph replays, one box): bf16
+  // steps whose loads go out together; measured for this launch (graph replays, one GPU): bf16
   // 16 / 8 / 4 took OLMoE-shaped T=1 to 45.8 / 40.5 / 39.5 us and DeepSeek-V3-shaped T=1 to
   // 174 / 151.7 / 151.1 us (five launches: 41.4 and 153.8), DeepSeek-V2-Lite-shaped T=1 to
   // 56.1 / 50.5 / 53.1 us (five launches: 52.3)
