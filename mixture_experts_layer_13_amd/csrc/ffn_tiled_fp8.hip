@@ -6,9 +6,10 @@
 //
 // Why not the FP8 MFMA: it needs both operands in FP8, i.e. the activations
 // quantised as well, which is a different layer from the one with bf16
-// activations and fp8 weights.  Why not the chip's scaled FP8 conversion: it
-// applies only the exponent of its fp32 scale (measured: bf16(fp8 * s) for
-// power-of-two s only), and the channel scales here are arbitrary.
+// activations and fp8 weights (that layer is ffn_tiled_f8f8.hip).  Why not
+// the chip's scaled FP8 conversion: it applies only the exponent of its fp32
+// scale (measured: bf16(fp8 * s) for power-of-two s only), and the channel
+// scales here are arbitrary.
 #include "ffn_common.hpp"
 
 namespace moe {
