@@ -634,6 +634,49 @@ def prefill_sweep(layout, steps=20, warmup=3):
                       "padding excluded)", "points": res}
 
 
+def ep_shard(sp, lay, x, idx, layout, n_gpus=8, steps=10, warmup=3):
+    """One GPU's share of the layer under expert parallelism over n_gpus GPUs (a design the
+    library does not run across GPUs; this measures its per-GPU kernel work at the real shape):
+    experts 0 .. E/n_gpus - 1 of the layer, fed the rows that the routing of all T tokens sends
+    to them, as a dispatch all-to-all would deliver them.  Each received row is one local token
+    with its one local expert and gate 1, run as the route-replay forward (permutation, expert
+    GEMMs, combine into received-row order); the shared expert, which each GPU would run on its
+    own T / n_gpus tokens, is left out.  Eager forwards timed between two events."""
+    import torch
+
+    import moe_synth as S
+    E_loc = sp.E // n_gpus
+    t_idx, j_idx = (idx < E_loc).nonzero(as_tuple=True)
+    x_recv = x[t_idx].contiguous()
+    idx_loc = idx[t_idx, j_idx].to(torch.int32).view(-1, 1).contiguous()
+    gates = torch.ones(idx_loc.shape, dtype=torch.float32, device=x.device)
+    R = int(x_recv.shape[0])
+    sp_loc = sp.replace(name=f"{sp.name}_ep{n_gpus}_shard0", E=E_loc, k=1, n_shared=0, ffn_shared=0,
+                        score="softmax", renorm=False, gate_scale=1.0, logit_bias_std=0.0, select_bias_std=0.0)
+    lay_loc = S.Layer(sp_loc, lay.w_router[:E_loc].contiguous(), None, None, lay.w_gate[:E_loc], lay.w_up[:E_loc],
+                      lay.w_down[:E_loc])
+    ml = moe_layer(sp_loc, lay_loc, layout)
+    for _ in range(warmup):
+        ml.forward_with_routes(x_recv, idx_loc, gates)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ml.forward_with_routes(x_recv, idx_loc, gates)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 6.0 * sp.d * sp.ffn * R
+    out = {"n_gpus": n_gpus, "local_experts": E_loc, "rows_received": R,
+           "rows_per_gpu_if_balanced": int(idx.numel()) // n_gpus, "ms_per_step": round(ms, 4),
+           "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "method": f"route-replay forward of experts 0..{E_loc - 1} on the rows the routing sends them; "
+                     f"eager, {steps} timed after {warmup}; shared expert not included"}
+    del ml, lay_loc, x_recv
+    torch.cuda.empty_cache()
+    return out
+
+
 def roofline_of(sp, T, w, per, workload):
     t_gu = per["gateup"] * 1e-3
     achieved = w["gateup_flops"] / t_gu / 1e12
@@ -719,6 +762,7 @@ def main():
                   "wall_s_timed": round(wall, 3)},
         "routing": {workload: head["routing"]},
     }
+    line["ep8_shard"] = ep_shard(sp, lay, x, outs[1], args.layout)
     del ml, outs
     torch.cuda.empty_cache()
     if not args.no_cpu:

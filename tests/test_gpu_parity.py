@@ -271,3 +271,31 @@ def test_256_row_kernels_match_the_128_row_kernels_bitwise(name, T, cap, monkeyp
                                v.view(torch.uint8) if v.dtype == torch.bfloat16 else v), (name, T, cap, env)
     if cap is not None:
         assert int(runs["0"][3].sum()) > 0  # some pairs were dropped
+
+
+def test_expert_parallel_shard_reproduces_the_layers_rows():
+    """One GPU's share under expert parallelism (experts 0..31 of the DeepSeek-V3-shaped
+    layer, fed the rows its routing sends them, one local expert per received row, gate 1)
+    returns, row for row and bit for bit, the expert outputs the single-GPU layer computes
+    for those pairs: each output row depends on its own activation row and expert only, and
+    both run the same kernels in the same K order."""
+    sp, lay, ml = get_layer("dsv3")
+    T, E_loc = 4096, sp.E // 8
+    x = S.make_tokens(sp, T, device="cuda")
+    idx, gates, _ = ml.route(x, want_scores=False)
+    counts, offsets, row_token, slot_row, drop = ml.permute(idx)
+    y_rows, _ = ml.expert_ffn(x, offsets, row_token)
+    t_idx, j_idx = (idx < E_loc).nonzero(as_tuple=True)
+    x_recv = x[t_idx].contiguous()
+    idx_loc = idx[t_idx, j_idx].to(torch.int32).view(-1, 1).contiguous()
+    sp_loc = sp.replace(E=E_loc, k=1, n_shared=0, ffn_shared=0, score="softmax", renorm=False, gate_scale=1.0,
+                        logit_bias_std=0.0, select_bias_std=0.0)
+    lay_loc = S.Layer(sp_loc, lay.w_router[:E_loc].contiguous(), None, None, lay.w_gate[:E_loc],
+                      lay.w_up[:E_loc], lay.w_down[:E_loc])
+    shard = layer_of(sp_loc, lay_loc)
+    out, _ = shard.forward_with_routes(x_recv, idx_loc, torch.ones(idx_loc.shape, dtype=torch.float32,
+                                                                   device="cuda"))
+    ref = y_rows[slot_row[t_idx, j_idx].long()]
+    torch.cuda.synchronize()
+    assert x_recv.shape[0] > T // 2
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
