@@ -5,9 +5,12 @@ the benchmark's CPU-baseline leg may import this module.  It shares no code
 with the HIP library and imports nothing from it.
 
 Every function computes its step in float64 from the exact bit patterns the
-GPU receives (bf16 / fp32 / INT4 nibbles + bf16 scales), one step at a time
-and in the order the pages describe, with numpy matmuls and sorts as the only
-library primitives.
+GPU receives (bf16 / fp32 / INT4 nibbles + bf16 scales, FP8 bytes + fp32
+scales), one step at a time and in the order the pages describe, with numpy
+matmuls and sorts as the only library primitives.  The one exception is the
+per-row FP8 quantisation of activations, whose scale and product are defined
+in IEEE fp32 (the reading in quantize_rows_e4m3) and are computed here in
+numpy float32, so that both sides take the same rounding decisions.
 
 Sources (the pages this follows):
   [MoE-dyn]  "MoE: dynamism the compiler cannot remove" -- the natural
