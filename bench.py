@@ -607,8 +607,8 @@ def prefill_sweep(layout, steps=20, warmup=3):
     """The other prefill layers: DeepSeek-V2-Lite T=8192 (dropless and C=1.25), the
     DeepSeek-V3 token-sweep step T=4096, the INT4 layer at T=4096 (with its routing drift),
     FP8 experts (OLMoE-shaped T=4096, DeepSeek-V2-Lite-shaped T=8192 with FP8 shared
-    experts), and FP8 experts with FP8 activations (OLMoE-shaped T=4096, DeepSeek-V3-shaped
-    T=16384): useful-flop fraction of the matrix peak the layer multiplies at (bf16, or FP8
+    experts), and FP8 experts with FP8 activations (OLMoE-shaped T=4096, DeepSeek-V2-Lite-shaped
+    T=8192 with its two shared experts, DeepSeek-V3-shaped T=16384): useful-flop fraction of the matrix peak the layer multiplies at (bf16, or FP8
     for FP8 activations; `mfma_peak_tflops`) of the whole layer and of its gate/up launch
     (with FP8 activations the gate/up and down figures include the row quantisation ahead of
     each GEMM)."""
@@ -618,7 +618,7 @@ def prefill_sweep(layout, steps=20, warmup=3):
     res = {}
     for name, Ts in (("dsv2_lite", (8192,)), ("dsv2_lite_cap", (8192,)), ("dsv3", (4096,)), ("qwen3_int4", (4096,)),
                      ("olmoe_fp8", (4096,)), ("dsv2_lite_fp8", (8192,)), ("olmoe_fp8a8", (4096,)),
-                     ("dsv3_fp8a8", (16384,))):
+                     ("dsv2_lite_fp8a8", (8192,)), ("dsv3_fp8a8", (16384,))):
         sp = S.SPECS[name]
         lay = S.make_layer(sp, device="cuda")
         ml = moe_layer(sp, lay, layout)

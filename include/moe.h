@@ -79,13 +79,13 @@ typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
  * (shared experts: shs_gate / shs_up [S][ffn_shared], shs_down [S][d]); the
  * activations stay bf16.  The decode kernels convert each byte to bf16 exactly
  * and apply the scale in fp32; the prefill kernels round fp8 * s to bf16 once.
- * MOE_FP8_E4M3_A8 (act_dtype MOE_BF16, n_shared <= 1): the same weights, and
+ * MOE_FP8_E4M3_A8 (act_dtype MOE_BF16): the same weights, and
  * the activations of both expert GEMMs in FP8 as well, so that the GEMMs run
  * on the FP8 matrix unit ("MoE at the inference level", Fields, weight_dtype,
  * and workarounds: fp8 expert weights).  Each GEMM row is quantised on its own:
- * x_t for gate/up, and for down the bf16 SwiGLU output row (the shared expert's
- * likewise); with amax = max |v| over the row, inv = 448 / amax and
- * scale = amax / 448 in IEEE fp32, code_i = E4M3(v_i * inv) rounded to
+ * x_t for gate/up, and for down the bf16 SwiGLU output row (for the shared
+ * experts, their rows concatenated); with amax = max |v| over the row,
+ * inv = 448 / amax and scale = amax / 448 in IEEE fp32, code_i = E4M3(v_i * inv) rounded to
  * nearest even (an all-zero row: codes 0, scale 0), and the row stands for
  * code_i * scale.  The GEMMs accumulate code products in fp32 and scale by the
  * row's and the output channel's scales.  Every T takes the tiled kernels;

@@ -102,8 +102,6 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   const bool quant = c->expert_dtype == MOE_INT4_G128 || fp8_weights(c->expert_dtype);
   if (!(c->expert_dtype == c->act_dtype || (quant && c->act_dtype == MOE_BF16)))
     return fail(MOE_ERR_UNSUPPORTED, "expert_dtype=%d with act_dtype=%d", c->expert_dtype, c->act_dtype);
-  if (c->expert_dtype == MOE_FP8_E4M3_A8 && c->n_shared > 1)
-    return fail(MOE_ERR_UNSUPPORTED, "n_shared=%d: FP8 activations take at most one shared expert", c->n_shared);
   if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID)
     return fail(MOE_ERR_INVALID_ARG, "score=%d is not a moe_score", c->score);
   if (c->renorm != 0 && c->renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm=%d is not 0 or 1", c->renorm);
@@ -258,7 +256,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   q.o_xs = take(q.a8 ? (size_t)q.T * 4 : 0);
   q.o_hq = take(q.a8 ? (size_t)q.R * q.F : 0);
   q.o_hs = take(q.a8 ? (size_t)q.R * 4 : 0);
-  q.o_hshq = take(q.a8 && q.S ? (size_t)q.T * q.FS : 0);
+  q.o_hshq = take(q.a8 && q.S ? (size_t)q.T * q.S * q.FS : 0);
   q.o_hshs = take(q.a8 && q.S ? (size_t)q.T * 4 : 0);
   q.total = o;
   return MOE_OK;
@@ -326,7 +324,7 @@ moe_status enqueue_down(const Plan& p, void* ws, const FfnArgs& a, hipStream_t s
   if (!p.a8) return hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM");
   const A8Args q = a8_args(p, ws);
   moe_status st = hip_ok(launch_quant_rows(a.h, q.hq, q.hs, (int)p.R, p.F, p.S ? a.hsh : nullptr,
-                                           q.hshq, q.hshs, p.T, p.FS, s),
+                                           q.hshq, q.hshs, p.T, p.S * p.FS, s),
                          "intermediate quantisation");
   return st ? st : hip_ok(launch_ffn_a8(false, a, q, s), "down GEMM");
 }

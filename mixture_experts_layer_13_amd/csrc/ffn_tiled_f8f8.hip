@@ -93,8 +93,12 @@ hipError_t launch_quant_rows(const void* src0, void* q0, float* sc0, int rows0, 
 
 // ------------------------------------------------------------------ tiled FP8 x FP8 GEMMs
 // A operand: the quantised activations (x codes gathered through row_token for
-// gate/up; h codes for down); B operand: the fp8 weight rows.  At most one shared
-// expert (its down GEMM then has one weight scale per output channel).
+// gate/up; h codes for down); B operand: the fp8 weight rows.  The shared
+// experts' down GEMM runs over their S concatenated K slabs, each with its own
+// channel scales, as S passes of the K loop: with s'_j = s_j (or 1 where a
+// channel's scale is 0, whose codes are then all 0), the sums are multiplied by
+// s'_j / s'_(j+1) between slab j and slab j + 1 and by the last slab's s' in the
+// epilogue, which gives the sum over j of s'_j times slab j's products.
 // STREAMW: weights loaded non-temporally (each expert's weights read by one row tile).
 template <bool GATEUP, bool TILED, bool STREAMW>
 __global__ __launch_bounds__(256, 2) void ffn_tiled_f8f8_kernel(FfnArgs a, A8Args qa) {
@@ -118,8 +122,10 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_f8f8_kernel(FfnArgs a, A8Arg
   if (!tile_of(a, NT, ti)) return;
   const int e = ti.e, row0 = ti.row0, mrows = ti.mrows, n0 = ti.n0;
   const bool shared = ti.shared;
-  const int Kfull = GATEUP ? a.d : (shared ? a.FS : a.F);
-  const uint32_t Kb = (uint32_t)Kfull;  // bytes per weight row
+  const int Kfull = GATEUP ? a.d : (shared ? a.S * a.FS : a.F);  // K of the activation rows
+  const int Kseg = GATEUP ? a.d : (shared ? a.FS : a.F);          // K of one weight matrix
+  const int nslab = Kfull / Kseg;                                  // weight slabs (shared down: S)
+  const uint32_t Kb = (uint32_t)Kseg;                              // bytes per weight row
 
   const char* bmat[2];
   const float* smat[2];
@@ -129,8 +135,8 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_f8f8_kernel(FfnArgs a, A8Arg
     smat[0] = (const float*)(shared ? a.shsg : expert_scales_of<FP8>(a.sg, e, a.F, a.d));
     smat[1] = (const float*)(shared ? a.shsu : expert_scales_of<FP8>(a.su, e, a.F, a.d));
   } else {
-    bmat[0] = bmat[1] = (const char*)(shared ? a.shd : expert_mat<FP8>(a.wd, e, a.d, Kfull));
-    smat[0] = smat[1] = (const float*)(shared ? a.shsd : expert_scales_of<FP8>(a.sd, e, a.d, Kfull));
+    bmat[0] = bmat[1] = (const char*)(shared ? a.shd : expert_mat<FP8>(a.wd, e, a.d, Kseg));
+    smat[0] = smat[1] = (const float*)(shared ? a.shsd : expert_scales_of<FP8>(a.sd, e, a.d, Kseg));
   }
   uint32_t boff[2];
   float wsc[2];  // the lane's output-channel weight scales (gate, up; or its two down columns)
@@ -140,7 +146,8 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_f8f8_kernel(FfnArgs a, A8Arg
     const int rb = GATEUP ? n0 + 32 * w : min(n0 + 64 * w + 32 * nt, a.d - 32);
     const int row = rb + c;
     boff[nt] = TILED ? (uint32_t)(row & ~15) * Kb + 256 * h + 16 * (row & 15) : (uint32_t)row * Kb + 16 * h;
-    wsc[nt] = smat[nt][row];
+    const float sv = smat[nt][row];
+    wsc[nt] = sv == 0.f ? 1.f : sv;
   }
   // activation chunk sources: rows (tid / CPR) + RPT q, 16-byte chunk tid % CPR; row scales
   const int ch = tid % CPR;
@@ -170,9 +177,11 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_f8f8_kernel(FfnArgs a, A8Arg
   }
 
   u32x4 b0q[2][2 * SUB], b1q[2][2 * SUB];
-  const int nkt = Kfull / KSTEP;
+  const int nkt = Kseg / KSTEP;  // K steps of one slab
+  size_t slab_off = 0;           // byte offset of the current slab's weight matrix
+  int slab_k = 0;                // first K step of the current slab in the activation rows
   auto load_b = [&](u32x4 (&bq)[2][2 * SUB], int kt) {
-    const size_t o = (size_t)(kt * KSTEP / 64) * cstride;
+    const size_t o = slab_off + (size_t)(kt * KSTEP / 64) * cstride;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -194,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_f8f8_kernel(FfnArgs a, A8Arg
     u32x4 ar[CPT];
     auto load_a = [&](int kt) {
 #pragma unroll
-      for (int q = 0; q < MTA; ++q) ar[q] = ld16(aptr[q] + kt * KSTEP);
+      for (int q = 0; q < MTA; ++q) ar[q] = ld16(aptr[q] + (slab_k + kt) * KSTEP);
     };
     auto store_a = [&](unsigned char* dst) {
 #pragma unroll
@@ -231,29 +240,50 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_f8f8_kernel(FfnArgs a, A8Arg
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     };
 
-    // two-step ping-pong without branches (as in the bf16 tiled kernel)
-    load_b(b0q, 0);
-    load_a(0);
-    store_a(As[0]);
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 2 <= nkt; kt += 2) {
-      load_a(min(kt + 1, nkt - 1));
-      load_b(b1q, min(kt + 1, nkt - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(As[0], b0q);
-      __builtin_amdgcn_sched_barrier(0);
-      store_a(As[1]);
-      __syncthreads();
-      load_a(min(kt + 2, nkt - 1));
-      load_b(b0q, min(kt + 2, nkt - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(As[1], b1q);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int slab = 0; slab < nslab; ++slab) {
+      if (slab > 0) {
+        // the next shared slab: its weights and scales, the sums rescaled to them; every wave is
+        // done reading the activation buffers before they are refilled
+        slab_off = (size_t)slab * a.d * Kb;
+        slab_k = slab * nkt;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int row = min(n0 + 64 * w + 32 * nt, a.d - 32) + c;
+          float cur = smat[nt][(size_t)slab * a.d + row];
+          cur = cur == 0.f ? 1.f : cur;
+          const float ratio = wsc[nt] / cur;
+#pragma unroll
+          for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= ratio;
+          wsc[nt] = cur;
+        }
+        __syncthreads();
+      }
+      // two-step ping-pong without branches (as in the bf16 tiled kernel)
+      load_b(b0q, 0);
+      load_a(0);
       store_a(As[0]);
       __syncthreads();
+      int kt = 0;
+      for (; kt + 2 <= nkt; kt += 2) {
+        load_a(min(kt + 1, nkt - 1));
+        load_b(b1q, min(kt + 1, nkt - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(As[0], b0q);
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(As[1]);
+        __syncthreads();
+        load_a(min(kt + 2, nkt - 1));
+        load_b(b0q, min(kt + 2, nkt - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(As[1], b1q);
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(As[0]);
+        __syncthreads();
+      }
+      if (kt < nkt) compute(As[0], b0q);
     }
-    if (kt < nkt) compute(As[0], b0q);
 
     // epilogue through LDS: row scale x channel scale, SwiGLU (gate/up), one bf16 rounding
     __syncthreads();
@@ -275,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled_f8f8_kernel(FfnArgs a, A8Arg
     }
     __syncthreads();
     bf16* const out = (bf16*)(GATEUP ? (shared ? a.hsh : a.h) : (shared ? a.ysh : a.y));
-    const int ld = GATEUP ? (shared ? a.FS : a.F) : a.d;
+    const int ld = GATEUP ? (shared ? a.S * a.FS : a.F) : a.d;
     const int ncols = ld;
     constexpr int CK = NC / 8;
 #pragma unroll

@@ -13,7 +13,7 @@ struct A8Args {
   float* xs;      // [T]
   uint8_t* hq;    // [R][F]
   float* hs;      // [R]
-  uint8_t* hshq;  // [T][FS] (at most one shared expert; null without)
+  uint8_t* hshq;  // [T][S * FS] (null without shared experts)
   float* hshs;    // [T]
 };
 

@@ -96,6 +96,9 @@ SPECS["dsv2_lite_fp8"] = SPECS["dsv2_lite"].replace(name="dsv2_lite_fp8", cfg_id
 # OLMoE-shaped layer and the DeepSeek-V3-shaped layer (one shared expert)
 SPECS["olmoe_fp8a8"] = SPECS["olmoe_fp8"].replace(name="olmoe_fp8a8", expert="fp8a8")
 SPECS["dsv3_fp8a8"] = SPECS["dsv3"].replace(name="dsv3_fp8a8", expert="fp8a8")
+# the DeepSeek-V2-Lite-shaped layer (two shared experts) with FP8 activations, on the weights of
+# dsv2_lite_fp8
+SPECS["dsv2_lite_fp8a8"] = SPECS["dsv2_lite_fp8"].replace(name="dsv2_lite_fp8a8", expert="fp8a8")
 
 
 def spec(name: str) -> LayerSpec:

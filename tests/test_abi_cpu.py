@@ -272,7 +272,7 @@ def test_256_row_item_rule(B, monkeypatch):
 
 
 def test_fp8_activation_mode_rules(B):
-    """FP8 weights with FP8 activations: bf16 activations only, at most one shared expert,
+    """FP8 weights with FP8 activations: bf16 activations only, any number of shared experts,
     seven launches (two row quantisations), and a workspace holding the E4M3 codes and row
     scales of x and h beyond the weight-only FP8 mode's."""
     a8 = B.make_cfg(4096, 2048, 64, 8, 1024, expert="fp8a8")
@@ -284,5 +284,8 @@ def test_fp8_activation_mode_rules(B):
     # a single token keeps the tiled path (no one-launch down + combine)
     assert B.lib.moe_forward_launches(B.cfg_with_T(a8, 1)) == 7
     assert B.validate(B.make_cfg(64, 7168, 256, 8, 2048, 1, 2048, expert="fp8a8", score="sigmoid")) == B.MOE_OK
-    assert B.validate(B.make_cfg(64, 2048, 64, 6, 1408, 2, 1408, expert="fp8a8")) == B.MOE_ERR_UNSUPPORTED
+    assert B.validate(B.make_cfg(64, 2048, 64, 6, 1408, 2, 1408, expert="fp8a8")) == B.MOE_OK
+    # the shared experts' codes cover their concatenated intermediate: T * S * FS bytes more than one
+    one, two = (B.workspace_bytes(B.make_cfg(4096, 2048, 64, 6, 1408, S, 1408, expert="fp8a8")) for S in (1, 2))
+    assert two - one >= 4096 * 1408 * (2 + 1)  # bf16 h and its E4M3 codes of the second expert
     assert B.validate(B.make_cfg(64, 128, 8, 2, 256, act="f32", expert="fp8a8")) == B.MOE_ERR_UNSUPPORTED

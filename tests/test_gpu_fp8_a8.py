@@ -131,3 +131,14 @@ def test_a8_capacity_drops_match_oracle():
     print(f"  olmoe_fp8a8 C=5/4 T=4096: {int(ref['drop'].sum())} pairs dropped, max row rel err "
           f"{rel.max():.2e}, median {np.median(rel):.2e}")
     assert rel.max() <= tol_of(sp) and np.median(rel) <= A8_MEDIAN_TOL
+
+
+@pytest.mark.parametrize("T,layout", [(40, "rows"), (300, "tiled"), (3000, "tiled")])
+def test_a8_two_shared_experts_match_oracle(T, layout):
+    """The DeepSeek-V2-Lite-shaped layer with FP8 activations: two shared experts, whose SwiGLU
+    rows are quantised as one concatenated row and whose down GEMM walks their two K slabs, each
+    with its own channel scales."""
+    sp, lay = _layer("dsv2_lite_fp8a8")
+    ml = layer_of(sp, lay, layout)
+    print(f"case dsv2_lite_fp8a8 T={T} {layout}", flush=True)
+    _check(sp, lay, ml, T, seed=T)
