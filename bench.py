@@ -500,7 +500,8 @@ def decode_other(layout):
     copies of its 0.31 GB of expert weights) and DeepSeek-V3 at T=1 and 16 (2 copies:
     one token already touches 0.8 GB), plus DeepSeek-V3 T=256 from its token sweep,
     and the OLMoE-shaped layer with FP8 experts (half the bf16 bytes) at T=1..64, with bf16
-    activations and with FP8 activations (the tiled FP8 MFMA kernels at every T)."""
+    activations and with FP8 activations (the streaming FP8 kernels on E4M3 codes up to T=32, the
+    tiled FP8 MFMA kernels above)."""
     import torch
 
     import moe_synth as S

@@ -88,8 +88,10 @@ typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
  * inv = 448 / amax and scale = amax / 448 in IEEE fp32, code_i = E4M3(v_i * inv) rounded to
  * nearest even (an all-zero row: codes 0, scale 0), and the row stands for
  * code_i * scale.  The GEMMs accumulate code products in fp32 and scale by the
- * row's and the output channel's scales.  Every T takes the tiled kernels;
- * a forward is seven launches (two row quantisations added).
+ * row's and the output channel's scales.  Up to 32 tokens the streaming FP8
+ * kernels run on the codes held as exact bf16 values, with the row scales in
+ * their epilogues; above, the tiled FP8 MFMA kernels.  A forward is seven
+ * launches (two row quantisations added).
  * Group-limited selection ("MoE Research", section 2, node-limited routing;
  * "MoE at the inference level", workarounds, device-limited routing): with
  * n_groups = G > 0 the experts form G equal groups of consecutive indices

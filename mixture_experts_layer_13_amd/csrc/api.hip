@@ -38,6 +38,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 constexpr int kSingleMaxT = 256;   // T up to which routing runs as split router + route_small
 static_assert(kSingleMaxT * kMaxK <= kSmallMaxPairs, "every small-T forward must fit the small route's pair buffers");
 constexpr int kStreamMaxT = 64;    // T up to which the expert GEMMs use the streaming kernels
+constexpr int kA8StreamMaxT = 32;  // the same with FP8 activations
 constexpr int64_t kMaxT = 1 << 20;
 // The 256-row tiled kernels (ffn_tiled256.hip, eight waves) and when the plan takes them.  By
 // default: the bf16 gate/up GEMM of a layer with a long K (d >= 4096) whose experts average at
@@ -180,9 +181,9 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   if (q.rpb < 1) q.rpb = 1;
   q.n_rb = (q.n_rt + q.rpb - 1) / q.rpb;
   q.a8 = q.wdt == MOE_FP8_E4M3_A8;
-  // FP8 activations run on the tiled FP8 MFMA kernels at every T (the streaming kernels take
-  // bf16 activations)
-  q.mode = q.a8 ? 1 : ((q.act == MOE_F32 || q.T <= kStreamMaxT) ? 0 : 1);
+  // FP8 activations: the tiled FP8 MFMA kernels, or up to kA8StreamMaxT tokens the streaming FP8
+  // kernels on the codes held as bf16 (exact), with the row scales in their epilogues
+  q.mode = q.a8 ? (q.T <= kA8StreamMaxT ? 0 : 1) : ((q.act == MOE_F32 || q.T <= kStreamMaxT) ? 0 : 1);
   // streaming kernels take items of 16 rows (T <= 16: an expert gets each token at most once; or
   // at most 8 pairs per expert on average, where splitting a hot expert costs less than the
   // registers of 32-row items: measured on OLMoE T=64, 170 -> 161 us) or 32 rows; above 32 a hot
@@ -231,6 +232,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   q.sh_items_dn = q.S > 0 ? (q.T + q.bm_dn - 1) / q.bm_dn : 0;
 
   const size_t es = q.act == MOE_F32 ? 4 : 2;
+  const size_t cs = q.mode == 0 ? 2 : 1;  // bytes per E4M3 code: bf16 values for the streaming kernels
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -252,11 +254,11 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
   q.o_hsh = take((size_t)q.T * q.S * q.FS * es);
   q.o_y = take((size_t)q.R * q.d * es);
   q.o_ysh = take(q.S ? (size_t)q.T * q.d * es : 0);
-  q.o_xq = take(q.a8 ? (size_t)q.T * q.d : 0);
+  q.o_xq = take(q.a8 ? (size_t)q.T * q.d * cs : 0);
   q.o_xs = take(q.a8 ? (size_t)q.T * 4 : 0);
-  q.o_hq = take(q.a8 ? (size_t)q.R * q.F : 0);
+  q.o_hq = take(q.a8 ? (size_t)q.R * q.F * cs : 0);
   q.o_hs = take(q.a8 ? (size_t)q.R * 4 : 0);
-  q.o_hshq = take(q.a8 && q.S ? (size_t)q.T * q.S * q.FS : 0);
+  q.o_hshq = take(q.a8 && q.S ? (size_t)q.T * q.S * q.FS * cs : 0);
   q.o_hshs = take(q.a8 && q.S ? (size_t)q.T * 4 : 0);
   q.total = o;
   return MOE_OK;
@@ -286,7 +288,7 @@ moe_status hip_ok(hipError_t e, const char* what) {
 // Qwen3 INT4-shaped T=1 37.4 -> 34.8 us, OLMoE-shaped FP8 T=1 35.9 -> 33.0 us, bf16 OLMoE-shaped
 // T=1 41.8 -> 40.3 us, DeepSeek-V2-Lite-shaped T=1 51.9 -> 50.3 us, DeepSeek-V3-shaped T=1
 // 154.2 -> 150.4 us (means of two rounds).
-bool one_token(const Plan& p) { return p.T == 1 && p.mode == 0; }
+bool one_token(const Plan& p) { return p.T == 1 && p.mode == 0 && !p.a8; }
 
 // the down GEMM's arguments: its own tile map when its items differ from the gate/up GEMM's
 FfnArgs down_args(const Plan& p, void* ws, FfnArgs a) {
@@ -315,18 +317,29 @@ A8Args a8_args(const Plan& p, void* ws) {
 moe_status enqueue_gateup(const Plan& p, void* ws, const FfnArgs& a, hipStream_t s) {
   if (!p.a8) return hip_ok(launch_ffn_gateup(p.mode, p.act, p.wdt, a, s), "gate/up GEMM");
   const A8Args q = a8_args(p, ws);
-  moe_status st = hip_ok(launch_quant_rows(a.x, q.xq, q.xs, p.T, p.d, nullptr, nullptr, nullptr, 0, 0, s),
+  const bool str = p.mode == 0;
+  moe_status st = hip_ok(launch_quant_rows(a.x, q.xq, q.xs, p.T, p.d, nullptr, nullptr, nullptr, 0, 0, str, s),
                          "activation quantisation");
-  return st ? st : hip_ok(launch_ffn_a8(true, a, q, s), "gate/up GEMM");
+  if (st) return st;
+  if (!str) return hip_ok(launch_ffn_a8(true, a, q, s), "gate/up GEMM");
+  FfnArgs b = a;
+  b.x = q.xq;  // the x codes as bf16
+  return hip_ok(launch_ffn_a8_stream(true, b, q, s), "gate/up GEMM");
 }
 // the down GEMM (a: its own tile map; with FP8 activations the quantisation of h before it)
 moe_status enqueue_down(const Plan& p, void* ws, const FfnArgs& a, hipStream_t s) {
   if (!p.a8) return hip_ok(launch_ffn_down(p.mode, p.act, p.wdt, a, s), "down GEMM");
   const A8Args q = a8_args(p, ws);
+  const bool str = p.mode == 0;
   moe_status st = hip_ok(launch_quant_rows(a.h, q.hq, q.hs, (int)p.R, p.F, p.S ? a.hsh : nullptr,
-                                           q.hshq, q.hshs, p.T, p.S * p.FS, s),
+                                           q.hshq, q.hshs, p.T, p.S * p.FS, str, s),
                          "intermediate quantisation");
-  return st ? st : hip_ok(launch_ffn_a8(false, a, q, s), "down GEMM");
+  if (st) return st;
+  if (!str) return hip_ok(launch_ffn_a8(false, a, q, s), "down GEMM");
+  FfnArgs b = a;
+  b.h = q.hq;  // the h codes as bf16
+  b.hsh = q.hshq;
+  return hip_ok(launch_ffn_a8_stream(false, b, q, s), "down GEMM");
 }
 
 // the expert GEMMs and the combine of moe_forward / moe_forward_with_routes

@@ -184,6 +184,15 @@ hipError_t launch_ffn_a8(bool gateup, const FfnArgs& a, const A8Args& q, hipStre
   return hipGetLastError();
 }
 
+hipError_t launch_ffn_a8_stream(bool gateup, const FfnArgs& a, const A8Args& q, hipStream_t s) {
+  const int cpb = gateup ? stream_channels_per_block(true, kFP8)
+                         : stream_channels_per_block(false, kFP8) / stream_down_split(kFP8, a.T);
+  const int grid = gateup ? ffn_grid(a, a.F / cpb, a.S * a.FS / cpb) : ffn_grid(a, a.d / cpb, a.d / cpb);
+  if (grid == 0) return hipSuccess;
+  launch_stream_ffn_a8(gateup, a, q, grid, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(int act, const void* y, const int32_t* slot_row, const float* w, const void* ysh, void* out,
                           int T, int d, int k, int R, hipStream_t s) {
   const int V = act == kF32 ? 4 : 8;

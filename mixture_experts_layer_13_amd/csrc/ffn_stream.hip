@@ -3,6 +3,7 @@
 // output channels; its waves read their weight slice once, straight from
 // memory into MFMA operands, so the weight stream is the whole cost.
 #include "ffn_common.hpp"
+#include "kernels_f8f8.hpp"
 
 namespace moe {
 
@@ -159,8 +160,12 @@ int stream_down_split(int wdt, int T) { return (T > 1 && (wdt == kBF16 || wdt ==
 // 157.1 us), so the host takes it for T = 1 only.  The same buffers in the single-token down +
 // combine launch were slower (DeepSeek-V3-shaped T=1 147.6 -> 148.3 / 150.3 us with 8 / 4 steps
 // per buffer).
-template <typename TW, bool GATEUP, int MT, bool PIPE = false, int DKS = 1>
-__global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
+// A8 (FP8 weights, FP8 activations at decode sizes): the activation rows hold the E4M3 codes of x
+// (gate/up) or h (down) as exact bf16 values, and the epilogue multiplies each row's sums by its
+// fp32 row scale (qa.xs by token for gate/up, qa.hs / qa.hshs by row for down) before SwiGLU
+// or the store.
+template <typename TW, bool GATEUP, int MT, bool PIPE = false, int DKS = 1, bool A8 = false>
+__global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a, A8Args qa) {
   using D = Dec<TW>;
   using TA = typename D::TA;
   constexpr int NM = GATEUP ? 2 : 1;
@@ -387,21 +392,39 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(FfnArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * mt + 4 * g + i;
       if (r >= mrows) continue;
+      float rs = 1.f;
+      if constexpr (A8) {
+        if (GATEUP) {
+          int tok = shared ? row0 + r : a.row_token[row0 + r];
+          tok = min(max(tok, 0), a.T - 1);
+          rs = qa.xs[tok];
+        } else {
+          rs = (shared ? qa.hshs : qa.hs)[row0 + r];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const int n = n0 + 16 * j;
         if (GATEUP) {
-          const float hv = silu(acc[0][j][mt][i]) * acc[NM - 1][j][mt][i];
+          float gv = acc[0][j][mt][i], uv = acc[NM - 1][j][mt][i];
+          if constexpr (A8) {
+            gv *= rs;
+            uv *= rs;
+          }
+          const float hv = silu(gv) * uv;
           TA* hout = (TA*)(shared ? a.hsh : a.h);
           hout[(size_t)(row0 + r) * (shared ? Ns : Nr) + n] = from_f32<TA>(hv);
         } else {
+          float yv = acc[0][j][mt][i];
+          if constexpr (A8) yv *= rs;
           TA* yout = (TA*)(shared ? a.ysh : a.y);
-          yout[(size_t)(row0 + r) * a.d + n] = from_f32<TA>(acc[0][j][mt][i]);
+          yout[(size_t)(row0 + r) * a.d + n] = from_f32<TA>(yv);
         }
       }
     }
   }
 }
+
 
 // ------------------------------------------------------------------ one token: down + combine
 // For a single token (T = 1) the down projection and the weighted combine are one launch:
@@ -519,19 +542,41 @@ hipError_t launch_down_combine_one(int wdt, const FfnArgs& a, const int32_t* top
 template <bool GATEUP, int MT>
 static void launch_stream(int wdt, const FfnArgs& a, int grid, hipStream_t s) {
   if (MT == 1 && wdt == kBF16 && a.T == 1)
-    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, 1, true>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, 1, true>), dim3(grid), dim3(256), 0, s, a, A8Args{});
   else if (wdt == kF32)
-    hipLaunchKernelGGL((ffn_stream_kernel<float, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_stream_kernel<float, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a, A8Args{});
   else if (wdt == kBF16 && !GATEUP && stream_down_split(wdt, a.T) == 2)
-    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT, false, 2>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT, false, 2>), dim3(grid), dim3(256), 0, s, a, A8Args{});
   else if (wdt == kBF16)
-    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_stream_kernel<bf16, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a, A8Args{});
   else if (wdt == kFP8 && !GATEUP && stream_down_split(wdt, a.T) == 2)
-    hipLaunchKernelGGL((ffn_stream_kernel<FP8, GATEUP, MT, false, 2>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_stream_kernel<FP8, GATEUP, MT, false, 2>), dim3(grid), dim3(256), 0, s, a, A8Args{});
   else if (wdt == kFP8)
-    hipLaunchKernelGGL((ffn_stream_kernel<FP8, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_stream_kernel<FP8, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a, A8Args{});
   else
-    hipLaunchKernelGGL((ffn_stream_kernel<INT4, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ffn_stream_kernel<INT4, GATEUP, MT>), dim3(grid), dim3(256), 0, s, a, A8Args{});
+}
+
+// FP8 weights with FP8 activations at decode sizes (the down GEMM split as for FP8 weights)
+template <bool GATEUP, int MT>
+static void launch_stream_a8(const FfnArgs& a, const A8Args& q, int grid, hipStream_t s) {
+  if (!GATEUP && stream_down_split(kFP8, a.T) == 2)
+    hipLaunchKernelGGL((ffn_stream_kernel<FP8, GATEUP, MT, false, 2, true>), dim3(grid), dim3(256), 0, s, a, q);
+  else
+    hipLaunchKernelGGL((ffn_stream_kernel<FP8, GATEUP, MT, false, 1, true>), dim3(grid), dim3(256), 0, s, a, q);
+}
+
+void launch_stream_ffn_a8(bool gateup, const FfnArgs& a, const A8Args& q, int grid, hipStream_t s) {
+  const int mt = a.bm <= 16 ? 1 : (a.bm <= 32 ? 2 : 4);
+  if (gateup) {
+    if (mt == 1) launch_stream_a8<true, 1>(a, q, grid, s);
+    else if (mt == 2) launch_stream_a8<true, 2>(a, q, grid, s);
+    else launch_stream_a8<true, 4>(a, q, grid, s);
+  } else {
+    if (mt == 1) launch_stream_a8<false, 1>(a, q, grid, s);
+    else if (mt == 2) launch_stream_a8<false, 2>(a, q, grid, s);
+    else launch_stream_a8<false, 4>(a, q, grid, s);
+  }
 }
 
 // items of <= 16, 32 or 64 rows take 1, 2 or 4 row tiles of 16

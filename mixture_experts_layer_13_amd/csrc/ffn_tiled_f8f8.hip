@@ -40,9 +40,10 @@ __device__ __forceinline__ f32x16 mma32_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 
 // shared experts' h rows); blocks [0, nb0) take segment 0.
 struct QuantSeg {
   const bf16* src;  // [rows][cols]
-  uint8_t* q;       // [rows][cols]
+  uint8_t* q;       // [rows][cols] codes, or with bf16 set [rows][cols] bf16 values of the codes
   float* scale;     // [rows]
   int rows, cols;
+  int bf16;         // store each code as its (exact) bf16 value: the streaming kernels' operand
 };
 
 __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(QuantSeg s0, QuantSeg s1, int nb0) {
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(QuantSeg s0, Quant
   wave_max_n<1>(mv);
   m = mv[0];
   const float inv = m > 0.f ? __fdiv_rn(448.f, m) : 0.f;
-  uint8_t* qrow = sg.q + (size_t)r * sg.cols;
+  uint8_t* qrow = sg.q + (size_t)r * sg.cols * (sg.bf16 ? 2 : 1);
   for (int c = lane; c < nch; c += kWave) {
     const u32x4 v = ld16(row + 16 * c);
     uint32_t w[2];
@@ -76,15 +77,28 @@ __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(QuantSeg s0, Quant
                                           bf16_bits_to_f32(v[2 * p + 1] >> 16) * inv, o, true);
       w[p] = (uint32_t)o;
     }
-    *reinterpret_cast<uint2*>(qrow + 8 * c) = make_uint2(w[0], w[1]);
+    if (sg.bf16) {
+      // codes 4p .. 4p + 3 of the chunk back to fp32 (exact) and to bf16 (exact: 4 significant bits)
+      u32x4 b;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[p], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[p], true);
+        b[2 * p] = pack_bf16x2(lo[0], lo[1]);
+        b[2 * p + 1] = pack_bf16x2(hi[0], hi[1]);
+      }
+      st16(qrow + 16 * c, b);
+    } else {
+      *reinterpret_cast<uint2*>(qrow + 8 * c) = make_uint2(w[0], w[1]);
+    }
   }
   if (lane == 0) sg.scale[r] = m > 0.f ? __fdiv_rn(m, 448.f) : 0.f;
 }
 
 hipError_t launch_quant_rows(const void* src0, void* q0, float* sc0, int rows0, int cols0, const void* src1, void* q1,
-                             float* sc1, int rows1, int cols1, hipStream_t s) {
-  QuantSeg a{(const bf16*)src0, (uint8_t*)q0, sc0, rows0, cols0};
-  QuantSeg b{(const bf16*)src1, (uint8_t*)q1, sc1, src1 ? rows1 : 0, cols1};
+                             float* sc1, int rows1, int cols1, bool bf16_codes, hipStream_t s) {
+  QuantSeg a{(const bf16*)src0, (uint8_t*)q0, sc0, rows0, cols0, bf16_codes ? 1 : 0};
+  QuantSeg b{(const bf16*)src1, (uint8_t*)q1, sc1, src1 ? rows1 : 0, cols1, bf16_codes ? 1 : 0};
   const int nb0 = (a.rows + 3) / 4, nb1 = (b.rows + 3) / 4;
   if (nb0 + nb1 == 0) return hipSuccess;
   hipLaunchKernelGGL(quant_rows_e4m3_kernel, dim3(nb0 + nb1), dim3(256), 0, s, a, b, nb0);

@@ -4,8 +4,9 @@ expert weights): each GEMM row quantised to E4M3 with an fp32 row scale.
 
 - Parity against the FP64 oracle, which quantises the same bf16 rows with the
   same fp32 arithmetic (oracle.quantize_rows_e4m3), on the OLMoE-shaped layer at
-  decode and prefill sizes (a ragged T among them) and on the DeepSeek-V3-shaped
-  layer with its shared expert.
+  decode sizes (the streaming kernels up to T = 32) and prefill sizes (the tiled
+  FP8 MFMA kernels; a ragged T among them), on the DeepSeek-V3-shaped layer with
+  its shared expert and on the DeepSeek-V2-Lite-shaped one with two.
 - The two weight layouts, and the split path (route -> permute -> expert_ffn ->
   combine) against the fused forward, bit for bit; the forward captured in a HIP
   graph (seven launches, no memset nodes) replays to the eager result."""
@@ -133,11 +134,11 @@ def test_a8_capacity_drops_match_oracle():
     assert rel.max() <= tol_of(sp) and np.median(rel) <= A8_MEDIAN_TOL
 
 
-@pytest.mark.parametrize("T,layout", [(40, "rows"), (300, "tiled"), (3000, "tiled")])
+@pytest.mark.parametrize("T,layout", [(20, "tiled"), (40, "rows"), (300, "tiled"), (3000, "tiled")])
 def test_a8_two_shared_experts_match_oracle(T, layout):
     """The DeepSeek-V2-Lite-shaped layer with FP8 activations: two shared experts, whose SwiGLU
     rows are quantised as one concatenated row and whose down GEMM walks their two K slabs, each
-    with its own channel scales."""
+    with its own channel scales (T = 20: the streaming kernels; from T = 40: the tiled ones)."""
     sp, lay = _layer("dsv2_lite_fp8a8")
     ml = layer_of(sp, lay, layout)
     print(f"case dsv2_lite_fp8a8 T={T} {layout}", flush=True)
